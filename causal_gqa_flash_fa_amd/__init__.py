@@ -1,0 +1,191 @@
+"""Python binding of libfa: causal GQA flash attention for MI355X (gfx950).
+
+Argument marshalling only. Every function here forwards to the C-ABI entry
+point of the same name in libfa.so (declared in include/fa.h); all the
+attention work runs in the HIP kernels behind it. PyTorch supplies device
+memory and streams: tensors are passed by data pointer, streams by handle.
+
+There is no fallback: if libfa.so is missing, importing this package raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfa.so")
+
+FA_OK = 0
+FA_EINVAL = -1
+FA_ENULL = -2
+FA_EUNSUPPORTED = -3
+FA_EWORKSPACE = -4
+FA_EHIP = -5
+FA_ERANGE = -6
+FA_EDEVICE = -7
+
+FA_KV_F32 = 0
+FA_KV_Q4_0 = 1
+
+EXPORTS = [
+    "fa_cache_row_bytes", "fa_cache_bytes", "fa_init", "fa_kv_append", "fa_prefill",
+    "fa_prefill_tile_shape", "fa_decode_plan", "fa_decode_plan_params",
+    "fa_decode_workspace_bytes", "fa_decode", "fa_strerror",
+]
+
+
+class fa_cache(ctypes.Structure):
+    """Mirror of `struct fa_cache` in include/fa.h."""
+    _fields_ = [("format", ctypes.c_int), ("n_slots", ctypes.c_int),
+                ("n_kv_head", ctypes.c_int), ("head_dim", ctypes.c_int),
+                ("max_seq", ctypes.c_int), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p)]
+
+
+class FaError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {fa_strerror(code)} (code {code})")
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python -m causal_gqa_flash_fa_amd.build` "
+            "(there is no CPU fallback)")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I, Z, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_float
+    PI = ctypes.POINTER(ctypes.c_int)
+    C = ctypes.POINTER(fa_cache)
+    L.fa_cache_row_bytes.argtypes = [I, I]
+    L.fa_cache_row_bytes.restype = Z
+    L.fa_cache_bytes.argtypes = [C]
+    L.fa_cache_bytes.restype = Z
+    L.fa_init.argtypes = []
+    L.fa_init.restype = I
+    L.fa_kv_append.argtypes = [C, I, I, I, P, P, P]
+    L.fa_kv_append.restype = I
+    L.fa_prefill.argtypes = [C, I, P, I, I, I, I, I, F, P, P, P]
+    L.fa_prefill.restype = I
+    L.fa_prefill_tile_shape.argtypes = [I, I, I, PI, PI]
+    L.fa_prefill_tile_shape.restype = I
+    L.fa_decode_plan.argtypes = [I, PI, PI]
+    L.fa_decode_plan.restype = I
+    L.fa_decode_plan_params.argtypes = [PI, PI, PI]
+    L.fa_decode_plan_params.restype = None
+    L.fa_decode_workspace_bytes.argtypes = [C, I, I, I]
+    L.fa_decode_workspace_bytes.restype = Z
+    L.fa_decode.argtypes = [C, P, P, I, I, I, I, I, F, P, P, Z, P, P]
+    L.fa_decode.restype = I
+    L.fa_strerror.argtypes = [I]
+    L.fa_strerror.restype = ctypes.c_char_p
+    return L
+
+
+lib = _load()
+
+
+def _ptr(x) -> int | None:
+    """Device pointer of a tensor (or an int address, or None -> NULL)."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    """hipStream_t handle: a torch stream, an int handle, or torch's current stream."""
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(rc: int, where: str) -> int:
+    if rc < 0:
+        raise FaError(rc, where)
+    return rc
+
+
+def fa_strerror(code: int) -> str:
+    return lib.fa_strerror(code).decode()
+
+
+def fa_cache_row_bytes(fmt: int, head_dim: int) -> int:
+    return lib.fa_cache_row_bytes(fmt, head_dim)
+
+
+def fa_cache_bytes(cache: fa_cache) -> int:
+    return lib.fa_cache_bytes(ctypes.byref(cache))
+
+
+def fa_init() -> None:
+    _check(lib.fa_init(), "fa_init")
+
+
+def fa_kv_append(cache: fa_cache, slot: int, pos0: int, n: int, k_new, v_new,
+                 stream=None) -> None:
+    _check(lib.fa_kv_append(ctypes.byref(cache), slot, pos0, n, _ptr(k_new), _ptr(v_new),
+                            _stream(stream)), "fa_kv_append")
+
+
+def fa_prefill(cache: fa_cache, slot: int, q, pos0: int, n: int, n_head: int,
+               attn_sink: int, attn_win: int, scale: float, out, tile_stats=None,
+               stream=None) -> None:
+    _check(lib.fa_prefill(ctypes.byref(cache), slot, _ptr(q), pos0, n, n_head, attn_sink,
+                          attn_win, scale, _ptr(out), _ptr(tile_stats), _stream(stream)),
+           "fa_prefill")
+
+
+def fa_prefill_tile_shape(n_head: int, n_kv_head: int, head_dim: int) -> tuple[int, int]:
+    bq, bk = ctypes.c_int(), ctypes.c_int()
+    _check(lib.fa_prefill_tile_shape(n_head, n_kv_head, head_dim, ctypes.byref(bq),
+                                     ctypes.byref(bk)), "fa_prefill_tile_shape")
+    return bq.value, bk.value
+
+
+def fa_decode_plan(seq_len: int) -> tuple[int, int, int]:
+    """(live, n_splits, split_len)."""
+    n, sl = ctypes.c_int(), ctypes.c_int()
+    live = _check(lib.fa_decode_plan(seq_len, ctypes.byref(n), ctypes.byref(sl)),
+                  "fa_decode_plan")
+    return live, n.value, sl.value
+
+
+def fa_decode_plan_params() -> tuple[int, int, int]:
+    """(kps, cap, key_tile)."""
+    a, b, c = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    lib.fa_decode_plan_params(ctypes.byref(a), ctypes.byref(b), ctypes.byref(c))
+    return a.value, b.value, c.value
+
+
+def fa_decode_workspace_bytes(cache: fa_cache, n_slots: int, n_head: int, max_ctx: int) -> int:
+    return lib.fa_decode_workspace_bytes(ctypes.byref(cache), n_slots, n_head, max_ctx)
+
+
+def fa_decode(cache: fa_cache, q, d_pos, n_slots: int, max_ctx_hint: int, n_head: int,
+              attn_sink: int, attn_win: int, scale: float, out, ws, ws_bytes: int,
+              tile_stats=None, stream=None) -> None:
+    _check(lib.fa_decode(ctypes.byref(cache), _ptr(q), _ptr(d_pos), n_slots, max_ctx_hint,
+                         n_head, attn_sink, attn_win, scale, _ptr(out), _ptr(ws), ws_bytes,
+                         _ptr(tile_stats), _stream(stream)), "fa_decode")
+
+
+def make_cache(fmt: int, n_slots: int, n_kv_head: int, head_dim: int, max_seq: int,
+               device="cuda"):
+    """Allocate K and V cache tensors with torch and describe them.
+
+    Returns (fa_cache, k_tensor, v_tensor); keep the tensors alive as long as
+    the struct is used. Memory comes from torch's allocator: libfa never
+    allocates.
+    """
+    import torch
+    probe = fa_cache(fmt, n_slots, n_kv_head, head_dim, max_seq, None, None)
+    nbytes = lib.fa_cache_bytes(ctypes.byref(probe))
+    if nbytes == 0:
+        raise FaError(FA_EINVAL, "make_cache")
+    k = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    v = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return fa_cache(fmt, n_slots, n_kv_head, head_dim, max_seq, k.data_ptr(), v.data_ptr()), k, v

@@ -1,0 +1,214 @@
+// C-ABI layer of libfa: argument validation, geometry, and dispatch to the
+// kernel launchers. Nothing here allocates device memory or synchronises.
+// Unsupported or inconsistent arguments are refused with a code before any
+// launch ([VT] kernel registration contract: fail loudly, never truncate).
+#include <math.h>
+#include <string.h>
+
+#include "../../include/fa.h"
+#include "fa_device.hpp"
+#include "fa_internal.hpp"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+int g_device_ok[kMaxDevices];   // 0 unknown, 1 gfx950, -1 other
+
+bool dim_ok(int head_dim) { return head_dim == 64 || head_dim == 128 || head_dim == 256; }
+bool group_ok(int g) { return g == 1 || g == 2 || g == 4 || g == 8; }
+
+int check_cache(const fa_cache *c) {
+    if (!c) return FA_ENULL;
+    if (c->format != FA_KV_F32 && c->format != FA_KV_Q4_0) return FA_EUNSUPPORTED;
+    if (!dim_ok(c->head_dim)) return FA_EUNSUPPORTED;
+    if (c->n_slots < 1 || c->n_kv_head < 1 || c->max_seq < 1) return FA_EINVAL;
+    if (!c->k || !c->v) return FA_ENULL;
+    return FA_OK;
+}
+
+int check_heads(const fa_cache *c, int n_head) {
+    if (n_head < 1 || n_head % c->n_kv_head != 0) return FA_EINVAL;
+    if (!group_ok(n_head / c->n_kv_head)) return FA_EUNSUPPORTED;
+    return FA_OK;
+}
+
+int check_scale(float scale) {
+    return (isfinite(scale) && scale > 0.0f) ? FA_OK : FA_EINVAL;
+}
+
+size_t slot_stride_bytes(const fa_cache *c) {
+    return (size_t)c->n_kv_head * c->max_seq * fa_cache_row_bytes(c->format, c->head_dim);
+}
+
+int hip_rc(hipError_t e) { return e == hipSuccess ? FA_OK : FA_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+size_t fa_cache_row_bytes(int format, int head_dim) {
+    if (!dim_ok(head_dim)) return 0;
+    if (format == FA_KV_F32) return (size_t)head_dim * 4;
+    if (format == FA_KV_Q4_0) return (size_t)fa::q4_row_bytes(head_dim);
+    return 0;
+}
+
+size_t fa_cache_bytes(const fa_cache *c) {
+    if (!c || c->n_slots < 1 || c->n_kv_head < 1 || c->max_seq < 1) return 0;
+    const size_t rb = fa_cache_row_bytes(c->format, c->head_dim);
+    return (size_t)c->n_slots * slot_stride_bytes(c) * (rb ? 1 : 0);
+}
+
+int fa_init(void) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return FA_EHIP;
+    if (dev < 0 || dev >= kMaxDevices) return FA_EDEVICE;
+    if (g_device_ok[dev] == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return FA_EHIP;
+        g_device_ok[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    }
+    return g_device_ok[dev] == 1 ? FA_OK : FA_EDEVICE;
+}
+
+int fa_kv_append(const fa_cache *cache, int slot, int pos0, int n, const float *k_new,
+                 const float *v_new, void *stream) {
+    int rc = check_cache(cache);
+    if (rc) return rc;
+    if (slot < 0 || slot >= cache->n_slots || pos0 < 0 || n < 0) return FA_EINVAL;
+    if ((long long)pos0 + n > cache->max_seq) return FA_ERANGE;
+    if (n == 0) return FA_OK;
+    if (!k_new || !v_new) return FA_ENULL;
+    if ((rc = fa_init())) return rc;
+    fa::AppendArgs a;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.k = (uint8_t *)cache->k + (size_t)slot * slot_stride_bytes(cache);
+    a.v = (uint8_t *)cache->v + (size_t)slot * slot_stride_bytes(cache);
+    a.n = n;
+    a.n_kv = cache->n_kv_head;
+    a.head_dim = cache->head_dim;
+    a.max_seq = cache->max_seq;
+    a.pos0 = pos0;
+    return hip_rc(fa::launch_append(cache->format, a, (hipStream_t)stream));
+}
+
+int fa_prefill_tile_shape(int n_head, int n_kv_head, int head_dim, int *q_positions,
+                          int *key_tile) {
+    if (n_kv_head < 1 || n_head < 1 || n_head % n_kv_head) return FA_EINVAL;
+    if (!group_ok(n_head / n_kv_head) || !dim_ok(head_dim)) return FA_EUNSUPPORTED;
+    if (q_positions) *q_positions = fa::prefill_q_positions(n_head / n_kv_head);
+    if (key_tile) *key_tile = fa::kPrefillKeyTile;
+    return FA_OK;
+}
+
+int fa_prefill(const fa_cache *cache, int slot, const float *q, int pos0, int n, int n_head,
+               int attn_sink, int attn_win, float scale, float *out,
+               unsigned long long *tile_stats, void *stream) {
+    int rc = check_cache(cache);
+    if (rc) return rc;
+    if ((rc = check_heads(cache, n_head))) return rc;
+    if ((rc = check_scale(scale))) return rc;
+    if (slot < 0 || slot >= cache->n_slots || pos0 < 0 || n < 0) return FA_EINVAL;
+    if ((long long)pos0 + n > cache->max_seq) return FA_ERANGE;
+    if (n == 0) return FA_OK;
+    if (!q || !out) return FA_ENULL;
+    if ((rc = fa_init())) return rc;
+    const int group = n_head / cache->n_kv_head;
+    const int bq = fa::prefill_q_positions(group);
+    fa::PrefillArgs a;
+    a.q = q;
+    a.out = out;
+    a.k = (const uint8_t *)cache->k + (size_t)slot * slot_stride_bytes(cache);
+    a.v = (const uint8_t *)cache->v + (size_t)slot * slot_stride_bytes(cache);
+    a.stats = tile_stats;
+    a.n = n;
+    a.pos0 = pos0;
+    a.n_head = n_head;
+    a.n_kv = cache->n_kv_head;
+    a.max_seq = cache->max_seq;
+    a.sink = attn_sink < 0 ? 0 : attn_sink;
+    a.win = attn_win;
+    a.qscale = scale * fa::kLog2e;
+    a.n_qblocks = (n + bq - 1) / bq;
+    return hip_rc(fa::launch_prefill(cache->format, cache->head_dim, group, a,
+                                     (hipStream_t)stream));
+}
+
+void fa_decode_plan_params(int *kps, int *cap, int *key_tile) {
+    if (kps) *kps = fa::kDecodeKps;
+    if (cap) *cap = fa::kDecodeSplitCap;
+    if (key_tile) *key_tile = fa::kDecodeKeyTile;
+}
+
+int fa_decode_plan(int seq_len, int *n_splits, int *split_len) {
+    if (seq_len < 1) return FA_EINVAL;
+    int n, len;
+    const int live = fa::decode_plan(seq_len, fa::kDecodeKps, fa::kDecodeSplitCap,
+                                     fa::kDecodeKeyTile, &n, &len);
+    if (n_splits) *n_splits = n;
+    if (split_len) *split_len = len;
+    return live;
+}
+
+size_t fa_decode_workspace_bytes(const fa_cache *cache, int n_slots, int n_head, int max_ctx) {
+    if (!cache || !dim_ok(cache->head_dim) || n_slots < 0 || n_head < 1 || max_ctx < 1)
+        return 0;
+    const int splits = fa_decode_plan(max_ctx, nullptr, nullptr);
+    return (size_t)n_slots * n_head * splits * (cache->head_dim + 2) * sizeof(float);
+}
+
+int fa_decode(const fa_cache *cache, const float *q, const int *d_pos, int n_slots,
+              int max_ctx_hint, int n_head, int attn_sink, int attn_win, float scale,
+              float *out, void *ws, size_t ws_bytes, unsigned long long *tile_stats,
+              void *stream) {
+    int rc = check_cache(cache);
+    if (rc) return rc;
+    if ((rc = check_heads(cache, n_head))) return rc;
+    if ((rc = check_scale(scale))) return rc;
+    if (n_slots < 0 || n_slots > cache->n_slots) return FA_EINVAL;
+    if (max_ctx_hint < 1 || max_ctx_hint > cache->max_seq) return FA_EINVAL;
+    if (n_slots == 0) return FA_OK;
+    if (!q || !d_pos || !out || !ws) return FA_ENULL;
+    if (ws_bytes < fa_decode_workspace_bytes(cache, n_slots, n_head, max_ctx_hint))
+        return FA_EWORKSPACE;
+    if ((rc = fa_init())) return rc;
+    const int splits = fa_decode_plan(max_ctx_hint, nullptr, nullptr);
+    const size_t parts = (size_t)n_slots * n_head * splits;
+    fa::DecodeArgs a;
+    a.q = q;
+    a.pos = d_pos;
+    a.k = cache->k;
+    a.v = cache->v;
+    a.ws_m = (float *)ws;
+    a.ws_l = a.ws_m + parts;
+    a.ws_acc = a.ws_l + parts;
+    a.out = out;
+    a.stats = tile_stats;
+    a.n_head = n_head;
+    a.n_kv = cache->n_kv_head;
+    a.max_seq = cache->max_seq;
+    a.sink = attn_sink < 0 ? 0 : attn_sink;
+    a.win = attn_win;
+    a.qscale = scale * fa::kLog2e;
+    a.kps = fa::kDecodeKps;
+    a.cap = fa::kDecodeSplitCap;
+    return hip_rc(fa::launch_decode(cache->format, cache->head_dim, n_head / cache->n_kv_head,
+                                    a, n_slots, splits, (hipStream_t)stream));
+}
+
+const char *fa_strerror(int code) {
+    switch (code) {
+    case FA_OK: return "ok";
+    case FA_EINVAL: return "invalid argument value";
+    case FA_ENULL: return "required pointer is NULL";
+    case FA_EUNSUPPORTED: return "unsupported head_dim, group size or KV format";
+    case FA_EWORKSPACE: return "decode workspace too small";
+    case FA_EHIP: return "HIP runtime error";
+    case FA_ERANGE: return "positions beyond the cache (pos0 + n > max_seq)";
+    case FA_EDEVICE: return "current device is not gfx950";
+    }
+    return "unknown error code";
+}
+
+}  // extern "C"

@@ -1,0 +1,103 @@
+// KV-cache append: fp32 copy and fp32 -> Q4_0 block quantisation.
+//
+// [FA] fc_attn_kv_append: rows [n][n_kv][hd] land at cache[kv][pos0+t][:].
+// [FA] fc_kvq4_quant_block: per 32-element block, amax fold from 0,
+// d = amax / -8 (negative scale), id = 1/d or 0, code = clamp(rint(x*id)+8,
+// 0, 15) (convert, then +8, then clamp), binary16 d in bytes 0-1 (LE), byte
+// 2+j = code_j | code_{j+16} << 4. Every step is an IEEE fp32 operation
+// (correctly rounded divide, v_rndne for rint, v_cvt_f16_f32 round-to-even),
+// so the bytes equal any other exact implementation of the same steps.
+//
+// One thread owns one 32-element block here (no cross-lane fold), so both
+// launches are plain streaming kernels: each thread reads 128 B of input and
+// writes 18 B (Q4) or 16 B (fp32) with consecutive threads on consecutive
+// addresses.
+#include "fa_device.hpp"
+#include "fa_internal.hpp"
+
+namespace fa {
+namespace {
+
+constexpr int kAppendThreads = 256;
+
+__global__ __launch_bounds__(kAppendThreads) void append_f32_kernel(AppendArgs a) {
+    const int tensor = blockIdx.y;                    // 0: K, 1: V
+    const float *src = tensor ? a.v_new : a.k_new;
+    float *dst = (float *)(tensor ? a.v : a.k);
+    const int c4_per_row = a.head_dim / 4;
+    const int64_t total = (int64_t)a.n * a.n_kv * c4_per_row;
+    const int64_t i = (int64_t)blockIdx.x * kAppendThreads + threadIdx.x;
+    if (i >= total) return;
+    const int c4 = (int)(i % c4_per_row);
+    const int64_t th = i / c4_per_row;                // t * n_kv + h
+    const int h = (int)(th % a.n_kv);
+    const int t = (int)(th / a.n_kv);
+    const f32x4 x = *(const f32x4 *)(src + 4 * i);
+    const int64_t row = (int64_t)h * a.max_seq + a.pos0 + t;
+    *(f32x4 *)(dst + row * a.head_dim + 4 * c4) = x;
+}
+
+__device__ __forceinline__ int clamp_code(int c) {
+    return c < 0 ? 0 : (c > 15 ? 15 : c);
+}
+
+__global__ __launch_bounds__(kAppendThreads) void append_q4_kernel(AppendArgs a) {
+    const int tensor = blockIdx.y;
+    const float *src = tensor ? a.v_new : a.k_new;
+    uint8_t *dst = (uint8_t *)(tensor ? a.v : a.k);
+    const int nb = a.head_dim / kQ4Block;
+    const int64_t total = (int64_t)a.n * a.n_kv * nb;
+    const int64_t i = (int64_t)blockIdx.x * kAppendThreads + threadIdx.x;
+    if (i >= total) return;
+    const int blk = (int)(i % nb);
+    const int64_t th = i / nb;
+    const int h = (int)(th % a.n_kv);
+    const int t = (int)(th / a.n_kv);
+
+    float x[kQ4Block];
+    const f32x4 *xs = (const f32x4 *)(src + i * kQ4Block);
+#pragma unroll
+    for (int c = 0; c < kQ4Block / 4; c++) {
+        const f32x4 v = xs[c];
+        x[4 * c + 0] = v[0];
+        x[4 * c + 1] = v[1];
+        x[4 * c + 2] = v[2];
+        x[4 * c + 3] = v[3];
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kQ4Block; j++)
+        amax = fmaxf(amax, fabsf(x[j]));
+    const float d = amax / -8.0f;
+    const float id = (d != 0.0f) ? 1.0f / d : 0.0f;
+
+    const int rb = q4_row_bytes(a.head_dim);
+    const int64_t row = (int64_t)h * a.max_seq + a.pos0 + t;
+    uint16_t *out = (uint16_t *)(dst + row * rb + blk * kQ4BlockBytes);
+    out[0] = __builtin_bit_cast(uint16_t, (_Float16)d);
+#pragma unroll
+    for (int j = 0; j < kQ4Block / 2; j += 2) {
+        const int c0 = clamp_code((int)rintf(x[j] * id) + 8);
+        const int c1 = clamp_code((int)rintf(x[j + 1] * id) + 8);
+        const int c16 = clamp_code((int)rintf(x[j + 16] * id) + 8);
+        const int c17 = clamp_code((int)rintf(x[j + 17] * id) + 8);
+        const uint32_t b0 = (uint32_t)(c0 | (c16 << 4));
+        const uint32_t b1 = (uint32_t)(c1 | (c17 << 4));
+        out[1 + j / 2] = (uint16_t)(b0 | (b1 << 8));   // bytes 2+j, 3+j (little-endian)
+    }
+}
+
+}  // namespace
+
+hipError_t launch_append(int format, const AppendArgs &a, hipStream_t s) {
+    const int per_row = format == 0 ? a.head_dim / 4 : a.head_dim / kQ4Block;
+    const int64_t total = (int64_t)a.n * a.n_kv * per_row;
+    const dim3 grid((unsigned)((total + kAppendThreads - 1) / kAppendThreads), 2);
+    if (format == 0)
+        hipLaunchKernelGGL(append_f32_kernel, grid, dim3(kAppendThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL(append_q4_kernel, grid, dim3(kAppendThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace fa

@@ -1,0 +1,84 @@
+// Device-side helpers shared by the libfa kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Q4_0 block geometry ([FA] "4-bit KV cache (Q4_0 blocks)"): 32 elements in
+// 18 bytes, a binary16 scale then 16 code bytes (element j low nibble,
+// element j+16 high nibble of byte 2+j).
+constexpr int kQ4Block = 32;
+constexpr int kQ4BlockBytes = 18;
+
+__host__ __device__ constexpr int q4_row_bytes(int head_dim) {
+    return head_dim / kQ4Block * kQ4BlockBytes;
+}
+
+// log2(e): scores are kept in base-2 units (s * log2 e) so the softmax
+// exponentials are single v_exp_f32 instructions.
+constexpr float kLog2e = 1.44269504088896340736f;
+
+__device__ __forceinline__ float half_bits_to_float(uint32_t bits) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(bits & 0xffffu));
+}
+
+__device__ __forceinline__ float fast_exp2(float x) {
+    return __builtin_amdgcn_exp2f(x);   // v_exp_f32; exp2(-inf) = 0
+}
+
+// One code nibble (0..15) as a float: exact.
+__device__ __forceinline__ float nib(uint32_t w, int shift) {
+    return (float)((w >> shift) & 0xfu);
+}
+
+// MFMA wrappers (fp32 inputs, fp32 accumulate).
+//   32x32x2: A[m][k] from lane (m = lane&31, k = lane>>5), B[k][n] from lane
+//   (k = lane>>5, n = lane&31); D[m][n] in lane (n = lane&31), register r
+//   holding m = 8*(r/4) + 4*(lane>>5) + r%4.
+__device__ __forceinline__ f32x16 mfma32(float a, float b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+//   4x4x1, 16 blocks: lane 4*blk+i gives A_blk[i], lane 4*blk+j gives
+//   B_blk[j]; D_blk[i][j] lands in lane 4*blk+j, register i.
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_4x4x1f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+        x = fmaxf(x, __shfl_xor(x, o));
+    return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+        x += __shfl_xor(x, o);
+    return x;
+}
+
+// Orders this wave's LDS writes before its later LDS reads of other lanes'
+// data (a wave's LDS operations execute in order; this stops the compiler
+// from moving them across).
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Key-set membership ([FA] file header): causal, plus sink U recent window
+// when attn_win > 0.
+__device__ __forceinline__ bool in_key_set(int j, int p, int sink, int win) {
+    return j <= p && (win <= 0 || j < sink || j >= p - win + 1);
+}
+
+}  // namespace fa

@@ -1,0 +1,77 @@
+// Internal launcher interface between the C-ABI layer (fa_api.cpp) and the
+// kernel translation units. Arguments reaching these functions have already
+// been validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fa {
+
+struct AppendArgs {
+    const float *k_new, *v_new;   // [n][n_kv][hd]
+    void *k, *v;                  // slot base of the cache: [n_kv][max_seq][row]
+    int n, n_kv, head_dim, max_seq, pos0;
+};
+
+struct PrefillArgs {
+    const float *q;               // [n][n_head][hd]
+    float *out;                   // [n][n_head][hd]
+    const void *k, *v;            // slot base: [n_kv][max_seq][row]
+    unsigned long long *stats;    // NULL or [2]
+    int n, pos0, n_head, n_kv, max_seq;
+    int sink, win;
+    float qscale;                 // scale * log2(e)
+    int n_qblocks;
+};
+
+struct DecodeArgs {
+    const float *q;               // [n_slots][n_head][hd]
+    const int *pos;               // device [n_slots]
+    const void *k, *v;            // cache base: [n_slots_cache][n_kv][max_seq][row]
+    float *ws_m, *ws_l, *ws_acc;  // partials [n_slots*n_head][splits](+[hd])
+    float *out;                   // [n_slots][n_head][hd]
+    unsigned long long *stats;
+    int n_head, n_kv, max_seq;
+    int sink, win;
+    float qscale;
+    int kps, cap;                 // split plan constants
+};
+
+// Geometry of the prefill work-group: 4 waves of 32 (position, head) rows.
+constexpr int kPrefillWaves = 4;
+constexpr int kPrefillRowsPerWave = 32;
+constexpr int kPrefillKeyTile = 32;
+// Decode: 4 waves, each folding tiles of 64 keys (one key per lane).
+constexpr int kDecodeWaves = 4;
+constexpr int kDecodeKeyTile = 64;
+// Split plan constants: about kDecodeKps keys per split, at most
+// kDecodeSplitCap splits per slot.
+constexpr int kDecodeKps = 2048;
+constexpr int kDecodeSplitCap = 16;
+
+inline int prefill_q_positions(int group) {
+    return kPrefillWaves * kPrefillRowsPerWave / group;
+}
+
+hipError_t launch_append(int format, const AppendArgs &a, hipStream_t s);
+hipError_t launch_prefill(int format, int head_dim, int group, const PrefillArgs &a,
+                          hipStream_t s);
+hipError_t launch_decode(int format, int head_dim, int group, const DecodeArgs &a,
+                         int n_slots, int launch_splits, hipStream_t s);
+
+// Host copy of the device plan ([FA] fc_attn_dec_plan).
+__host__ __device__ inline int decode_plan(int seq_len, int kps, int cap, int tile, int *n_splits,
+                       int *split_len) {
+    int n = (seq_len + kps - 1) / kps;
+    if (n < 1) n = 1;
+    if (n > cap) n = cap;
+    int len = (seq_len + n - 1) / n;
+    len = (len + tile - 1) / tile * tile;
+    *n_splits = n;
+    *split_len = len;
+    return (seq_len + len - 1) / len;
+}
+
+}  // namespace fa

@@ -1,0 +1,174 @@
+/*
+ * libfa: causal grouped-query flash attention for AMD Instinct MI355X (gfx950)
+ * over a device-resident KV cache stored as fp32 or as 4-bit Q4_0 blocks.
+ *
+ * Sources cited below:
+ *   [FA] Foundry cuda_kernels/attention.cu (the kernel file this method
+ *        comes from): file header, "4-bit KV cache (Q4_0 blocks)" section,
+ *        fc_kvq4_quant_block, fc_attn_tile_in_window, fc_attn_kv_append,
+ *        fc_attn_flash_prefill, "Decode-mode flash attention" section,
+ *        fc_attn_dec_plan, fc_attn_flash_decode_combine, "Multi-user decode
+ *        attention (slots)" section.
+ *   [VT] vllm-cpp-sys include/vt/ops.h: vt::Attention, AttentionWindow,
+ *        MlaDecodeAttention (split determinism), PagedAttentionArgs
+ *        (host-known max_seq_len hint), kernel registration contract
+ *        (unsupported inputs fail loudly).
+ *
+ * Conventions shared by every entry point:
+ *   - Pointers named k, v, k_new, v_new, q, out, d_pos, ws, tile_stats are
+ *     DEVICE pointers owned by the caller. The library never allocates,
+ *     frees or keeps them after the call returns, and never synchronises.
+ *   - `stream` is a hipStream_t passed as void*; NULL means the default
+ *     stream. All work is enqueued on it, in call order.
+ *   - Every argument is validated on the host before anything is enqueued.
+ *     A rejected call returns a negative FA_E* code and enqueues nothing;
+ *     fa_strerror() names the code. A launch the runtime refuses returns
+ *     FA_EHIP. No C++ exception crosses this interface.
+ *   - Layouts are row-major with the last index fastest.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---------------------------------------------------------------- codes */
+#define FA_OK            0
+#define FA_EINVAL       -1  /* a size, index or scalar is out of its valid range */
+#define FA_ENULL        -2  /* a required pointer is NULL */
+#define FA_EUNSUPPORTED -3  /* valid but not built: head_dim, group size or format */
+#define FA_EWORKSPACE   -4  /* decode workspace smaller than fa_decode_workspace_bytes() */
+#define FA_EHIP         -5  /* the HIP runtime refused a launch or query */
+#define FA_ERANGE       -6  /* positions past the cache (pos0 + n > max_seq) */
+#define FA_EDEVICE      -7  /* current device is not a gfx950 GPU */
+
+/* ----------------------------------------------------------- KV formats */
+/* fp32 rows of head_dim floats. [FA] fc_attn_kv_append. */
+#define FA_KV_F32   0
+/* Q4_0 rows of head_dim/32 blocks of 18 bytes: bytes 0-1 the binary16 scale
+ * d (little-endian, stored negative: d = amax / -8), byte 2+j element j in
+ * the low nibble and element j+16 in the high nibble; code c decodes to
+ * (c - 8) * d. [FA] "4-bit KV cache (Q4_0 blocks)" and fc_kvq4_quant_block. */
+#define FA_KV_Q4_0  1
+
+/* A KV cache of n_slots independent sequences.
+ * k and v each hold [n_slots][n_kv_head][max_seq][row] where row is
+ * fa_cache_row_bytes(format, head_dim) bytes ([FA] slots section: one ring
+ * per slot, each slot's slice laid out like the single-user cache). */
+typedef struct fa_cache {
+    int format;      /* FA_KV_F32 or FA_KV_Q4_0 */
+    int n_slots;     /* >= 1 */
+    int n_kv_head;   /* >= 1 */
+    int head_dim;    /* 64, 128 or 256 */
+    int max_seq;     /* rows per (slot, kv head), >= 1 */
+    void *k;         /* device, fa_cache_bytes() bytes */
+    void *v;         /* device, fa_cache_bytes() bytes */
+} fa_cache;
+
+/* Bytes of one cache row (head_dim*4 for fp32, head_dim/32*18 for Q4_0);
+ * 0 if format or head_dim is invalid. */
+size_t fa_cache_row_bytes(int format, int head_dim);
+
+/* Bytes of the k (or v) tensor of a cache; 0 if a field is invalid. */
+size_t fa_cache_bytes(const fa_cache *cache);
+
+/* Checks that the current HIP device is gfx950. FA_OK or FA_EDEVICE/FA_EHIP.
+ * Every compute entry point calls it once per device. */
+int fa_init(void);
+
+/* ------------------------------------------------------------ KV append */
+/* Writes n new K/V rows of one slot into the cache at positions
+ * pos0 .. pos0+n-1. [FA] fc_attn_kv_append (fp32 copy) and
+ * fc_attn_kv_append_q4 + fc_kvq4_quant_block (Q4_0: per 32-element block,
+ * amax fold, d = amax/-8, id = 1/d or 0, code = clamp(rint(x*id)+8, 0, 15),
+ * binary16 scale), all in IEEE fp32 so the bytes are exactly determined.
+ *   k_new, v_new: device [n][n_kv_head][head_dim] fp32 (finite values).
+ *   slot in [0, n_slots); pos0 >= 0; n >= 0; pos0 + n <= max_seq (the
+ *   cache never wraps: FA_ERANGE otherwise). n == 0 enqueues nothing. */
+int fa_kv_append(const fa_cache *cache, int slot, int pos0, int n,
+                 const float *k_new, const float *v_new, void *stream);
+
+/* -------------------------------------------------------------- prefill */
+/* Causal GQA attention for n query rows of one slot at absolute positions
+ * pos0 .. pos0+n-1, against cache rows [0, pos0+n) of that slot, which must
+ * already be appended. [VT] vt::Attention: for q head h (kv head h/G,
+ * G = n_head / n_kv_head) and query position p,
+ *     s_j = scale * (q . k_j) for j in K(p);  out = sum_j softmax(s)_j v_j
+ * with the key set of the [FA] file header:
+ *     K(p) = {0..p}                                   if attn_win <= 0
+ *     K(p) = {j <= p : j < attn_sink or j >= p-attn_win+1}  otherwise
+ * (attn_win = W is the causal window (W-1, 0) of [VT] AttentionWindow).
+ * The N x N score matrix is never formed: key tiles are folded into a
+ * running max and running sum ([FA] file header), and key tiles that meet
+ * neither the sink nor any row's window are skipped before they are loaded
+ * ([FA] fc_attn_tile_in_window).
+ *   q:   device [n][n_head][head_dim] fp32.  out: device, same shape.
+ *   n_head % n_kv_head == 0, G in {1,2,4,8}; head_dim in {64,128,256};
+ *   scale finite and > 0 (applied to q.k); attn_sink < 0 acts as 0.
+ *   tile_stats: NULL, or device uint64[2] to which the call ADDS the number
+ *   of key tiles it visited ([0]) and window-skipped ([1]); tile geometry
+ *   from fa_prefill_tile_shape(). Tiles past the causal bound are neither.
+ * Rows of q and out must not overlap. */
+int fa_prefill(const fa_cache *cache, int slot, const float *q, int pos0, int n,
+               int n_head, int attn_sink, int attn_win, float scale, float *out,
+               unsigned long long *tile_stats, void *stream);
+
+/* Tile geometry fa_prefill uses for a shape: each work-group owns
+ * *q_positions consecutive query positions (from pos0) of one kv head and
+ * walks key tiles of *key_tile keys from key 0. FA_OK or FA_EUNSUPPORTED. */
+int fa_prefill_tile_shape(int n_head, int n_kv_head, int head_dim,
+                          int *q_positions, int *key_tile);
+
+/* --------------------------------------------------------------- decode */
+/* Split plan of one slot with seq_len = pos + 1 keys. [FA] fc_attn_dec_plan:
+ *   n = clamp(ceil(seq_len / kps), 1, cap); split_len = ceil(seq_len / n)
+ *   rounded up to a multiple of the decode key tile; returns the live split
+ *   count ceil(seq_len / split_len) (or FA_EINVAL if seq_len < 1).
+ * kps, cap and the key tile are the library's constants
+ * (fa_decode_plan_params); the device computes the same plan per slot. */
+int fa_decode_plan(int seq_len, int *n_splits, int *split_len);
+void fa_decode_plan_params(int *kps, int *cap, int *key_tile);
+
+/* Workspace for fa_decode: per (slot, head, launched split) one partial
+ * {m, l, acc[head_dim]} fp32 ([FA] "Decode-mode flash attention": partial
+ * running max, running sum and unnormalised accumulator). The launch width
+ * is the live split count of max_ctx. 0 if an argument is invalid. */
+size_t fa_decode_workspace_bytes(const fa_cache *cache, int n_slots, int n_head,
+                                 int max_ctx);
+
+/* One decode step for slots 0..n_slots-1: the query row of slot s sits at
+ * position d_pos[s] and attends K(d_pos[s]) of that slot's cache (its own
+ * row already appended). Two launches on `stream` ([FA] "Decode-mode flash
+ * attention" and slots sections): a partial pass over (split, kv head, slot)
+ * whose per-slot plan is computed on the device from d_pos[s]; splits a slot
+ * does not use write empty partials (m = -inf, l = 0, acc = 0). Then a combine
+ * pass per (slot, head): M = max_s m_s, out = sum_s w_s acc_s / sum_s w_s l_s
+ * with w_s = exp(m_s - M), splits in ascending order, no atomics, so a fixed
+ * launch gives bit-identical results ([VT] MlaDecodeAttention determinism).
+ *   q, out: device [n_slots][n_head][head_dim] fp32.
+ *   d_pos:  device int32[n_slots]. A value outside [0, max_seq) reads no
+ *           memory and makes that slot's output rows NaN.
+ *   max_ctx_hint: host upper bound on d_pos[s]+1, 1..max_seq ([VT]
+ *           PagedAttentionArgs max_seq_len: sizes the grid without a device
+ *           read). A slot with more keys than the hint is still computed
+ *           exactly; it is only spread over fewer work-groups.
+ *   ws, ws_bytes: device scratch of at least
+ *           fa_decode_workspace_bytes(cache, n_slots, n_head, max_ctx_hint).
+ *   tile_stats: as in fa_prefill, decode key tiles of the plan's tile size.
+ * n_slots == 0 enqueues nothing. Other rules as fa_prefill. */
+int fa_decode(const fa_cache *cache, const float *q, const int *d_pos, int n_slots,
+              int max_ctx_hint, int n_head, int attn_sink, int attn_win, float scale,
+              float *out, void *ws, size_t ws_bytes, unsigned long long *tile_stats,
+              void *stream);
+
+/* Message for a return code (static storage). */
+const char *fa_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

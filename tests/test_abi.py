@@ -1,0 +1,143 @@
+"""Host-side checks of libfa that need no GPU: the library loads, exports every
+entry point include/fa.h declares, validates arguments before touching the
+device, and its plan / geometry helpers agree with the oracle.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import causal_gqa_flash_fa_amd as fa
+import oracle
+from tests.conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "fa.h")
+FAKE = 0x10000   # never dereferenced: every call below is refused before any launch
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_function_is_exported():
+    names = declared_functions()
+    assert len(names) >= 10
+    for name in names:
+        assert hasattr(fa.lib, name), name          # ctypes lookup of the exported symbol
+    assert sorted(fa.EXPORTS) == names
+
+
+def test_strerror_names_every_code():
+    for code in range(0, -8, -1):
+        assert fa.fa_strerror(code) != "unknown error code"
+    assert fa.fa_strerror(-99) == "unknown error code"
+
+
+def cache(fmt=fa.FA_KV_F32, n_slots=2, n_kv=2, hd=128, max_seq=100, k=FAKE, v=FAKE):
+    return fa.fa_cache(fmt, n_slots, n_kv, hd, max_seq, k, v)
+
+
+def rc_append(c, slot=0, pos0=0, n=1, kn=FAKE, vn=FAKE):
+    return fa.lib.fa_kv_append(ctypes.byref(c) if c is not None else None, slot, pos0, n, kn, vn,
+                               None)
+
+
+def rc_prefill(c, slot=0, q=FAKE, pos0=0, n=1, n_head=4, sink=0, win=0, scale=0.1, out=FAKE):
+    return fa.lib.fa_prefill(ctypes.byref(c) if c is not None else None, slot, q, pos0, n,
+                             n_head, sink, win, scale, out, None, None)
+
+
+def rc_decode(c, q=FAKE, pos=FAKE, n_slots=1, hint=10, n_head=4, scale=0.1, out=FAKE, ws=FAKE,
+              ws_bytes=1 << 30):
+    return fa.lib.fa_decode(ctypes.byref(c) if c is not None else None, q, pos, n_slots, hint,
+                            n_head, 0, 0, scale, out, ws, ws_bytes, None, None)
+
+
+def test_row_and_cache_bytes():
+    assert fa.fa_cache_row_bytes(fa.FA_KV_F32, 256) == 1024
+    assert fa.fa_cache_row_bytes(fa.FA_KV_Q4_0, 256) == 144
+    assert fa.fa_cache_row_bytes(fa.FA_KV_Q4_0, 64) == 36
+    assert fa.fa_cache_row_bytes(fa.FA_KV_Q4_0, 96) == 0
+    assert fa.fa_cache_row_bytes(7, 128) == 0
+    assert fa.fa_cache_bytes(cache(fa.FA_KV_Q4_0, 3, 2, 256, 32768)) == 3 * 2 * 32768 * 144
+    assert fa.fa_cache_bytes(cache(n_slots=0)) == 0
+
+
+def test_append_validation():
+    assert rc_append(None) == fa.FA_ENULL
+    assert rc_append(cache(hd=96)) == fa.FA_EUNSUPPORTED
+    assert rc_append(cache(fmt=5)) == fa.FA_EUNSUPPORTED
+    assert rc_append(cache(k=0)) == fa.FA_ENULL
+    assert rc_append(cache(max_seq=0)) == fa.FA_EINVAL
+    assert rc_append(cache(), slot=2) == fa.FA_EINVAL
+    assert rc_append(cache(), slot=-1) == fa.FA_EINVAL
+    assert rc_append(cache(), pos0=-1) == fa.FA_EINVAL
+    assert rc_append(cache(), n=-1) == fa.FA_EINVAL
+    assert rc_append(cache(), pos0=90, n=11) == fa.FA_ERANGE      # would wrap: refused
+    assert rc_append(cache(), pos0=0, n=0) == fa.FA_OK            # empty: nothing enqueued
+    assert rc_append(cache(), pos0=100, n=0) == fa.FA_OK
+    assert rc_append(cache(), kn=0) == fa.FA_ENULL
+
+
+def test_prefill_validation():
+    c = cache()
+    assert rc_prefill(None) == fa.FA_ENULL
+    assert rc_prefill(c, n_head=3) == fa.FA_EINVAL                 # not a multiple of n_kv
+    assert rc_prefill(c, n_head=32) == fa.FA_EUNSUPPORTED          # group 16
+    assert rc_prefill(c, n_head=6) == fa.FA_EUNSUPPORTED           # group 3
+    assert rc_prefill(c, scale=0.0) == fa.FA_EINVAL
+    assert rc_prefill(c, scale=-1.0) == fa.FA_EINVAL
+    assert rc_prefill(c, scale=float("nan")) == fa.FA_EINVAL
+    assert rc_prefill(c, scale=float("inf")) == fa.FA_EINVAL
+    assert rc_prefill(c, slot=5) == fa.FA_EINVAL
+    assert rc_prefill(c, pos0=50, n=51) == fa.FA_ERANGE
+    assert rc_prefill(c, n=0) == fa.FA_OK
+    assert rc_prefill(c, q=0) == fa.FA_ENULL
+    assert rc_prefill(c, out=0) == fa.FA_ENULL
+
+
+def test_decode_validation():
+    c = cache(n_slots=4, max_seq=100)
+    need = fa.fa_decode_workspace_bytes(c, 4, 4, 100)
+    assert need == 4 * 4 * fa.fa_decode_plan(100)[0] * (128 + 2) * 4
+    assert rc_decode(None) == fa.FA_ENULL
+    assert rc_decode(c, n_slots=5) == fa.FA_EINVAL
+    assert rc_decode(c, hint=0) == fa.FA_EINVAL
+    assert rc_decode(c, hint=101) == fa.FA_EINVAL
+    assert rc_decode(c, n_head=8, scale=0.0) == fa.FA_EINVAL
+    assert rc_decode(c, n_slots=4, hint=100, ws_bytes=need - 1) == fa.FA_EWORKSPACE
+    assert rc_decode(c, n_slots=0) == fa.FA_OK
+    assert rc_decode(c, ws=0) == fa.FA_ENULL
+    assert rc_decode(c, pos=0) == fa.FA_ENULL
+
+
+def test_plan_matches_oracle_with_library_constants():
+    kps, cap, tile = fa.fa_decode_plan_params()
+    assert tile == 64 and kps >= tile and cap >= 1
+    for L in list(range(1, 200)) + [4096, 4097, 20000, 32767, 32768, 65536]:
+        assert fa.fa_decode_plan(L) == oracle.decode_plan(L, kps, cap, tile)
+    assert fa.lib.fa_decode_plan(0, None, None) == fa.FA_EINVAL
+
+
+def test_prefill_tile_shape():
+    assert fa.fa_prefill_tile_shape(16, 2, 256) == (16, 32)
+    assert fa.fa_prefill_tile_shape(4, 1, 64) == (32, 32)
+    assert fa.fa_prefill_tile_shape(8, 8, 128) == (128, 32)
+    with pytest.raises(fa.FaError):
+        fa.fa_prefill_tile_shape(16, 2, 96)
+
+
+def gpu_count():
+    import torch
+    return torch.cuda.device_count()
+
+
+@pytest.mark.skipif(gpu_count() > 0, reason="only meaningful where no GPU is present")
+def test_valid_call_without_a_gpu_fails_loudly():
+    rc = rc_prefill(cache())
+    assert rc in (fa.FA_EHIP, fa.FA_EDEVICE)
+    with pytest.raises(fa.FaError):
+        fa.fa_init()
