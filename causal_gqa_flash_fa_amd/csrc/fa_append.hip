@@ -74,7 +74,11 @@ __global__ __launch_bounds__(kAppendThreads) void append_q4_kernel(AppendArgs a)
     const int rb = q4_row_bytes(a.head_dim);
     const int64_t row = (int64_t)h * a.max_seq + a.pos0 + t;
     uint16_t *out = (uint16_t *)(dst + row * rb + blk * kQ4BlockBytes);
-    out[0] = __builtin_bit_cast(uint16_t, (_Float16)d);
+    // A zero scale is stored as binary16 -0.0 (0x8000), the sign of amax/-8.
+    // Spelled out because the compiler folds the divide-by-(-8) and the fp16
+    // conversion into one fused multiply-add whose +0 addend would turn -0
+    // into +0.
+    out[0] = d == 0.0f ? (uint16_t)0x8000u : __builtin_bit_cast(uint16_t, (_Float16)d);
 #pragma unroll
     for (int j = 0; j < kQ4Block / 2; j += 2) {
         const int c0 = clamp_code((int)rintf(x[j] * id) + 8);
