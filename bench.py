@@ -1,0 +1,267 @@
+#!/usr/bin/env python3
+"""Benchmark of the causal GQA flash-attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Prints ONE JSON line. The headline step is the prefill-f32kv-2k workload
+(2048 query rows, 16 q heads / 2 kv heads, head_dim 256, fp32 KV, full
+causal): fa_kv_append of the 2048 K/V rows followed by fa_prefill, inputs
+resident in HBM. `value` is key-set-counted prefill FLOPs (4*head_dim per
+attended (query, head, key)) per second of step time. The same line carries
+the other workloads as `legs` (Q4_0 8k prefill, 32k sliding-window prefill,
+64-slot Q4_0 decode), a `roofline` object for the dominant kernel (timed with
+HIP events on the launch stream) and the CPU oracle timed on the host cores
+as `cpu_baseline`.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+METRIC = "prefill causal attn TFLOP/s + decode KV-read GB/s (fraction of roofline)"
+PEAK_FP32_MFMA_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+
+
+def keyset_pairs(n: int, pos0: int, sink: int, win: int) -> int:
+    """Sum over query positions p of |K(p)| (attended keys of one q head)."""
+    p = np.arange(pos0, pos0 + n, dtype=np.int64)
+    if win <= 0:
+        return int((p + 1).sum())
+    lo = np.maximum(0, p - win + 1)
+    sink = max(sink, 0)
+    return int(np.minimum(p + 1, np.minimum(sink, lo) + (p - lo + 1)).sum())
+
+
+def prefill_flops(w) -> float:
+    return 4.0 * w.head_dim * w.n_head * keyset_pairs(w.n, w.pos0, w.attn_sink, w.attn_win)
+
+
+def _events(torch, n):
+    return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(n)]
+
+
+def prefill_leg(fa, torch, w, steps: int, warmup: int) -> dict:
+    dev = torch.device("cuda:0")
+    q = torch.from_numpy(workloads.prefill_q(w)).to(dev)
+    k_np, v_np = workloads.prefill_kv(w)
+    kd, vd = torch.from_numpy(k_np).to(dev), torch.from_numpy(v_np).to(dev)
+    del k_np, v_np
+    cache, kt, vt = fa.make_cache(w.kv_format, 1, w.n_kv_head, w.head_dim, w.max_seq, dev)
+    out = torch.empty_like(q)
+    rows = w.pos0 + w.n
+    ev = _events(torch, steps)
+
+    def step(i=None):
+        fa.fa_kv_append(cache, 0, 0, rows, kd, vd)
+        if i is not None:
+            ev[i][0].record()
+        fa.fa_prefill(cache, 0, q, w.pos0, w.n, w.n_head, w.attn_sink, w.attn_win, w.scale, out)
+        if i is not None:
+            ev[i][1].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kms = [a.elapsed_time(b) for a, b in ev]
+    flops = prefill_flops(w)
+    step_ms = (t1 - t0) * 1e3 / steps
+    kern_ms = float(np.mean(kms))
+    return {
+        "workload": w.name, "kind": "prefill", "kv": "q4_0" if w.kv_format else "f32",
+        "n": w.n, "n_head": w.n_head, "n_kv_head": w.n_kv_head, "head_dim": w.head_dim,
+        "attn_sink": w.attn_sink, "attn_win": w.attn_win,
+        "flops": flops, "ms_per_step": step_ms, "tflops_step": flops / step_ms / 1e9,
+        "prefill_kernel_ms": kern_ms, "prefill_kernel_ms_min": float(np.min(kms)),
+        "tflops_kernel": flops / kern_ms / 1e9,
+        "frac_fp32_mfma_peak": flops / kern_ms / 1e9 / PEAK_FP32_MFMA_TFLOPS,
+    }
+
+
+def decode_leg(fa, torch, w, steps: int, warmup: int) -> dict:
+    dev = torch.device("cuda:0")
+    ctx = workloads.decode_ctx(w)
+    cache, kt, vt = fa.make_cache(w.kv_format, w.n_slots, w.n_kv_head, w.head_dim, w.max_seq, dev)
+    for s in range(w.n_slots):
+        k, v = workloads.decode_kv(w, s, int(ctx[s]))
+        fa.fa_kv_append(cache, s, 0, int(ctx[s]), torch.from_numpy(k).to(dev),
+                        torch.from_numpy(v).to(dev))
+    q = torch.from_numpy(workloads.decode_q(w)).to(dev)
+    pos = torch.from_numpy(ctx - 1).to(dev)
+    out = torch.empty_like(q)
+    hint = int(ctx.max())
+    ws_bytes = fa.fa_decode_workspace_bytes(cache, w.n_slots, w.n_head, hint)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)   # > 256 MB last-level cache
+    ev = _events(torch, steps)
+
+    def step(i=None):
+        if i is not None:
+            ev[i][0].record()
+        fa.fa_decode(cache, q, pos, w.n_slots, hint, w.n_head, 0, 0, w.scale, out, ws, ws_bytes)
+        if i is not None:
+            ev[i][1].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    for i in range(steps):
+        flush.zero_()          # evict the KV cache from L2 / MALL between reps (not timed)
+        step(i)
+    torch.cuda.synchronize()
+    kms = [a.elapsed_time(b) for a, b in ev]
+    ms = float(np.mean(kms))
+    row_bytes = w.head_dim // 32 * 18 if w.kv_format else w.head_dim * 4
+    kv_bytes = int(ctx.sum()) * w.n_kv_head * 2 * row_bytes
+    qo_bytes = 2 * w.n_slots * w.n_head * w.head_dim * 4
+    flops = 4.0 * w.head_dim * w.n_head * float(ctx.sum())
+    gbs = (kv_bytes + qo_bytes) / ms / 1e6
+    compute_ceiling_gbs = PEAK_FP32_MFMA_TFLOPS * 1e12 / (flops / (kv_bytes + qo_bytes)) / 1e9
+    return {
+        "workload": w.name, "kind": "decode", "kv": "q4_0" if w.kv_format else "f32",
+        "n_slots": w.n_slots, "ctx_sum": int(ctx.sum()), "ctx_min": int(ctx.min()),
+        "ctx_max": int(ctx.max()), "launch_splits": fa.fa_decode_plan(hint)[0],
+        "kv_bytes": kv_bytes, "bytes": kv_bytes + qo_bytes, "flops": flops,
+        "decode_ms": ms, "decode_ms_min": float(np.min(kms)), "gbs": gbs,
+        "frac_hbm_peak": gbs / PEAK_HBM_GBS, "tflops": flops / ms / 1e9,
+        "fp32_compute_ceiling_gbs": compute_ceiling_gbs,
+        "frac_of_min_ceiling": gbs / min(PEAK_HBM_GBS, compute_ceiling_gbs),
+    }
+
+
+def cpu_baseline(w) -> dict:
+    """The oracle (plain C, double precision, single-threaded per call) over
+    every row of the workload, rows spread over the host's cores."""
+    import oracle
+    q = workloads.prefill_q(w)
+    k, v = workloads.prefill_kv(w)
+    kt = np.ascontiguousarray(k.transpose(1, 0, 2))
+    vt = np.ascontiguousarray(v.transpose(1, 0, 2))
+    if w.kv_format:
+        kt = oracle.q4_dequantize(oracle.q4_quantize(kt), w.head_dim)
+        vt = oracle.q4_dequantize(oracle.q4_quantize(vt), w.head_dim)
+    threads = min(16, os.cpu_count() or 1)
+    t0 = time.perf_counter()
+    oracle.prefill(q, kt, vt, w.pos0, w.attn_sink, w.attn_win, w.scale, threads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": prefill_flops(w) / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle", "seconds": dt,
+            "sample": f"all {w.n * w.n_head} rows of {w.name} (fp64 global-max softmax)"}
+
+
+def copy_calibration(torch, nbytes: int = 1 << 30) -> dict:
+    """A plain device copy of known size, for scaling HBM byte counters."""
+    x = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+    y = torch.empty_like(x)
+    x.fill_(1)
+    torch.cuda.synchronize()
+    y.copy_(x)
+    torch.cuda.synchronize()
+    return {"copy_bytes_read": nbytes, "copy_bytes_written": nbytes}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--legs", default="prefill-q4kv-8k,window-prefill-32k,decode-64slots-q4kv",
+                    help="comma-separated extra workloads ('' for none)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a 1 GiB device copy (for counter scaling)")
+    ap.add_argument("--only", default="",
+                    help="run just this workload and print its leg as the JSON line "
+                         "(for profiling one kernel)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    import causal_gqa_flash_fa_amd as fa
+    torch.cuda.set_device(0)
+    fa.fa_init()
+
+    if args.only:
+        w = workloads.BY_NAME[args.only]
+        leg = (prefill_leg if w.kind == "prefill" else decode_leg)(fa, torch, w, args.steps,
+                                                                   args.warmup)
+        if args.copy_calibration:
+            leg["copy_calibration"] = copy_calibration(torch)
+        print(json.dumps(leg), flush=True)
+        return 0
+
+    head = workloads.BY_NAME["prefill-f32kv-2k"]
+    print(f"[bench] {head.name}: warmup {args.warmup}, steps {args.steps}", file=sys.stderr,
+          flush=True)
+    main_leg = prefill_leg(fa, torch, head, args.steps, args.warmup)
+    legs = []
+    for name in [s for s in args.legs.split(",") if s]:
+        w = workloads.BY_NAME[name]
+        print(f"[bench] leg {name}", file=sys.stderr, flush=True)
+        if w.kind == "prefill":
+            legs.append(prefill_leg(fa, torch, w, args.steps, args.warmup))
+        else:
+            legs.append(decode_leg(fa, torch, w, args.steps, args.warmup))
+        torch.cuda.empty_cache()
+    extra = {}
+    if args.copy_calibration:
+        extra["copy_calibration"] = copy_calibration(torch)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(head)
+
+    kern_tflops = main_leg["tflops_kernel"]
+    line = {
+        "metric": METRIC,
+        "value": round(main_leg["tflops_step"], 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(main_leg["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": head.name, "n": head.n, "pos0": head.pos0,
+                   "n_head": head.n_head, "n_kv_head": head.n_kv_head,
+                   "head_dim": head.head_dim, "kv": "f32", "attn_sink": head.attn_sink,
+                   "attn_win": head.attn_win, "step": "fa_kv_append + fa_prefill"},
+        "roofline": {"bound": "mfma", "kernel": "prefill_kernel<256,8,f32>",
+                     "achieved": round(kern_tflops, 3), "peak": PEAK_FP32_MFMA_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(kern_tflops / PEAK_FP32_MFMA_TFLOPS, 4),
+                     "traffic": None,
+                     "kernel_ms": round(main_leg["prefill_kernel_ms"], 5),
+                     "flops_per_launch": main_leg["flops"]},
+        "cpu_baseline": cpu,
+        "legs": legs,
+        **extra,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
