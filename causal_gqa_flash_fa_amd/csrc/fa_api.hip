@@ -151,11 +151,37 @@ int fa_decode_plan(int seq_len, int *n_splits, int *split_len) {
     return live;
 }
 
+namespace {
+// Decode work distribution for a launch: waves and the workspace layout.
+struct DecodeLayout {
+    int waves;
+    size_t max_partials, table_bytes, m_off, l_off, acc_off, total;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+DecodeLayout decode_layout(const fa_cache *c, int n_slots, int n_head, int max_ctx) {
+    DecodeLayout d;
+    const size_t nsegs = (size_t)n_slots * c->n_kv_head;
+    const int group = n_head / c->n_kv_head;
+    const size_t items = nsegs * (size_t)fa_decode_plan(max_ctx, nullptr, nullptr);
+    d.waves = (int)(items < (size_t)fa::kDecodeMaxWaves ? (items ? items : 1)
+                                                        : (size_t)fa::kDecodeMaxWaves);
+    d.max_partials = nsegs + (size_t)d.waves;   // each run boundary adds at most one partial
+    d.table_bytes = align256(nsegs * 2 * sizeof(int));
+    d.m_off = d.table_bytes;
+    d.l_off = d.m_off + align256(d.max_partials * group * sizeof(float));
+    d.acc_off = d.l_off + align256(d.max_partials * group * sizeof(float));
+    d.total = d.acc_off + d.max_partials * group * (size_t)c->head_dim * sizeof(float);
+    return d;
+}
+}  // namespace
+
 size_t fa_decode_workspace_bytes(const fa_cache *cache, int n_slots, int n_head, int max_ctx) {
-    if (!cache || !dim_ok(cache->head_dim) || n_slots < 0 || n_head < 1 || max_ctx < 1)
+    if (!cache || !dim_ok(cache->head_dim) || cache->n_kv_head < 1 || n_slots < 0 ||
+        n_head < 1 || n_head % cache->n_kv_head || max_ctx < 1)
         return 0;
-    const int splits = fa_decode_plan(max_ctx, nullptr, nullptr);
-    return (size_t)n_slots * n_head * splits * (cache->head_dim + 2) * sizeof(float);
+    return decode_layout(cache, n_slots, n_head, max_ctx).total;
 }
 
 int fa_decode(const fa_cache *cache, const float *q, const int *d_pos, int n_slots,
@@ -170,21 +196,22 @@ int fa_decode(const fa_cache *cache, const float *q, const int *d_pos, int n_slo
     if (max_ctx_hint < 1 || max_ctx_hint > cache->max_seq) return FA_EINVAL;
     if (n_slots == 0) return FA_OK;
     if (!q || !d_pos || !out || !ws) return FA_ENULL;
-    if (ws_bytes < fa_decode_workspace_bytes(cache, n_slots, n_head, max_ctx_hint))
-        return FA_EWORKSPACE;
+    const DecodeLayout lay = decode_layout(cache, n_slots, n_head, max_ctx_hint);
+    if (ws_bytes < lay.total) return FA_EWORKSPACE;
     if ((rc = fa_init())) return rc;
-    const int splits = fa_decode_plan(max_ctx_hint, nullptr, nullptr);
-    const size_t parts = (size_t)n_slots * n_head * splits;
+    uint8_t *wsb = (uint8_t *)ws;
     fa::DecodeArgs a;
     a.q = q;
     a.pos = d_pos;
     a.k = cache->k;
     a.v = cache->v;
-    a.ws_m = (float *)ws;
-    a.ws_l = a.ws_m + parts;
-    a.ws_acc = a.ws_l + parts;
+    a.seg_table = (int *)wsb;
+    a.ws_m = (float *)(wsb + lay.m_off);
+    a.ws_l = (float *)(wsb + lay.l_off);
+    a.ws_acc = (float *)(wsb + lay.acc_off);
     a.out = out;
     a.stats = tile_stats;
+    a.n_slots = n_slots;
     a.n_head = n_head;
     a.n_kv = cache->n_kv_head;
     a.max_seq = cache->max_seq;
@@ -194,7 +221,7 @@ int fa_decode(const fa_cache *cache, const float *q, const int *d_pos, int n_slo
     a.kps = fa::kDecodeKps;
     a.cap = fa::kDecodeSplitCap;
     return hip_rc(fa::launch_decode(cache->format, cache->head_dim, n_head / cache->n_kv_head,
-                                    a, n_slots, splits, (hipStream_t)stream));
+                                    a, lay.waves, (hipStream_t)stream));
 }
 
 const char *fa_strerror(int code) {

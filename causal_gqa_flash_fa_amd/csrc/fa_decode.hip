@@ -1,31 +1,52 @@
-// Multi-slot split-KV decode on fp32 MFMA (gfx950): a partial pass over
-// (split, kv head, slot) and a combine pass over (slot, head).
+// Multi-slot split-KV decode on fp32 MFMA (gfx950): a partial pass that folds
+// key tiles into partials {m, l, acc}, and a combine pass over (slot, head).
 //
 // Method ([FA] "Decode-mode flash attention", fc_attn_dec_plan and the
 // "Multi-user decode attention" section): each slot's keys [0, pos] are cut
-// into splits by a plan computed from that slot's own position; each split
-// folds its tiles into a partial {running max m, running sum l, unnormalised
-// accumulator acc}; splits past a slot's plan write empty partials
-// (m = -inf, l = 0, acc = 0); the combine rescales every partial by
-// exp(m_s - M) and divides, splits in ascending order.
+// into splits by a plan computed on the device from that slot's own
+// position; a partial holds the running max m, running sum l and the
+// unnormalised accumulator acc of the keys it folded; the combine rescales
+// every partial of a (slot, head) by exp(m_s - M) and divides, in ascending
+// order, with no atomics.
 //
-// MI355X layout of the work: with one query row per slot the GQA group has
-// only G (<= 8) rows, far too few for 32x32 or 16x16 MFMA tiles. This kernel
-// uses v_mfma_f32_4x4x1f32 (16 blocks of 4x4x1, same 64 FLOP/clk/SIMD rate)
-// with the keys spread across the 16 blocks:
-//   * QK: lane = key (64 keys per wave tile). Every block receives the same
-//     4 q-head values (A, from LDS, broadcast) and its 4 keys' K values (B,
-//     decoded in registers), so one instruction scores 64 keys x 4 heads for
-//     one contraction element and all G heads reuse each decoded K element.
-//   * PV: lane = output dims. Every block receives the same 4 heads'
-//     probabilities for one key (A, from a per-wave LDS copy of P) and 4 of
-//     that key's V values (B), so one instruction adds one key's V row into
-//     64 dims x 4 heads.
-// Both contractions keep every MFMA row busy. The 4 waves of a work-group
-// take interleaved 64-key tiles of the split, keep independent (m, l, acc)
-// and merge them through LDS before writing the split's partial.
-// Scores are kept in base-2 units (q pre-scaled by scale*log2 e), so the
-// partial m is log2-scaled and the combine uses exp2.
+// MI355X schedule (stream-K over the splits): the splits of all (slot, kv
+// head) segments, in order, form one list of work items; a fixed grid of
+// single-wave work-groups takes equal contiguous runs of that list. A wave
+// folds every split of one segment that falls in its run into one running
+// state (consecutive splits are consecutive keys), so it writes one partial
+// per segment it touches. Every wave gets the same amount of work whatever
+// the context lengths, no work-group sits idle, and a wave streams many tiles
+// between its prologue and its partial write. The list and the partial
+// offsets are recomputed by every wave from the device positions; wave 0
+// also writes the per-segment partial table that the combine reads.
+//
+// MFMA layout: one query row per slot leaves only G (<= 8) rows per kv head,
+// too few for 32x32 or 16x16 tiles, so both contractions use
+// v_mfma_f32_4x4x1f32 (16 blocks of 4x4x1, full fp32 rate on gfx950):
+//   * QK: lane = key (64-key tiles). Every block gets the same 4 q-head
+//     values (A, broadcast from LDS) and its 4 keys' K values (B, decoded in
+//     registers): one instruction scores 64 keys x 4 heads for one
+//     contraction element, and all G heads reuse each decoded K element.
+//   * PV: lanes = output dims. Every block gets the same 4 heads'
+//     probabilities of one key (A, from an LDS copy of P) and that key's V
+//     values for its 4 dims (B).
+// Scores are kept in base-2 units (q pre-scaled by scale*log2 e), so partial
+// m values are log2-scaled and the combine uses exp2.
+//
+// Q4_0 tiles: the next tile's K and V bytes (64 contiguous rows each) are
+// fetched with coalesced loads into registers while the current tile
+// computes, then go through a per-wave LDS buffer (K first: each lane reads
+// back its own key's row; then V). A code nibble c becomes (c - 8) * d with
+// one v_fma_mix_f32: the nibble is placed in a binary16 whose value is
+// 1024 + c, and (1024 + c) * d - 1032 * d is exact. PV takes two keys per
+// instruction (lanes 0-31 even keys, 32-63 odd keys), each lane owning dims
+// that share one block's code bytes; the two halves are summed at the end.
+// fp32 tiles: each lane reads its key's K row and, in PV, 4 dims of each V
+// row straight from memory.
+//
+// The running max is recomputed across the wave only when some score exceeds
+// it by more than 8 (base-2 units); any reference max gives the same
+// softmax, and the bound keeps every exp2(s - m) <= 256.
 #include "fa_device.hpp"
 #include "fa_internal.hpp"
 
@@ -33,353 +54,494 @@ namespace fa {
 namespace {
 
 template <int HD, int G, int FMT>
-struct DecodeShape {
-    static constexpr int W = kDecodeWaves;
-    static constexpr int BKD = kDecodeKeyTile;   // keys per wave tile (one per lane)
-    static constexpr int NHG = (G + 3) / 4;      // groups of 4 q heads
-    static constexpr int HP = NHG * 4;           // padded head count
-    static constexpr int VPL = HD / 64;          // V values (output dims) per lane
+struct DShape {
+    static constexpr int BKD = kDecodeKeyTile;      // keys per tile, one per lane in QK
+    static constexpr int NHG = (G + 3) / 4;         // groups of 4 q heads
+    static constexpr int HP = NHG * 4;              // padded head count
+    static constexpr int QS = HD + 4;               // padded LDS rows: broadcast reads hit distinct banks
+    static constexpr int PS = BKD + 4;
     static constexpr int NB = HD / kQ4Block;
     static constexpr int RB = FMT == 0 ? HD * 4 : NB * kQ4BlockBytes;
+    static constexpr int CB = FMT == 0 ? 16 : RB / 9;   // Q4: 9 chunks of 16 / 8 / 4 bytes per row
+    static constexpr int TILE_BYTES = FMT == 0 ? 16 : BKD * RB;
+    static constexpr int LPB = 32 / NB;             // Q4 PV: lanes per block per half-wave
+    static constexpr int BPL = 16 / LPB;            // Q4 PV: code bytes per lane (4 / 2 / 1)
+    static constexpr int OD = FMT == 0 ? HD / 64 : 2 * BPL;   // output dims per lane
 };
 
-// Output dim held by `lane` for its c-th PV accumulator. fp32 rows: plain
-// stride 64. Q4_0 rows: the dims a lane owns share one or two code bytes of
-// one block, so its V values come from a single 2-byte (or 1-byte) read.
+template <int CB> struct Chunk;
+template <> struct Chunk<16> { typedef u32x4 T; };
+template <> struct Chunk<8> { typedef u32x2 T; };
+template <> struct Chunk<4> { typedef uint32_t T; };
+
+// Output dim of accumulator c in `lane`.
 template <int HD, int FMT>
-__device__ __forceinline__ int pv_dim(int lane, int c) {
+__device__ __forceinline__ int o_dim(int lane, int c) {
     if constexpr (FMT == 0) {
         return lane + 64 * c;
-    } else if constexpr (HD == 256) {
-        const int bb = lane >> 3, jj = 2 * (lane & 7);
-        const int off[4] = {0, 1, 16, 17};
-        return 32 * bb + jj + off[c];
-    } else if constexpr (HD == 128) {
-        return 32 * (lane >> 4) + (lane & 15) + 16 * c;
     } else {
-        return lane;
+        using Sh = DShape<HD, 1, 1>;
+        const int ll = lane & 31;
+        const int bb = ll / Sh::LPB, jb = (ll % Sh::LPB) * Sh::BPL;
+        return bb * kQ4Block + jb + (c < Sh::BPL ? c : 16 + c - Sh::BPL);
     }
 }
 
+__device__ __forceinline__ float byte_f(uint32_t w, int t) {
+    return (float)((w >> (8 * t)) & 0xffu);   // v_cvt_f32_ubyte{t}
+}
+
+// Two nibbles of w (bits sh..sh+3 and sh+16..sh+19) as binary16 values 1024+c.
+__device__ __forceinline__ uint32_t nib_pair(uint32_t w, int sh) {
+    return ((w >> sh) & 0x000f000fu) | 0x64006400u;
+}
+__device__ __forceinline__ float lo_h(uint32_t r) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(r & 0xffffu));
+}
+__device__ __forceinline__ float hi_h(uint32_t r) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(r >> 16));
+}
+
+__device__ __forceinline__ int wave_sum_i(int x) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+    return x;
+}
+__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+    }
+    return x;
+}
+
+// Items (splits) of a slot whose query sits at `pos`; 0 for a position
+// outside the cache.
+__device__ __forceinline__ int slot_items(int pos, const DecodeArgs &a, int *split_len) {
+    if (pos < 0 || pos >= a.max_seq) {
+        *split_len = kDecodeKeyTile;
+        return 0;
+    }
+    int n;
+    return decode_plan(pos + 1, a.kps, a.cap, kDecodeKeyTile, &n, split_len);
+}
+
 template <int HD, int G, int FMT>
-__global__ __launch_bounds__(256) void decode_partial_kernel(DecodeArgs a) {
-    using Sh = DecodeShape<HD, G, FMT>;
-    constexpr int W = Sh::W, BKD = Sh::BKD, NHG = Sh::NHG, HP = Sh::HP, VPL = Sh::VPL;
-    constexpr int NB = Sh::NB, RB = Sh::RB;
-    __shared__ float Qs[HP * HD];
-    __shared__ float Ps[W][HP * BKD];
-    __shared__ float Om[W][HP * HD];
-    __shared__ float Mm[W][HP], Lm[W][HP];
+__global__ __attribute__((amdgpu_flat_work_group_size(64, 64), amdgpu_waves_per_eu(2)))
+void decode_partial_kernel(DecodeArgs a) {
+    using Sh = DShape<HD, G, FMT>;
+    constexpr int BKD = Sh::BKD, NHG = Sh::NHG, HP = Sh::HP, QS = Sh::QS, PS = Sh::PS;
+    constexpr int NB = Sh::NB, RB = Sh::RB, CB = Sh::CB, BPL = Sh::BPL, OD = Sh::OD;
+    constexpr float TAU = 8.0f;
+    typedef typename Chunk<CB>::T chunk_t;
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int w = tid >> 6;
-    const int split0 = blockIdx.x;
-    const int S = gridDim.x;
-    const int kvh = blockIdx.y;
-    const int slot = blockIdx.z;
+    __shared__ float Qs[HP * QS];
+    __shared__ float Pw[HP * PS];
+    __shared__ __attribute__((aligned(16))) uint8_t Rw[Sh::TILE_BYTES];
 
-    const int pos = a.pos[slot];
-    const bool bad = pos < 0 || pos >= a.max_seq;
-    const int L = pos + 1;
+    const int lane = threadIdx.x;
+    const int w = blockIdx.x;
+    const int NW = gridDim.x;
+    const int nsegs = a.n_slots * a.n_kv;
 
-    for (int idx = tid; idx < HP * HD; idx += 256) {
-        const int hr = idx / HD, e = idx % HD;
-        Qs[idx] = hr < G ? a.q[((size_t)slot * a.n_head + kvh * G + hr) * HD + e] * a.qscale
-                         : 0.0f;
+    // ---- pass 1: total number of items
+    int total = 0;
+    for (int base = 0; base < nsegs; base += 64) {
+        const int s = base + lane;
+        int sl;
+        const int it = s < nsegs ? slot_items(a.pos[s / a.n_kv], a, &sl) : 0;
+        total += wave_sum_i(it);
     }
-    __syncthreads();
-
-    float m[HP], l[HP];
-    f32x4 O[VPL][NHG];
-#pragma unroll
-    for (int h = 0; h < HP; h++) {
-        m[h] = -INFINITY;
-        l[h] = 0.0f;
-    }
-#pragma unroll
-    for (int c = 0; c < VPL; c++)
-#pragma unroll
-        for (int hg = 0; hg < NHG; hg++) O[c][hg] = f32x4{};
+    const long long lo = (long long)w * total / NW;
+    const long long hi = (long long)(w + 1) * total / NW;
+    // wave owning item f: the last wave whose run starts at or before f
+    auto owner = [&](long long f) -> int { return (int)(((f + 1) * NW - 1) / total); };
 
     unsigned vis = 0, skp = 0;
-    const size_t head_rows = ((size_t)slot * a.n_kv + kvh) * a.max_seq;
-    const uint8_t *kb = (const uint8_t *)a.k + head_rows * RB;
-    const uint8_t *vb = (const uint8_t *)a.v + head_rows * RB;
-    float *Pw = Ps[w];
 
-    auto tile = [&](int j0, int k_hi) {
-        const int key = j0 + lane;
-        const bool kval = key < k_hi && in_key_set(key, pos, a.sink, a.win);
-        const int krow = min(key, k_hi - 1);        // never read past the live rows
-        f32x4 sacc[NHG];
-#pragma unroll
-        for (int hg = 0; hg < NHG; hg++) sacc[hg] = f32x4{};
-        const float *qlane = Qs + (lane & 3) * HD;
+    // ---- per-segment fold of items [it_lo, it_hi) into one partial
+    auto run_segment = [&](int seg, int it_lo, int it_hi, int pidx) {
+        const int slot = seg / a.n_kv, kvh = seg % a.n_kv;
+        const int pos = a.pos[slot];
+        int split_len;
+        slot_items(pos, a, &split_len);
+        const int L = pos + 1;
+        const int k_lo = it_lo * split_len;
+        const int k_hi = min(L, it_hi * split_len);
 
-        if constexpr (FMT == 0) {
-            const f32x4 *kr = (const f32x4 *)(kb + (size_t)krow * RB);
-#pragma unroll 8
-            for (int c4 = 0; c4 < HD / 4; c4++) {
-                const f32x4 kv = kr[c4];
-#pragma unroll
-                for (int hg = 0; hg < NHG; hg++) {
-                    const f32x4 qv = *(const f32x4 *)(qlane + hg * 4 * HD + 4 * c4);
-#pragma unroll
-                    for (int t = 0; t < 4; t++) sacc[hg] = mfma4(qv[t], kv[t], sacc[hg]);
-                }
-            }
-        } else {
-            // this lane's whole Q4 row as dwords (row starts are 4-byte aligned)
-            uint32_t rw[RB / 4];
-            const uint8_t *kr = kb + (size_t)krow * RB;
-            if constexpr (RB % 16 == 0) {
-#pragma unroll
-                for (int i = 0; i < RB / 16; i++) {
-                    const u32x4 v = ((const u32x4 *)kr)[i];
-                    rw[4 * i] = v[0]; rw[4 * i + 1] = v[1]; rw[4 * i + 2] = v[2]; rw[4 * i + 3] = v[3];
-                }
-            } else if constexpr (RB % 8 == 0) {
-#pragma unroll
-                for (int i = 0; i < RB / 8; i++) {
-                    const u32x2 v = ((const u32x2 *)kr)[i];
-                    rw[2 * i] = v[0]; rw[2 * i + 1] = v[1];
-                }
-            } else {
-#pragma unroll
-                for (int i = 0; i < RB / 4; i++) rw[i] = ((const uint32_t *)kr)[i];
-            }
-#pragma unroll
-            for (int blk = 0; blk < NB; blk++) {
-                const int o = blk * kQ4BlockBytes;     // compile-time after unrolling
-                const int dw = o / 4;
-                const bool odd = (blk & 1) != 0;       // odd blocks start 2 bytes into a dword
-                const uint32_t sbits = odd ? (rw[dw] >> 16) : (rw[dw] & 0xffffu);
-                const float d = half_bits_to_float(sbits);
-                const float m8d = -8.0f * d;
-#pragma unroll
-                for (int q = 0; q < 4; q++) {
-                    const uint32_t cw = odd ? rw[dw + 1 + q]
-                                            : ((rw[dw + q] >> 16) | (rw[dw + q + 1] << 16));
-                    const float lo[4] = {fmaf(nib(cw, 0), d, m8d), fmaf(nib(cw, 8), d, m8d),
-                                         fmaf(nib(cw, 16), d, m8d), fmaf(nib(cw, 24), d, m8d)};
-                    const float hi[4] = {fmaf(nib(cw, 4), d, m8d), fmaf(nib(cw, 12), d, m8d),
-                                         fmaf(nib(cw, 20), d, m8d), fmaf(nib(cw, 28), d, m8d)};
-#pragma unroll
-                    for (int hg = 0; hg < NHG; hg++) {
-                        const float *qb = qlane + hg * 4 * HD + blk * kQ4Block;
-                        const f32x4 qa = *(const f32x4 *)(qb + 4 * q);
-                        const f32x4 qh = *(const f32x4 *)(qb + 16 + 4 * q);
-#pragma unroll
-                        for (int t = 0; t < 4; t++) {
-                            sacc[hg] = mfma4(qa[t], lo[t], sacc[hg]);
-                            sacc[hg] = mfma4(qh[t], hi[t], sacc[hg]);
-                        }
-                    }
-                }
-            }
-        }
-
-        // online softmax per head; lane = key, register = head within group
-        float corr[HP];
-        bool moved = false;
-#pragma unroll
-        for (int hg = 0; hg < NHG; hg++) {
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const int h = 4 * hg + i;
-                const float s = kval ? sacc[hg][i] : -INFINITY;
-                const float tmax = wave_max(s);
-                const float m_new = fmaxf(m[h], tmax);
-                const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-                corr[h] = fast_exp2(m[h] - m_use);
-                moved |= m_new > m[h];
-                m[h] = m_new;
-                const float p = fast_exp2(s - m_use);
-                l[h] = l[h] * corr[h] + p;
-                Pw[h * BKD + lane] = p;
-            }
-        }
-        if (moved) {
-#pragma unroll
-            for (int c = 0; c < VPL; c++)
-#pragma unroll
-                for (int hg = 0; hg < NHG; hg++)
-#pragma unroll
-                    for (int i = 0; i < 4; i++) O[c][hg][i] *= corr[4 * hg + i];
+        wave_lds_sync();          // previous segment done with Qs
+        for (int idx = lane; idx < HP * HD; idx += 64) {
+            const int hr = idx / HD, e = idx % HD;
+            Qs[hr * QS + e] =
+                hr < G ? a.q[((size_t)slot * a.n_head + kvh * G + hr) * HD + e] * a.qscale : 0.0f;
         }
         wave_lds_sync();
 
-        // PV: one key per contraction step, lanes over output dims
-        const float *plane = Pw + (lane & 3) * BKD;
-#pragma unroll 2
-        for (int k4 = 0; k4 < BKD / 4; k4++) {
-            f32x4 pa[NHG];
-#pragma unroll
-            for (int hg = 0; hg < NHG; hg++) pa[hg] = *(const f32x4 *)(plane + hg * 4 * BKD + 4 * k4);
-#pragma unroll
-            for (int t = 0; t < 4; t++) {
-                const int vrow = min(j0 + 4 * k4 + t, k_hi - 1);
-                float vv[VPL];
-                if constexpr (FMT == 0) {
-                    const float *vr = (const float *)(vb + (size_t)vrow * RB);
-#pragma unroll
-                    for (int c = 0; c < VPL; c++) vv[c] = vr[lane + 64 * c];
-                } else {
-                    const uint8_t *vr = vb + (size_t)vrow * RB;
-                    if constexpr (HD == 256) {
-                        const int bb = lane >> 3, jj = 2 * (lane & 7);
-                        const float d = half_bits_to_float(*(const uint16_t *)(vr + bb * kQ4BlockBytes));
-                        const uint32_t cw = *(const uint16_t *)(vr + bb * kQ4BlockBytes + 2 + jj);
-                        const float m8d = -8.0f * d;
-                        vv[0] = fmaf(nib(cw, 0), d, m8d);    // element jj
-                        vv[1] = fmaf(nib(cw, 8), d, m8d);    // element jj+1
-                        vv[2] = fmaf(nib(cw, 4), d, m8d);    // element jj+16
-                        vv[3] = fmaf(nib(cw, 12), d, m8d);   // element jj+17
-                    } else if constexpr (HD == 128) {
-                        const int bb = lane >> 4, jj = lane & 15;
-                        const float d = half_bits_to_float(*(const uint16_t *)(vr + bb * kQ4BlockBytes));
-                        const uint32_t cb = vr[bb * kQ4BlockBytes + 2 + jj];
-                        const float m8d = -8.0f * d;
-                        vv[0] = fmaf(nib(cb, 0), d, m8d);
-                        vv[1] = fmaf(nib(cb, 4), d, m8d);
-                    } else {
-                        const int bb = lane >> 5, e = lane & 31;
-                        const float d = half_bits_to_float(*(const uint16_t *)(vr + bb * kQ4BlockBytes));
-                        const uint32_t cb = vr[bb * kQ4BlockBytes + 2 + (e & 15)];
-                        vv[0] = fmaf(nib(cb, e < 16 ? 0 : 4), d, -8.0f * d);
-                    }
-                }
-#pragma unroll
-                for (int c = 0; c < VPL; c++)
-#pragma unroll
-                    for (int hg = 0; hg < NHG; hg++) O[c][hg] = mfma4(pa[hg][t], vv[c], O[c][hg]);
-            }
-        }
-        wave_lds_sync();          // P of this tile consumed before the next overwrites it
-    };
-
-    if (!bad) {
-        int n_splits, split_len;
-        const int live = decode_plan(L, a.kps, a.cap, BKD, &n_splits, &split_len);
-        for (int sp = split0; sp < live; sp += S) {
-            const int k_lo = sp * split_len;
-            const int k_hi = min(L, k_lo + split_len);
-            for (int j0 = k_lo + BKD * w; j0 < k_hi; j0 += BKD * W) {
-                const int e = min(j0 + BKD - 1, k_hi - 1);
-                if (a.win > 0 && j0 >= a.sink && e < pos - a.win + 1) {
-                    skp++;
-                    continue;
-                }
-                vis++;
-                tile(j0, k_hi);
-            }
-        }
-    }
-
-    // ---- merge the 4 waves' states, then write this split's partial
-#pragma unroll
-    for (int h = 0; h < HP; h++) l[h] = wave_sum(l[h]);
-    if (lane == 0) {
+        float m[HP], l[HP];
+        f32x4 O[OD][NHG];
 #pragma unroll
         for (int h = 0; h < HP; h++) {
-            Mm[w][h] = m[h];
-            Lm[w][h] = l[h];
+            m[h] = -INFINITY;
+            l[h] = 0.0f;
         }
-    }
 #pragma unroll
-    for (int c = 0; c < VPL; c++)
+        for (int c = 0; c < OD; c++)
 #pragma unroll
-        for (int hg = 0; hg < NHG; hg++)
-#pragma unroll
-            for (int i = 0; i < 4; i++) Om[w][(4 * hg + i) * HD + pv_dim<HD, FMT>(lane, c)] = O[c][hg][i];
-    __syncthreads();
+            for (int hg = 0; hg < NHG; hg++) O[c][hg] = f32x4{};
 
-    for (int idx = tid; idx < G * HD; idx += 256) {
-        const int h = idx / HD, dd = idx % HD;
-        float M = -INFINITY;
-#pragma unroll
-        for (int ww = 0; ww < W; ww++) M = fmaxf(M, Mm[ww][h]);
-        float o = 0.0f, lsum = 0.0f;
-        if (M != -INFINITY) {
-#pragma unroll
-            for (int ww = 0; ww < W; ww++) {
-                const float sc = fast_exp2(Mm[ww][h] - M);
-                o += Om[ww][h * HD + dd] * sc;
-                lsum += Lm[ww][h] * sc;
+        const size_t head_rows = ((size_t)slot * a.n_kv + kvh) * a.max_seq;
+        const uint8_t *kb = (const uint8_t *)a.k + head_rows * RB;
+        const uint8_t *vb = (const uint8_t *)a.v + head_rows * RB;
+        const int win_first = pos - a.win + 1;     // first key of the recent window
+
+        // first visited tile at or after j ([FA] fc_attn_tile_in_window)
+        auto next_visited = [&](int j) -> int {
+            if (j < k_hi && a.win > 0 && j >= a.sink && min(j + BKD - 1, k_hi - 1) < win_first) {
+                const int jn = (win_first / BKD) * BKD;    // tile holding the window's first key
+                const int stop = min(jn, k_hi);
+                skp += (unsigned)((stop - j + BKD - 1) / BKD);
+                return jn >= k_hi ? k_hi : jn;
             }
+            return j;
+        };
+
+        // softmax of one tile's scores; lane = key, register = head in group
+        auto softmax_tile = [&](f32x4 (&sacc)[NHG], bool kval, int pslot) {
+#pragma unroll
+            for (int hg = 0; hg < NHG; hg++) {
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const int h = 4 * hg + i;
+                    const float s = kval ? sacc[hg][i] : -INFINITY;
+                    if (__ballot(s > m[h] + TAU)) {
+                        const float m_new = fmaxf(m[h], wave_max(s));
+                        const float corr = fast_exp2(m[h] - m_new);
+                        m[h] = m_new;
+                        l[h] *= corr;
+#pragma unroll
+                        for (int c = 0; c < OD; c++) O[c][hg][i] *= corr;
+                    }
+                    const float p = fast_exp2(s - m[h]);
+                    l[h] += p;
+                    Pw[h * PS + pslot] = p;
+                }
+            }
+        };
+
+        const float *qlane = Qs + (lane & 3) * QS;
+
+        if constexpr (FMT == 0) {
+            // ---------------- fp32 tiles: direct row reads
+            for (int j = next_visited(k_lo); j < k_hi; j = next_visited(j + BKD)) {
+                vis++;
+                const int key = j + lane;
+                const bool kval = key < k_hi && in_key_set(key, pos, a.sink, a.win);
+                const f32x4 *kr = (const f32x4 *)(kb + (size_t)min(key, k_hi - 1) * RB);
+                f32x4 sacc2[NHG][2];
+#pragma unroll
+                for (int hg = 0; hg < NHG; hg++) sacc2[hg][0] = sacc2[hg][1] = f32x4{};
+#pragma unroll 8
+                for (int c4 = 0; c4 < HD / 4; c4++) {
+                    const f32x4 kv = kr[c4];
+#pragma unroll
+                    for (int hg = 0; hg < NHG; hg++) {
+                        const f32x4 qv = *(const f32x4 *)(qlane + hg * 4 * QS + 4 * c4);
+#pragma unroll
+                        for (int t = 0; t < 4; t++)
+                            sacc2[hg][t & 1] = mfma4(qv[t], kv[t], sacc2[hg][t & 1]);
+                    }
+                }
+                f32x4 sacc[NHG];
+#pragma unroll
+                for (int hg = 0; hg < NHG; hg++) sacc[hg] = sacc2[hg][0] + sacc2[hg][1];
+                softmax_tile(sacc, kval, lane);
+                wave_lds_sync();
+                const float *plane = Pw + (lane & 3) * PS;
+#pragma unroll 2
+                for (int k4 = 0; k4 < BKD / 4; k4++) {
+                    f32x4 pa[NHG];
+#pragma unroll
+                    for (int hg = 0; hg < NHG; hg++)
+                        pa[hg] = *(const f32x4 *)(plane + hg * 4 * PS + 4 * k4);
+#pragma unroll
+                    for (int t = 0; t < 4; t++) {
+                        const float *vr =
+                            (const float *)(vb + (size_t)min(j + 4 * k4 + t, k_hi - 1) * RB);
+                        float vv[OD];
+#pragma unroll
+                        for (int c = 0; c < OD; c++) vv[c] = vr[lane + 64 * c];
+#pragma unroll
+                        for (int c = 0; c < OD; c++)
+#pragma unroll
+                            for (int hg = 0; hg < NHG; hg++)
+                                O[c][hg] = mfma4(pa[hg][t], vv[c], O[c][hg]);
+                    }
+                }
+                wave_lds_sync();
+            }
+        } else {
+            // ---------------- Q4_0 tiles: prefetch, LDS staging, fused dequant
+            chunk_t pk[9], pv[9];
+            auto fetch = [&](chunk_t (&dst)[9], const uint8_t *base, int j) {
+                const int nrows = min(BKD, k_hi - j);
+                const uint8_t *t = base + (size_t)j * RB;
+#pragma unroll
+                for (int i = 0; i < 9; i++) {
+                    const int c = lane + 64 * i;
+                    dst[i] = c / 9 < nrows ? *(const chunk_t *)(t + c * CB) : chunk_t{};
+                }
+            };
+            int j = next_visited(k_lo);
+            if (j < k_hi) {
+                fetch(pk, kb, j);
+                fetch(pv, vb, j);
+            }
+            while (j < k_hi) {
+                const int tj = j;
+                vis++;
+#pragma unroll
+                for (int i = 0; i < 9; i++) *(chunk_t *)(Rw + (lane + 64 * i) * CB) = pk[i];
+                wave_lds_sync();
+                uint32_t rw[RB / 4];
+#pragma unroll
+                for (int i = 0; i < 9; i++) {
+                    const chunk_t v = *(const chunk_t *)(Rw + lane * RB + i * CB);
+                    if constexpr (CB == 16) {
+                        rw[4 * i] = v[0]; rw[4 * i + 1] = v[1]; rw[4 * i + 2] = v[2]; rw[4 * i + 3] = v[3];
+                    } else if constexpr (CB == 8) {
+                        rw[2 * i] = v[0]; rw[2 * i + 1] = v[1];
+                    } else {
+                        rw[i] = v;
+                    }
+                }
+                wave_lds_sync();
+#pragma unroll
+                for (int i = 0; i < 9; i++) *(chunk_t *)(Rw + (lane + 64 * i) * CB) = pv[i];
+                j = next_visited(tj + BKD);
+                if (j < k_hi) fetch(pk, kb, j);       // next K flies during this QK
+
+                // QK: 2 accumulator chains per head group
+                const int key = tj + lane;
+                const bool kval = key < k_hi && in_key_set(key, pos, a.sink, a.win);
+                f32x4 sacc2[NHG][2];
+#pragma unroll
+                for (int hg = 0; hg < NHG; hg++) sacc2[hg][0] = sacc2[hg][1] = f32x4{};
+#pragma unroll
+                for (int blk = 0; blk < NB; blk++) {
+                    const int dw = blk * kQ4BlockBytes / 4;
+                    const bool odd = (blk & 1) != 0;   // odd blocks start 2 bytes into a dword
+                    const uint32_t sbits = odd ? (rw[dw] >> 16) : (rw[dw] & 0xffffu);
+                    const float d = half_bits_to_float(sbits);
+                    const float bias = -1032.0f * d;  // (1024 + c) * d + bias == (c - 8) * d
+#pragma unroll
+                    for (int q = 0; q < 4; q++) {
+                        const uint32_t cw = odd ? rw[dw + 1 + q]
+                                                : __builtin_amdgcn_alignbyte(rw[dw + q + 1], rw[dw + q], 2);
+                        const uint32_t r0 = nib_pair(cw, 0), r1 = nib_pair(cw, 8);
+                        const uint32_t r2 = nib_pair(cw, 4), r3 = nib_pair(cw, 12);
+                        // elements blk*32 + 4q + t (low nibbles) and blk*32 + 16 + 4q + t (high)
+                        const float klo[4] = {fmaf(lo_h(r0), d, bias), fmaf(lo_h(r1), d, bias),
+                                              fmaf(hi_h(r0), d, bias), fmaf(hi_h(r1), d, bias)};
+                        const float khi[4] = {fmaf(lo_h(r2), d, bias), fmaf(lo_h(r3), d, bias),
+                                              fmaf(hi_h(r2), d, bias), fmaf(hi_h(r3), d, bias)};
+#pragma unroll
+                        for (int hg = 0; hg < NHG; hg++) {
+                            const float *qb = qlane + hg * 4 * QS + blk * kQ4Block;
+                            const f32x4 qa = *(const f32x4 *)(qb + 4 * q);
+                            const f32x4 qh = *(const f32x4 *)(qb + 16 + 4 * q);
+#pragma unroll
+                            for (int t = 0; t < 4; t++) {
+                                sacc2[hg][t & 1] = mfma4(qa[t], klo[t], sacc2[hg][t & 1]);
+                                sacc2[hg][t & 1] = mfma4(qh[t], khi[t], sacc2[hg][t & 1]);
+                            }
+                        }
+                    }
+                }
+                f32x4 sacc[NHG];
+#pragma unroll
+                for (int hg = 0; hg < NHG; hg++) sacc[hg] = sacc2[hg][0] + sacc2[hg][1];
+                softmax_tile(sacc, kval, (lane & 1) * 32 + (lane >> 1));   // even keys, then odd
+                if (j < k_hi) fetch(pv, vb, j);       // next V flies during this PV
+                wave_lds_sync();
+
+                // PV: lanes 0-31 even keys, lanes 32-63 odd keys
+                const int hk = lane >> 5;
+                const int ll = lane & 31;
+                const int bb = ll / Sh::LPB, jb = (ll % Sh::LPB) * BPL;
+                const float *plane = Pw + (lane & 3) * PS + hk * 32;
+#pragma unroll 1
+                for (int t4 = 0; t4 < 8; t4++) {
+                    f32x4 pa[NHG];
+#pragma unroll
+                    for (int hg = 0; hg < NHG; hg++)
+                        pa[hg] = *(const f32x4 *)(plane + hg * 4 * PS + 4 * t4);
+#pragma unroll
+                    for (int u = 0; u < 4; u++) {
+                        const int kl = 2 * (4 * t4 + u) + hk;
+                        const uint8_t *vr = Rw + kl * RB + bb * kQ4BlockBytes;
+                        const float d = half_bits_to_float(*(const uint16_t *)vr);
+                        float vv[OD];
+                        if constexpr (BPL == 4) {
+                            const uint32_t cw = *(const uint16_t *)(vr + 2 + jb) |
+                                                ((uint32_t)*(const uint16_t *)(vr + 4 + jb) << 16);
+                            const float bias = -1032.0f * d;
+                            const uint32_t r0 = nib_pair(cw, 0), r1 = nib_pair(cw, 8);
+                            const uint32_t r2 = nib_pair(cw, 4), r3 = nib_pair(cw, 12);
+                            vv[0] = fmaf(lo_h(r0), d, bias);   // element jb
+                            vv[1] = fmaf(lo_h(r1), d, bias);   // jb + 1
+                            vv[2] = fmaf(hi_h(r0), d, bias);   // jb + 2
+                            vv[3] = fmaf(hi_h(r1), d, bias);   // jb + 3
+                            vv[4] = fmaf(lo_h(r2), d, bias);   // 16 + jb
+                            vv[5] = fmaf(lo_h(r3), d, bias);   // 16 + jb + 1
+                            vv[6] = fmaf(hi_h(r2), d, bias);   // 16 + jb + 2
+                            vv[7] = fmaf(hi_h(r3), d, bias);   // 16 + jb + 3
+                        } else {
+                            const uint32_t cw = BPL == 2 ? (uint32_t)*(const uint16_t *)(vr + 2 + jb)
+                                                         : (uint32_t)vr[2 + jb];
+                            const float m8d = -8.0f * d;
+#pragma unroll
+                            for (int b = 0; b < BPL; b++) {
+                                vv[b] = fmaf(byte_f(cw & 0x0f0f0f0fu, b), d, m8d);
+                                vv[BPL + b] = fmaf(byte_f((cw >> 4) & 0x0f0f0f0fu, b), d, m8d);
+                            }
+                        }
+#pragma unroll
+                        for (int c = 0; c < OD; c++)
+#pragma unroll
+                            for (int hg = 0; hg < NHG; hg++)
+                                O[c][hg] = mfma4(pa[hg][u], vv[c], O[c][hg]);
+                    }
+                }
+                wave_lds_sync();
+            }
+#pragma unroll
+            for (int c = 0; c < OD; c++)
+#pragma unroll
+                for (int hg = 0; hg < NHG; hg++)
+#pragma unroll
+                    for (int i = 0; i < 4; i++) O[c][hg][i] += __shfl_xor(O[c][hg][i], 32);
         }
-        const size_t pidx = ((size_t)slot * a.n_head + kvh * G + h) * S + split0;
-        a.ws_acc[pidx * HD + dd] = o;
-        if (dd == 0) {
-            a.ws_m[pidx] = M;
-            a.ws_l[pidx] = lsum;
+
+        // ---- this segment's partial: m, l and acc for the G heads
+#pragma unroll
+        for (int h = 0; h < HP; h++) l[h] = wave_sum(l[h]);
+        const size_t pbase = (size_t)pidx * G;
+        if (lane < G) {
+            float mv = 0.0f, lv = 0.0f;
+#pragma unroll
+            for (int h = 0; h < HP; h++)
+                if (h == lane) {
+                    mv = m[h];
+                    lv = l[h];
+                }
+            a.ws_m[pbase + lane] = mv;
+            a.ws_l[pbase + lane] = lv;
         }
+        if (FMT == 0 || lane < 32) {
+#pragma unroll
+            for (int c = 0; c < OD; c++)
+#pragma unroll
+                for (int hg = 0; hg < NHG; hg++)
+#pragma unroll
+                    for (int i = 0; i < 4; i++)
+                        if (4 * hg + i < G)
+                            a.ws_acc[(pbase + 4 * hg + i) * HD + o_dim<HD, FMT>(lane, c)] = O[c][hg][i];
+        }
+    };
+
+    // ---- pass 2: segment prefix sums, the partial table, and this wave's run
+    int f_carry = 0, p_carry = 0;
+    for (int base = 0; base < nsegs; base += 64) {
+        const int s = base + lane;
+        int sl;
+        const int it = s < nsegs ? slot_items(a.pos[s / a.n_kv], a, &sl) : 0;
+        const int incl = wave_incl_scan(it, lane);
+        const int F = f_carry + incl - it;
+        const int nw = it > 0 ? owner(F + it - 1) - owner(F) + 1 : 0;
+        const int inclw = wave_incl_scan(nw, lane);
+        const int P = p_carry + inclw - nw;
+        if (w == 0 && s < nsegs) {
+            a.seg_table[2 * s] = P;
+            a.seg_table[2 * s + 1] = nw;
+        }
+        unsigned long long hit = __ballot(it > 0 && F < hi && F + it > lo);
+        while (hit) {
+            const int b = __builtin_ctzll(hit);
+            hit &= hit - 1;
+            const int Fs = __shfl(F, b), its = __shfl(it, b), Ps = __shfl(P, b);
+            const int it_lo = (int)max(lo, (long long)Fs) - Fs;
+            const int it_hi = (int)min(hi, (long long)Fs + its) - Fs;
+            run_segment(base + b, it_lo, it_hi, Ps + (w - owner(Fs)));
+        }
+        f_carry += __shfl(incl, 63);
+        p_carry += __shfl(inclw, 63);
     }
+
     if (a.stats && lane == 0) {
         atomicAdd(&a.stats[0], (unsigned long long)vis);
         atomicAdd(&a.stats[1], (unsigned long long)skp);
     }
 }
 
-// out = sum_s exp2(m_s - M) acc_s / sum_s exp2(m_s - M) l_s, ascending s.
-template <int HD>
-__global__ __launch_bounds__(HD) void decode_combine_kernel(DecodeArgs a, int S) {
-    const size_t gh = blockIdx.x;           // slot * n_head + head
+// out = sum_r exp2(m_r - M) acc_r / sum_r exp2(m_r - M) l_r over the
+// segment's partials in ascending order.
+template <int HD, int G>
+__global__ __launch_bounds__(HD) void decode_combine_kernel(DecodeArgs a) {
+    const int gh = blockIdx.x;              // slot * n_head + head
+    const int slot = gh / a.n_head, h = gh % a.n_head;
+    const int seg = slot * a.n_kv + h / G, g = h % G;
+    const int P = a.seg_table[2 * seg], n = a.seg_table[2 * seg + 1];
     const int dd = threadIdx.x;
-    const float *mm = a.ws_m + gh * S;
-    const float *ll = a.ws_l + gh * S;
-    const float *acc = a.ws_acc + gh * S * HD;
     float M = -INFINITY;
-    for (int s = 0; s < S; s++) M = fmaxf(M, mm[s]);
+    for (int r = 0; r < n; r++) M = fmaxf(M, a.ws_m[(size_t)(P + r) * G + g]);
     float o = 0.0f, L = 0.0f;
-    for (int s = 0; s < S; s++) {
-        const float wgt = fast_exp2(mm[s] - M);
-        L += ll[s] * wgt;
-        o += acc[(size_t)s * HD + dd] * wgt;
+    for (int r = 0; r < n; r++) {
+        const size_t pi = (size_t)(P + r) * G + g;
+        const float wgt = fast_exp2(a.ws_m[pi] - M);
+        L += a.ws_l[pi] * wgt;
+        o += a.ws_acc[pi * HD + dd] * wgt;
     }
-    a.out[gh * HD + dd] = o / L;
+    a.out[(size_t)gh * HD + dd] = o / L;   // no partial (bad position): 0/0 = NaN
 }
 
 template <int HD, int G, int FMT>
-hipError_t launch_one(const DecodeArgs &a, int n_slots, int splits, hipStream_t s) {
-    hipLaunchKernelGGL((decode_partial_kernel<HD, G, FMT>), dim3(splits, a.n_kv, n_slots),
-                       dim3(256), 0, s, a);
+hipError_t launch_one(const DecodeArgs &a, int waves, hipStream_t s) {
+    hipLaunchKernelGGL((decode_partial_kernel<HD, G, FMT>), dim3(waves), dim3(64), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(decode_combine_kernel<HD>, dim3(n_slots * a.n_head), dim3(HD), 0, s, a,
-                       splits);
+    hipLaunchKernelGGL((decode_combine_kernel<HD, G>), dim3(a.n_slots * a.n_head), dim3(HD), 0, s,
+                       a);
     return hipGetLastError();
 }
 
 template <int HD, int FMT>
-hipError_t by_group(int group, const DecodeArgs &a, int n_slots, int splits, hipStream_t s) {
+hipError_t by_group(int group, const DecodeArgs &a, int waves, hipStream_t s) {
     switch (group) {
-    case 1: return launch_one<HD, 1, FMT>(a, n_slots, splits, s);
-    case 2: return launch_one<HD, 2, FMT>(a, n_slots, splits, s);
-    case 4: return launch_one<HD, 4, FMT>(a, n_slots, splits, s);
-    case 8: return launch_one<HD, 8, FMT>(a, n_slots, splits, s);
+    case 1: return launch_one<HD, 1, FMT>(a, waves, s);
+    case 2: return launch_one<HD, 2, FMT>(a, waves, s);
+    case 4: return launch_one<HD, 4, FMT>(a, waves, s);
+    case 8: return launch_one<HD, 8, FMT>(a, waves, s);
     }
     return hipErrorInvalidValue;
 }
 
 template <int FMT>
-hipError_t by_dim(int head_dim, int group, const DecodeArgs &a, int n_slots, int splits,
-                  hipStream_t s) {
+hipError_t by_dim(int head_dim, int group, const DecodeArgs &a, int waves, hipStream_t s) {
     switch (head_dim) {
-    case 64: return by_group<64, FMT>(group, a, n_slots, splits, s);
-    case 128: return by_group<128, FMT>(group, a, n_slots, splits, s);
-    case 256: return by_group<256, FMT>(group, a, n_slots, splits, s);
+    case 64: return by_group<64, FMT>(group, a, waves, s);
+    case 128: return by_group<128, FMT>(group, a, waves, s);
+    case 256: return by_group<256, FMT>(group, a, waves, s);
     }
     return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_decode(int format, int head_dim, int group, const DecodeArgs &a, int n_slots,
-                         int launch_splits, hipStream_t s) {
-    return format == 0 ? by_dim<0>(head_dim, group, a, n_slots, launch_splits, s)
-                       : by_dim<1>(head_dim, group, a, n_slots, launch_splits, s);
+hipError_t launch_decode(int format, int head_dim, int group, const DecodeArgs &a, int waves,
+                         hipStream_t s) {
+    return format == 0 ? by_dim<0>(head_dim, group, a, waves, s)
+                       : by_dim<1>(head_dim, group, a, waves, s);
 }
 
 }  // namespace fa

@@ -30,10 +30,11 @@ struct DecodeArgs {
     const float *q;               // [n_slots][n_head][hd]
     const int *pos;               // device [n_slots]
     const void *k, *v;            // cache base: [n_slots_cache][n_kv][max_seq][row]
-    float *ws_m, *ws_l, *ws_acc;  // partials [n_slots*n_head][splits](+[hd])
+    float *ws_m, *ws_l, *ws_acc;  // partials [n_partials][G] (+[hd])
+    int *seg_table;               // [n_slots * n_kv][2]: first partial, partial count
     float *out;                   // [n_slots][n_head][hd]
     unsigned long long *stats;
-    int n_head, n_kv, max_seq;
+    int n_slots, n_head, n_kv, max_seq;
     int sink, win;
     float qscale;
     int kps, cap;                 // split plan constants
@@ -43,13 +44,14 @@ struct DecodeArgs {
 constexpr int kPrefillWaves = 4;
 constexpr int kPrefillRowsPerWave = 32;
 constexpr int kPrefillKeyTile = 32;
-// Decode: 4 waves, each folding tiles of 64 keys (one key per lane).
-constexpr int kDecodeWaves = 4;
+// Decode: single-wave work-groups folding tiles of 64 keys (one per lane).
 constexpr int kDecodeKeyTile = 64;
 // Split plan constants: about kDecodeKps keys per split, at most
-// kDecodeSplitCap splits per slot.
-constexpr int kDecodeKps = 2048;
-constexpr int kDecodeSplitCap = 16;
+// kDecodeSplitCap splits per slot. Splits are the schedulable work items.
+constexpr int kDecodeKps = 128;
+constexpr int kDecodeSplitCap = 512;
+// Work-groups of the decode partial pass: 8 waves per CU of a 256-CU MI355X.
+constexpr int kDecodeMaxWaves = 2048;
 
 inline int prefill_q_positions(int group) {
     return kPrefillWaves * kPrefillRowsPerWave / group;
@@ -58,8 +60,8 @@ inline int prefill_q_positions(int group) {
 hipError_t launch_append(int format, const AppendArgs &a, hipStream_t s);
 hipError_t launch_prefill(int format, int head_dim, int group, const PrefillArgs &a,
                           hipStream_t s);
-hipError_t launch_decode(int format, int head_dim, int group, const DecodeArgs &a,
-                         int n_slots, int launch_splits, hipStream_t s);
+hipError_t launch_decode(int format, int head_dim, int group, const DecodeArgs &a, int waves,
+                         hipStream_t s);
 
 // Host copy of the device plan ([FA] fc_attn_dec_plan).
 __host__ __device__ inline int decode_plan(int seq_len, int kps, int cap, int tile, int *n_splits,

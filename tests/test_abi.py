@@ -102,7 +102,11 @@ def test_prefill_validation():
 def test_decode_validation():
     c = cache(n_slots=4, max_seq=100)
     need = fa.fa_decode_workspace_bytes(c, 4, 4, 100)
-    assert need == 4 * 4 * fa.fa_decode_plan(100)[0] * (128 + 2) * 4
+    # at least one partial {m, l, acc[hd]} per (slot, head) plus the segment table
+    assert need >= 4 * 4 * (128 + 2) * 4 + 4 * 2 * 2 * 4
+    assert fa.fa_decode_workspace_bytes(c, 2, 4, 100) <= need
+    assert fa.fa_decode_workspace_bytes(c, 4, 4, 50) <= need
+    assert fa.fa_decode_workspace_bytes(c, 4, 3, 100) == 0      # heads not a multiple of n_kv
     assert rc_decode(None) == fa.FA_ENULL
     assert rc_decode(c, n_slots=5) == fa.FA_EINVAL
     assert rc_decode(c, hint=0) == fa.FA_EINVAL
