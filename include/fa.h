@@ -132,32 +132,39 @@ int fa_prefill_tile_shape(int n_head, int n_kv_head, int head_dim,
 int fa_decode_plan(int seq_len, int *n_splits, int *split_len);
 void fa_decode_plan_params(int *kps, int *cap, int *key_tile);
 
-/* Workspace for fa_decode: per (slot, head, launched split) one partial
- * {m, l, acc[head_dim]} fp32 ([FA] "Decode-mode flash attention": partial
- * running max, running sum and unnormalised accumulator). The launch width
- * is the live split count of max_ctx. 0 if an argument is invalid. */
+/* Workspace for fa_decode: partials {m, l, acc[head_dim]} fp32 ([FA]
+ * "Decode-mode flash attention": running max, running sum and unnormalised
+ * accumulator of the keys a partial folded) plus a per-(slot, kv head) table
+ * of where each one's partials start. The size depends on n_slots, the head
+ * counts and max_ctx (which fixes how many work-groups the partial pass
+ * uses), not on the device positions. 0 if an argument is invalid. */
 size_t fa_decode_workspace_bytes(const fa_cache *cache, int n_slots, int n_head,
                                  int max_ctx);
 
 /* One decode step for slots 0..n_slots-1: the query row of slot s sits at
  * position d_pos[s] and attends K(d_pos[s]) of that slot's cache (its own
  * row already appended). Two launches on `stream` ([FA] "Decode-mode flash
- * attention" and slots sections): a partial pass over (split, kv head, slot)
- * whose per-slot plan is computed on the device from d_pos[s]; splits a slot
- * does not use write empty partials (m = -inf, l = 0, acc = 0). Then a combine
- * pass per (slot, head): M = max_s m_s, out = sum_s w_s acc_s / sum_s w_s l_s
- * with w_s = exp(m_s - M), splits in ascending order, no atomics, so a fixed
- * launch gives bit-identical results ([VT] MlaDecodeAttention determinism).
+ * attention" and slots sections):
+ *   1. partial pass: every slot's keys [0, d_pos[s]] are cut into splits by
+ *      fa_decode_plan, computed on the device from d_pos[s]. The splits of
+ *      all (slot, kv head) pairs form one work list that a fixed grid of
+ *      single-wave work-groups divides into equal contiguous runs; a wave
+ *      folds the splits of one (slot, kv head) in its run into one partial.
+ *   2. combine per (slot, head): M = max_r m_r, out = sum_r w_r acc_r /
+ *      sum_r w_r l_r with w_r = exp(m_r - M), partials in ascending key
+ *      order, no atomics, so a fixed launch gives bit-identical results
+ *      ([VT] MlaDecodeAttention determinism).
  *   q, out: device [n_slots][n_head][head_dim] fp32.
  *   d_pos:  device int32[n_slots]. A value outside [0, max_seq) reads no
  *           memory and makes that slot's output rows NaN.
  *   max_ctx_hint: host upper bound on d_pos[s]+1, 1..max_seq ([VT]
- *           PagedAttentionArgs max_seq_len: sizes the grid without a device
+ *           PagedAttentionArgs max_seq_len: sizes the launch without a device
  *           read). A slot with more keys than the hint is still computed
- *           exactly; it is only spread over fewer work-groups.
+ *           exactly.
  *   ws, ws_bytes: device scratch of at least
  *           fa_decode_workspace_bytes(cache, n_slots, n_head, max_ctx_hint).
- *   tile_stats: as in fa_prefill, decode key tiles of the plan's tile size.
+ *   tile_stats: as in fa_prefill, key tiles of the plan's tile size walked
+ *           split by split.
  * n_slots == 0 enqueues nothing. Other rules as fa_prefill. */
 int fa_decode(const fa_cache *cache, const float *q, const int *d_pos, int n_slots,
               int max_ctx_hint, int n_head, int attn_sink, int attn_win, float scale,
