@@ -61,13 +61,16 @@ def prefill_leg(fa, torch, w, steps: int, warmup: int) -> dict:
     cache, kt, vt = fa.make_cache(w.kv_format, 1, w.n_kv_head, w.head_dim, w.max_seq, dev)
     out = torch.empty_like(q)
     rows = w.pos0 + w.n
+    ws_bytes = fa.fa_prefill_workspace_bytes(w.n, w.n_head, w.n_kv_head, w.head_dim)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     ev = _events(torch, steps)
 
     def step(i=None):
         fa.fa_kv_append(cache, 0, 0, rows, kd, vd)
         if i is not None:
             ev[i][0].record()
-        fa.fa_prefill(cache, 0, q, w.pos0, w.n, w.n_head, w.attn_sink, w.attn_win, w.scale, out)
+        fa.fa_prefill(cache, 0, q, w.pos0, w.n, w.n_head, w.attn_sink, w.attn_win, w.scale, out,
+                      ws, ws_bytes)
         if i is not None:
             ev[i][1].record()
 

@@ -29,7 +29,7 @@ FA_KV_Q4_0 = 1
 
 EXPORTS = [
     "fa_cache_row_bytes", "fa_cache_bytes", "fa_init", "fa_kv_append", "fa_prefill",
-    "fa_prefill_tile_shape", "fa_decode_plan", "fa_decode_plan_params",
+    "fa_prefill_tile_shape", "fa_prefill_workspace_bytes", "fa_decode_plan", "fa_decode_plan_params",
     "fa_decode_workspace_bytes", "fa_decode", "fa_strerror",
 ]
 
@@ -50,7 +50,7 @@ class FaError(RuntimeError):
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is not built; run `python -m causal_gqa_flash_fa_amd.build` "
+            f"{LIB_PATH} is not built; run `python causal_gqa_flash_fa_amd/build.py` "
             "(there is no CPU fallback)")
     L = ctypes.CDLL(LIB_PATH)
     P, I, Z, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_float
@@ -64,8 +64,10 @@ def _load() -> ctypes.CDLL:
     L.fa_init.restype = I
     L.fa_kv_append.argtypes = [C, I, I, I, P, P, P]
     L.fa_kv_append.restype = I
-    L.fa_prefill.argtypes = [C, I, P, I, I, I, I, I, F, P, P, P]
+    L.fa_prefill.argtypes = [C, I, P, I, I, I, I, I, F, P, P, Z, P, P]
     L.fa_prefill.restype = I
+    L.fa_prefill_workspace_bytes.argtypes = [I, I, I, I]
+    L.fa_prefill_workspace_bytes.restype = Z
     L.fa_prefill_tile_shape.argtypes = [I, I, I, PI, PI]
     L.fa_prefill_tile_shape.restype = I
     L.fa_decode_plan.argtypes = [I, PI, PI]
@@ -132,11 +134,15 @@ def fa_kv_append(cache: fa_cache, slot: int, pos0: int, n: int, k_new, v_new,
 
 
 def fa_prefill(cache: fa_cache, slot: int, q, pos0: int, n: int, n_head: int,
-               attn_sink: int, attn_win: int, scale: float, out, tile_stats=None,
-               stream=None) -> None:
+               attn_sink: int, attn_win: int, scale: float, out, ws, ws_bytes: int,
+               tile_stats=None, stream=None) -> None:
     _check(lib.fa_prefill(ctypes.byref(cache), slot, _ptr(q), pos0, n, n_head, attn_sink,
-                          attn_win, scale, _ptr(out), _ptr(tile_stats), _stream(stream)),
-           "fa_prefill")
+                          attn_win, scale, _ptr(out), _ptr(ws), ws_bytes, _ptr(tile_stats),
+                          _stream(stream)), "fa_prefill")
+
+
+def fa_prefill_workspace_bytes(n: int, n_head: int, n_kv_head: int, head_dim: int) -> int:
+    return lib.fa_prefill_workspace_bytes(n, n_head, n_kv_head, head_dim)
 
 
 def fa_prefill_tile_shape(n_head: int, n_kv_head: int, head_dim: int) -> tuple[int, int]:

@@ -1,6 +1,7 @@
 """Builds libfa.so (the HIP kernels and their C-ABI) for gfx950 with hipcc.
 
-Usage: python -m causal_gqa_flash_fa_amd.build  (or build() from Python).
+Usage: python causal_gqa_flash_fa_amd/build.py  (run as a script: importing the
+package itself loads libfa.so).
 Each .hip file compiles in its own hipcc process; the objects are linked into
 causal_gqa_flash_fa_amd/libfa.so, which the Python binding loads.
 """

@@ -13,6 +13,7 @@ namespace {
 
 constexpr int kMaxDevices = 64;
 int g_device_ok[kMaxDevices];   // 0 unknown, 1 gfx950, -1 other
+int g_device_cus[kMaxDevices];  // compute units of each checked device
 
 bool dim_ok(int head_dim) { return head_dim == 64 || head_dim == 128 || head_dim == 256; }
 bool group_ok(int g) { return g == 1 || g == 2 || g == 4 || g == 8; }
@@ -42,6 +43,8 @@ size_t slot_stride_bytes(const fa_cache *c) {
 
 int hip_rc(hipError_t e) { return e == hipSuccess ? FA_OK : FA_EHIP; }
 
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
 }  // namespace
 
 extern "C" {
@@ -67,6 +70,7 @@ int fa_init(void) {
         hipDeviceProp_t prop;
         if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return FA_EHIP;
         g_device_ok[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+        g_device_cus[dev] = prop.multiProcessorCount;
     }
     return g_device_ok[dev] == 1 ? FA_OK : FA_EDEVICE;
 }
@@ -102,8 +106,60 @@ int fa_prefill_tile_shape(int n_head, int n_kv_head, int head_dim, int *q_positi
     return FA_OK;
 }
 
+namespace {
+// Stream-K prefill layout: pieces of cut segments and the segment table.
+struct PrefillLayout {
+    int n_qblocks;
+    size_t pieces, table_bytes, m_off, l_off, acc_off, total;
+};
+
+PrefillLayout prefill_layout(int n, int n_head, int n_kv_head, int head_dim) {
+    PrefillLayout p;
+    const int bq = fa::prefill_q_positions(n_head / n_kv_head);
+    const size_t rows = (size_t)fa::kPrefillWaves * fa::kPrefillRowsPerWave;
+    p.n_qblocks = (n + bq - 1) / bq;
+    const size_t nsegs = (size_t)n_kv_head * p.n_qblocks;
+    // cut segments own at most 2 * (work-groups - 1) pieces in total
+    p.pieces = 2 * (size_t)fa::kPrefillMaxWorkGroups;
+    p.table_bytes = align256(nsegs * 2 * sizeof(int));
+    p.m_off = p.table_bytes;
+    p.l_off = p.m_off + align256(p.pieces * rows * sizeof(float));
+    p.acc_off = p.l_off + align256(p.pieces * rows * sizeof(float));
+    p.total = p.acc_off + p.pieces * rows * (size_t)head_dim * sizeof(float);
+    return p;
+}
+
+// Visited key tiles of a prefill call: the stream-K grid never needs more
+// work-groups than that.
+long long prefill_tiles(int n, int pos0, int bq, int sink, int win) {
+    const int bk = fa::kPrefillKeyTile;
+    long long total = 0;
+    for (int q0 = pos0; q0 < pos0 + n; q0 += bq) {
+        const int q1 = q0 + bq - 1 < pos0 + n - 1 ? q0 + bq - 1 : pos0 + n - 1;
+        const int walked = q1 / bk + 1;
+        int count = walked;
+        if (win > 0) {
+            const int win_lo = q0 - win + 1;
+            const int wt = win_lo > 0 ? win_lo / bk : 0;
+            int nsink = ((sink > 0 ? sink : 0) + bk - 1) / bk;
+            if (nsink > walked) nsink = walked;
+            if (wt > nsink) count = nsink + (walked - wt);
+        }
+        total += count;
+    }
+    return total;
+}
+}  // namespace
+
+size_t fa_prefill_workspace_bytes(int n, int n_head, int n_kv_head, int head_dim) {
+    if (n < 0 || n_head < 1 || n_kv_head < 1 || n_head % n_kv_head ||
+        !group_ok(n_head / n_kv_head) || !dim_ok(head_dim))
+        return 0;
+    return prefill_layout(n, n_head, n_kv_head, head_dim).total;
+}
+
 int fa_prefill(const fa_cache *cache, int slot, const float *q, int pos0, int n, int n_head,
-               int attn_sink, int attn_win, float scale, float *out,
+               int attn_sink, int attn_win, float scale, float *out, void *ws, size_t ws_bytes,
                unsigned long long *tile_stats, void *stream) {
     int rc = check_cache(cache);
     if (rc) return rc;
@@ -112,25 +168,41 @@ int fa_prefill(const fa_cache *cache, int slot, const float *q, int pos0, int n,
     if (slot < 0 || slot >= cache->n_slots || pos0 < 0 || n < 0) return FA_EINVAL;
     if ((long long)pos0 + n > cache->max_seq) return FA_ERANGE;
     if (n == 0) return FA_OK;
-    if (!q || !out) return FA_ENULL;
+    if (!q || !out || !ws) return FA_ENULL;
+    const PrefillLayout lay = prefill_layout(n, n_head, cache->n_kv_head, cache->head_dim);
+    if (ws_bytes < lay.total) return FA_EWORKSPACE;
     if ((rc = fa_init())) return rc;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return FA_EHIP;
     const int group = n_head / cache->n_kv_head;
     const int bq = fa::prefill_q_positions(group);
+    const int sink = attn_sink < 0 ? 0 : attn_sink;
+    long long n_wg = g_device_cus[dev] < fa::kPrefillMaxWorkGroups ? g_device_cus[dev]
+                                                                   : fa::kPrefillMaxWorkGroups;
+    const long long tiles = (long long)cache->n_kv_head * prefill_tiles(n, pos0, bq, sink, attn_win);
+    if (tiles < n_wg) n_wg = tiles;
+    if (n_wg < 1) n_wg = 1;
+    uint8_t *wsb = (uint8_t *)ws;
     fa::PrefillArgs a;
     a.q = q;
     a.out = out;
     a.k = (const uint8_t *)cache->k + (size_t)slot * slot_stride_bytes(cache);
     a.v = (const uint8_t *)cache->v + (size_t)slot * slot_stride_bytes(cache);
     a.stats = tile_stats;
+    a.seg_table = (int *)wsb;
+    a.ws_m = (float *)(wsb + lay.m_off);
+    a.ws_l = (float *)(wsb + lay.l_off);
+    a.ws_acc = (float *)(wsb + lay.acc_off);
     a.n = n;
     a.pos0 = pos0;
     a.n_head = n_head;
     a.n_kv = cache->n_kv_head;
     a.max_seq = cache->max_seq;
-    a.sink = attn_sink < 0 ? 0 : attn_sink;
+    a.sink = sink;
     a.win = attn_win;
     a.qscale = scale * fa::kLog2e;
-    a.n_qblocks = (n + bq - 1) / bq;
+    a.n_qblocks = lay.n_qblocks;
+    a.n_wg = (int)n_wg;
     return hip_rc(fa::launch_prefill(cache->format, cache->head_dim, group, a,
                                      (hipStream_t)stream));
 }
@@ -157,8 +229,6 @@ struct DecodeLayout {
     int waves;
     size_t max_partials, table_bytes, m_off, l_off, acc_off, total;
 };
-
-size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 DecodeLayout decode_layout(const fa_cache *c, int n_slots, int n_head, int max_ctx) {
     DecodeLayout d;

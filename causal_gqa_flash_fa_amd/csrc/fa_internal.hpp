@@ -20,10 +20,13 @@ struct PrefillArgs {
     float *out;                   // [n][n_head][hd]
     const void *k, *v;            // slot base: [n_kv][max_seq][row]
     unsigned long long *stats;    // NULL or [2]
+    float *ws_m, *ws_l, *ws_acc;  // pieces of cut segments: [piece][rows](+[hd])
+    int *seg_table;               // [n_kv * n_qblocks][2]: first piece, piece count
     int n, pos0, n_head, n_kv, max_seq;
     int sink, win;
     float qscale;                 // scale * log2(e)
     int n_qblocks;
+    int n_wg;                     // work-groups of the stream-K grid
 };
 
 struct DecodeArgs {
@@ -44,6 +47,8 @@ struct DecodeArgs {
 constexpr int kPrefillWaves = 4;
 constexpr int kPrefillRowsPerWave = 32;
 constexpr int kPrefillKeyTile = 32;
+// Stream-K prefill grid: at most one work-group per CU of a 256-CU MI355X.
+constexpr int kPrefillMaxWorkGroups = 256;
 // Decode: single-wave work-groups folding tiles of 64 keys (one per lane).
 constexpr int kDecodeKeyTile = 64;
 // Split plan constants: about kDecodeKps keys per split, at most

@@ -22,8 +22,15 @@
 //     per-lane multiply, done only when some row's max moved.
 //   * Q4_0 tiles are loaded as raw 18-byte blocks and decoded exactly
 //     ((c-8)*d) while being written to the fp32 LDS tile.
-//   * Heavy (late) query blocks are dispatched first. The next tile's global
-//     loads are issued into registers before the current tile is computed.
+//   * Stream-K schedule: the visited key tiles of every (kv head, query
+//     block) segment form one list, and a grid of one work-group per CU takes
+//     equal contiguous runs of it, so a long causal row is spread over several
+//     CUs instead of setting the critical path. A segment cut by a run
+//     boundary writes per-piece partials {m, l, acc} that a small combine
+//     kernel merges ([FA] decode combine formula); a whole segment writes its
+//     output directly.
+//   * The next tile's global loads are issued into registers before the
+//     current tile is computed.
 #include "fa_device.hpp"
 #include "fa_internal.hpp"
 
@@ -49,27 +56,153 @@ struct PrefillShape {
     static constexpr size_t LDS_BYTES = (size_t)2 * BK * KS * sizeof(float);
 };
 
+// Visited key tiles of the query block [q0, q1] ([FA] fc_attn_tile_in_window
+// over the union of the block's key sets): the causal walk has q1/BK + 1
+// tiles; with a window, tiles below the sink or reaching the union window
+// [q0 - win + 1, q1] are visited and the rest are skipped.
+struct SegTiles {
+    int walked, nsink, wt, count;       // visited tile i -> i < nsink ? i : wt + i - nsink
+    __device__ int tile(int i) const { return i < nsink ? i : wt + i - nsink; }
+};
+
+__device__ __forceinline__ SegTiles seg_tiles(int q0, int q1, int sink, int win, int bk) {
+    SegTiles t;
+    t.walked = q1 / bk + 1;
+    t.nsink = t.walked;
+    t.wt = t.walked;
+    t.count = t.walked;
+    if (win > 0) {
+        const int win_lo = q0 - win + 1;
+        const int wt = win_lo > 0 ? win_lo / bk : 0;
+        const int nsink = min((max(sink, 0) + bk - 1) / bk, t.walked);
+        if (wt > nsink) {
+            t.nsink = nsink;
+            t.wt = wt;
+            t.count = nsink + (t.walked - wt);
+        }
+    }
+    return t;
+}
+
+// Block-wide exclusive scan of one int per thread (256 threads); also
+// returns the total. `scratch` holds 4 ints.
+__device__ __forceinline__ int block_excl_scan(int x, int tid, int *scratch, int *total) {
+    const int lane = tid & 63, w = tid >> 6;
+    int incl = x;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o);
+        if (lane >= o) incl += y;
+    }
+    __syncthreads();
+    if (lane == 63) scratch[w] = incl;
+    __syncthreads();
+    int before = 0, sum = 0;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const int v = scratch[i];
+        before += i < w ? v : 0;
+        sum += v;
+    }
+    *total = sum;
+    return before + incl - x;
+}
+
 template <int HD, int G, int FMT>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void prefill_kernel(PrefillArgs a) {
     using Sh = PrefillShape<HD, G, FMT>;
     constexpr int BK = Sh::BK, KS = Sh::KS, NT = Sh::NT, GS = Sh::GS, HH = Sh::HH;
     constexpr int NB = Sh::NB, RB = Sh::RB;
+    constexpr int ROWS = Sh::W * Sh::R;
     extern __shared__ float lds[];
     float *Ks = lds;
     float *Vs = lds + BK * KS;
+    __shared__ int scan_scratch[4];
+    __shared__ int run_info[8];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = tid >> 6;
     const int hlf = lane >> 5;        // which half of the contraction / key sub-block
     const int r32 = lane & 31;        // this lane's query row within the wave
+    const int wg = blockIdx.x;
+    const int NWG = gridDim.x;
+    const int nsegs = a.n_kv * a.n_qblocks;
 
-    const int bid = blockIdx.x;
-    const int qb = a.n_qblocks - 1 - bid / a.n_kv;   // heavy blocks first
-    const int kvh = bid % a.n_kv;
-    const int q0 = a.pos0 + qb * Sh::BQ;
-    const int q1 = min(q0 + Sh::BQ - 1, a.pos0 + a.n - 1);
+    auto seg_of = [&](int s, int *q0, int *q1) {
+        const int qb = s % a.n_qblocks;
+        *q0 = a.pos0 + qb * Sh::BQ;
+        *q1 = min(*q0 + Sh::BQ - 1, a.pos0 + a.n - 1);
+    };
+
+    // ---- schedule: total tiles, this work-group's run, the piece table
+    int total = 0;
+    for (int base = 0; base < nsegs; base += 256) {
+        const int s = base + tid;
+        int cnt = 0;
+        if (s < nsegs) {
+            int q0, q1;
+            seg_of(s, &q0, &q1);
+            cnt = seg_tiles(q0, q1, a.sink, a.win, BK).count;
+        }
+        int chunk;
+        block_excl_scan(cnt, tid, scan_scratch, &chunk);
+        total += chunk;
+    }
+    const long long lo = (long long)wg * total / NWG;
+    const long long hi = (long long)(wg + 1) * total / NWG;
+    auto owner = [&](long long f) -> int { return (int)(((f + 1) * NWG - 1) / total); };
+    if (tid == 0) {
+        run_info[0] = -1;          // first segment of the run
+        run_info[1] = -1;          // last segment of the run
+    }
+    {
+        int f_carry = 0, p_carry = 0;
+        for (int base = 0; base < nsegs; base += 256) {
+            const int s = base + tid;
+            int cnt = 0;
+            if (s < nsegs) {
+                int q0, q1;
+                seg_of(s, &q0, &q1);
+                cnt = seg_tiles(q0, q1, a.sink, a.win, BK).count;
+            }
+            int chunk, chunk_p;
+            const int F = f_carry + block_excl_scan(cnt, tid, scan_scratch, &chunk);
+            const int np = cnt > 0 ? owner(F + cnt - 1) - owner(F) + 1 : 0;
+            const int pc = np > 1 ? np : 0;
+            const int P = p_carry + block_excl_scan(pc, tid, scan_scratch, &chunk_p);
+            if (wg == 0 && s < nsegs) {
+                a.seg_table[2 * s] = P;
+                a.seg_table[2 * s + 1] = np;
+            }
+            if (cnt > 0 && F <= lo && lo < F + cnt) {
+                run_info[0] = s;
+                run_info[2] = F;
+                run_info[3] = P;
+            }
+            if (cnt > 0 && F < hi && hi <= F + cnt) {
+                run_info[1] = s;
+                run_info[4] = F;
+                run_info[5] = P;
+            }
+            f_carry += chunk;
+            p_carry += chunk_p;
+        }
+    }
+    __syncthreads();
+    const int s_first = run_info[0], s_last = run_info[1];
+
+    unsigned visited = 0, skipped = 0;
+
+    // ---- fold tiles [t_lo, t_hi) of one segment; whole segments write out,
+    // cut ones write piece `piece` of the partial buffer
+    auto run_segment = [&](int seg, int t_lo, int t_hi, bool whole, int piece, bool first_owner) {
+    const int kvh = seg / a.n_qblocks;
+    int q0, q1;
+    seg_of(seg, &q0, &q1);
+    const SegTiles st = seg_tiles(q0, q1, a.sink, a.win, BK);
+    if (first_owner) skipped += (unsigned)(st.walked - st.count);
 
     const int row_wg = w * Sh::R + r32;
     const int p_row = q0 + row_wg / G;
@@ -102,18 +235,6 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int n = 0; n < NT; n++) O[n] = f32x16{};
     float m_run = -INFINITY, l_run = 0.0f;
-
-    // ---- tile walk ([FA] fc_attn_tile_in_window over the block's rows)
-    unsigned visited = 0, skipped = 0;
-    const int win_lo = q0 - a.win + 1;    // first key of the union of the rows' windows
-    auto first_visited = [&](int j0) -> int {
-        if (j0 <= q1 && a.win > 0 && j0 >= a.sink && j0 + BK - 1 < win_lo) {
-            const int jn = (win_lo / BK) * BK;
-            skipped += (unsigned)((jn - j0) / BK);
-            return jn;
-        }
-        return j0;
-    };
 
     // ---- staging registers for the next tile
     f32x4 pk[FMT == 0 ? Sh::NC : 1], pv[FMT == 0 ? Sh::NC : 1];
@@ -244,26 +365,39 @@ void prefill_kernel(PrefillArgs a) {
         }
     };
 
-    int j0 = first_visited(0);
-    if (j0 <= q1) load_tile(j0);
-    while (j0 <= q1) {
+    int ti = t_lo;
+    if (ti < t_hi) load_tile(st.tile(ti) * BK);
+    while (ti < t_hi) {
         __syncthreads();          // previous tile fully consumed
         store_tile();
         __syncthreads();
-        const int jc = j0;
+        const int jc = st.tile(ti) * BK;
         visited++;
-        j0 = first_visited(jc + BK);
-        if (j0 <= q1) load_tile(j0);
+        ti++;
+        if (ti < t_hi) load_tile(st.tile(ti) * BK);
         const bool wave_do = wave_live && jc <= pw1 &&
                              (a.win <= 0 || jc < a.sink || jc + BK - 1 >= pw0 - a.win + 1);
         if (wave_do) compute_tile(jc);
     }
 
-    // ---- finalise: out = acc / l, scattered back through the d permutation
+    // ---- finalise: out = acc / l (whole segment) or this piece's partial,
+    // scattered back through the d permutation
     const float l_tot = l_run + __shfl_xor(l_run, 32);
-    if (row_live) {
-        const float inv = 1.0f / l_tot;
-        float *op = a.out + ((size_t)(p_row - a.pos0) * a.n_head + kvh * G + g) * HD;
+    float *op;
+    float scale_out;
+    if (whole) {
+        op = a.out + ((size_t)(p_row - a.pos0) * a.n_head + kvh * G + g) * HD;
+        scale_out = 1.0f / l_tot;
+    } else {
+        const size_t prow = (size_t)piece * ROWS + row_wg;
+        op = a.ws_acc + prow * HD;
+        scale_out = 1.0f;
+        if (hlf == 0) {
+            a.ws_m[prow] = m_run;
+            a.ws_l[prow] = l_tot;
+        }
+    }
+    if (row_live || !whole) {
 #pragma unroll
         for (int r = 0; r < 16; r++) {
             const int mi = 8 * (r >> 2) + 4 * hlf + (r & 3);
@@ -272,17 +406,70 @@ void prefill_kernel(PrefillArgs a) {
                 float *dst = op + ng * 32 * GS + GS * mi;
                 if constexpr (GS == 4) {
                     *(f32x4 *)dst = f32x4{O[ng * 4 + 0][r], O[ng * 4 + 1][r], O[ng * 4 + 2][r],
-                                          O[ng * 4 + 3][r]} * inv;
+                                          O[ng * 4 + 3][r]} * scale_out;
                 } else {
-                    *(f32x2 *)dst = f32x2{O[ng * 2 + 0][r], O[ng * 2 + 1][r]} * inv;
+                    *(f32x2 *)dst = f32x2{O[ng * 2 + 0][r], O[ng * 2 + 1][r]} * scale_out;
                 }
             }
+        }
+    }
+    };   // run_segment
+
+    if (s_first >= 0 && lo < hi) {
+        int F = run_info[2];
+        for (int seg = s_first; seg <= s_last; seg++) {
+            int q0, q1;
+            seg_of(seg, &q0, &q1);
+            const int cnt = seg_tiles(q0, q1, a.sink, a.win, BK).count;
+            if (cnt > 0) {
+                const int t_lo = (int)max(lo - F, 0LL);
+                const int t_hi = (int)min(hi - F, (long long)cnt);
+                const int f_owner = owner(F);
+                const bool whole = owner(F + cnt - 1) == f_owner;
+                int piece = 0;
+                if (!whole) {
+                    // piece table offset of a cut segment: only the run's
+                    // first and last segments can be cut
+                    const int P = seg == s_first ? run_info[3] : run_info[5];
+                    piece = P + (wg - f_owner);
+                }
+                run_segment(seg, t_lo, t_hi, whole, piece, F >= lo);
+            }
+            F += cnt;
         }
     }
     if (a.stats && tid == 0) {
         atomicAdd(&a.stats[0], (unsigned long long)visited);
         atomicAdd(&a.stats[1], (unsigned long long)skipped);
     }
+}
+
+// Merges the pieces of segments cut between work-groups:
+// out = sum_p exp2(m_p - M) acc_p / sum_p exp2(m_p - M) l_p, ascending p.
+// One work-group per (row, segment), one thread per output dim.
+template <int HD, int G>
+__global__ __launch_bounds__(HD) void prefill_combine_kernel(PrefillArgs a) {
+    constexpr int ROWS = kPrefillWaves * kPrefillRowsPerWave;
+    constexpr int BQ = ROWS / G;
+    const int row = blockIdx.x;
+    const int seg = blockIdx.y;
+    const int np = a.seg_table[2 * seg + 1];
+    if (np <= 1) return;
+    const int qb = seg % a.n_qblocks, kvh = seg / a.n_qblocks;
+    const int p = a.pos0 + qb * BQ + row / G;
+    if (p > a.pos0 + a.n - 1) return;
+    const int P = a.seg_table[2 * seg];
+    const int dd = threadIdx.x;
+    float M = -INFINITY;
+    for (int k = 0; k < np; k++) M = fmaxf(M, a.ws_m[(size_t)(P + k) * ROWS + row]);
+    float o = 0.0f, L = 0.0f;
+    for (int k = 0; k < np; k++) {
+        const size_t pr = (size_t)(P + k) * ROWS + row;
+        const float wgt = fast_exp2(a.ws_m[pr] - M);
+        L += a.ws_l[pr] * wgt;
+        o += a.ws_acc[pr * HD + dd] * wgt;
+    }
+    a.out[((size_t)(p - a.pos0) * a.n_head + kvh * G + row % G) * HD + dd] = o / L;
 }
 
 template <int HD, int G, int FMT>
@@ -296,8 +483,12 @@ hipError_t launch_one(const PrefillArgs &a, hipStream_t s) {
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    const dim3 grid((unsigned)(a.n_qblocks * a.n_kv));
-    hipLaunchKernelGGL((prefill_kernel<HD, G, FMT>), grid, dim3(256), Sh::LDS_BYTES, s, a);
+    hipLaunchKernelGGL((prefill_kernel<HD, G, FMT>), dim3(a.n_wg), dim3(256), Sh::LDS_BYTES, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((prefill_combine_kernel<HD, G>),
+                       dim3(kPrefillWaves * kPrefillRowsPerWave, a.n_qblocks * a.n_kv), dim3(HD), 0,
+                       s, a);
     return hipGetLastError();
 }
 

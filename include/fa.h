@@ -108,13 +108,22 @@ int fa_kv_append(const fa_cache *cache, int slot, int pos0, int n,
  *   q:   device [n][n_head][head_dim] fp32.  out: device, same shape.
  *   n_head % n_kv_head == 0, G in {1,2,4,8}; head_dim in {64,128,256};
  *   scale finite and > 0 (applied to q.k); attn_sink < 0 acts as 0.
+ *   ws, ws_bytes: device scratch of at least fa_prefill_workspace_bytes().
  *   tile_stats: NULL, or device uint64[2] to which the call ADDS the number
  *   of key tiles it visited ([0]) and window-skipped ([1]); tile geometry
  *   from fa_prefill_tile_shape(). Tiles past the causal bound are neither.
- * Rows of q and out must not overlap. */
+ * Rows of q and out must not overlap. Two launches on `stream`. */
 int fa_prefill(const fa_cache *cache, int slot, const float *q, int pos0, int n,
                int n_head, int attn_sink, int attn_win, float scale, float *out,
-               unsigned long long *tile_stats, void *stream);
+               void *ws, size_t ws_bytes, unsigned long long *tile_stats, void *stream);
+
+/* Workspace fa_prefill needs for n query rows: when a query block's key
+ * tiles are spread over several work-groups (the schedule balances the
+ * causal triangle across CUs), each part leaves a partial {m, l, acc} per
+ * row ([FA] decode partial form) that a second launch merges; plus a table
+ * per (kv head, query block). Independent of pos0 and of the data. 0 if an
+ * argument is invalid. */
+size_t fa_prefill_workspace_bytes(int n, int n_head, int n_kv_head, int head_dim);
 
 /* Tile geometry fa_prefill uses for a shape: each work-group owns
  * *q_positions consecutive query positions (from pos0) of one kv head and

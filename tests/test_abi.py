@@ -45,9 +45,10 @@ def rc_append(c, slot=0, pos0=0, n=1, kn=FAKE, vn=FAKE):
                                None)
 
 
-def rc_prefill(c, slot=0, q=FAKE, pos0=0, n=1, n_head=4, sink=0, win=0, scale=0.1, out=FAKE):
+def rc_prefill(c, slot=0, q=FAKE, pos0=0, n=1, n_head=4, sink=0, win=0, scale=0.1, out=FAKE,
+               ws=FAKE, ws_bytes=1 << 30):
     return fa.lib.fa_prefill(ctypes.byref(c) if c is not None else None, slot, q, pos0, n,
-                             n_head, sink, win, scale, out, None, None)
+                             n_head, sink, win, scale, out, ws, ws_bytes, None, None)
 
 
 def rc_decode(c, q=FAKE, pos=FAKE, n_slots=1, hint=10, n_head=4, scale=0.1, out=FAKE, ws=FAKE,
@@ -97,6 +98,14 @@ def test_prefill_validation():
     assert rc_prefill(c, n=0) == fa.FA_OK
     assert rc_prefill(c, q=0) == fa.FA_ENULL
     assert rc_prefill(c, out=0) == fa.FA_ENULL
+    assert rc_prefill(c, ws=0) == fa.FA_ENULL
+    need = fa.fa_prefill_workspace_bytes(40, 4, 2, 128)
+    assert need > 0
+    assert rc_prefill(c, n=40, ws_bytes=need - 1) == fa.FA_EWORKSPACE
+    assert fa.fa_prefill_workspace_bytes(40, 6, 2, 128) == 0      # group 3
+    assert fa.fa_prefill_workspace_bytes(40, 4, 2, 96) == 0
+    # the table grows with the number of query blocks, the pieces do not
+    assert fa.fa_prefill_workspace_bytes(40000, 4, 2, 128) >= need
 
 
 def test_decode_validation():

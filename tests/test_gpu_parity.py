@@ -101,7 +101,9 @@ def run_prefill(fmt, q, k, v, pos0, n_head, sink, win, scale, max_seq=None, slot
     qd = U.to_dev(q)
     out = torch.full_like(qd, float("nan"))
     stats = torch.zeros(2, dtype=torch.int64, device=U.device())
-    fa.fa_prefill(cache, slot, qd, pos0, n, n_head, sink, win, scale, out, stats)
+    ws_bytes = fa.fa_prefill_workspace_bytes(n, n_head, n_kv, hd)
+    ws = torch.full((ws_bytes,), 0xff, dtype=torch.uint8, device=U.device())  # NaN-poisoned
+    fa.fa_prefill(cache, slot, qd, pos0, n, n_head, sink, win, scale, out, ws, ws_bytes, stats)
     torch.cuda.synchronize()
     return out.cpu().numpy(), tuple(int(x) for x in stats.cpu().numpy()), (kt, vt)
 
@@ -159,7 +161,7 @@ def test_prefill_other_slot_and_empty_call():
     U.compare_rows(out, ref, U.TOL_F32, "prefill slot 2")
     cache, kt, vt = fa.make_cache(fa.FA_KV_F32, 1, 1, 64, 8, U.device())
     o = torch.full((1, 4, 64), 7.0, device=U.device())
-    fa.fa_prefill(cache, 0, o, 8, 0, 4, 0, 0, 0.1, o)
+    fa.fa_prefill(cache, 0, o, 8, 0, 4, 0, 0, 0.1, o, None, 0)
     torch.cuda.synchronize()
     assert bool((o == 7.0).all())
 
