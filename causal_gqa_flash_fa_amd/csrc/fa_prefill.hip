@@ -29,8 +29,17 @@
 //     boundary writes per-piece partials {m, l, acc} that a small combine
 //     kernel merges ([FA] decode combine formula); a whole segment writes its
 //     output directly.
-//   * The next tile's global loads are issued into registers before the
-//     current tile is computed.
+//   * K/V tiles are double-buffered in LDS with one barrier per tile: fp32
+//     rows go straight from global memory into the next buffer
+//     (global_load_lds_dwordx4, one row per wave instruction, so no staging
+//     registers), Q4_0 blocks are staged in registers and decoded into the
+//     next buffer after the current tile's matrix work.
+//   * Lazy rescale: a row's reference max only moves when a tile's max
+//     exceeds it by more than kTau (log2 units). Probabilities are then
+//     bounded by 2^kTau, and the O rescale (a pass over all accumulators)
+//     runs a few times per row instead of on most tiles; the final acc / l
+//     is unchanged up to rounding because acc and l share the reference.
+//   * Tiles inside every row's key set skip the mask.
 #include "fa_device.hpp"
 #include "fa_internal.hpp"
 
@@ -53,8 +62,38 @@ struct PrefillShape {
     static constexpr int NC = BK * HD / 4 / 256;                       // fp32 float4 per thread per tensor
     static constexpr int QITEMS = 2 * BK * NB;                         // Q4 (row, block) items, K and V
     static constexpr int IPT = (QITEMS + 255) / 256;                   // Q4 items per thread
-    static constexpr size_t LDS_BYTES = (size_t)2 * BK * KS * sizeof(float);
+    static constexpr int BUF = 2 * BK * KS;     // floats per buffer: K tile then V tile
+    static constexpr size_t LDS_BYTES = (size_t)2 * BUF * sizeof(float);
 };
+
+// Reference-max slack of the lazy rescale (log2 units): p <= 2^kTau.
+constexpr float kTau = 8.0f;
+
+// 16-byte global -> LDS copy: lane i writes lds_row[4i .. 4i+3] (the LDS
+// base is wave-uniform; inactive lanes write nothing).
+__device__ __forceinline__ void dma16(const float *g, float *lds_row) {
+    __builtin_amdgcn_global_load_lds((const void *)g,
+                                     (__attribute__((address_space(3))) void *)lds_row, 16, 0, 0);
+}
+
+// acc *= c in place in the accumulation registers, one element at a time
+// through a single temporary VGPR: keeps the O accumulators in AGPRs (a
+// plain multiply makes the compiler carry a VGPR copy of all of O).
+__device__ __forceinline__ void scale_acc(f32x16 &acc, float c) {
+#pragma unroll
+    for (int r = 0; r < 16; r++) {
+        float x = acc[r], t;
+        asm volatile("v_accvgpr_read_b32 %1, %0\n\t"
+                     "v_mul_f32 %1, %1, %2\n\t"
+                     "v_accvgpr_write_b32 %0, %1"
+                     : "+a"(x), "=&v"(t)
+                     : "v"(c));
+        acc[r] = x;
+    }
+}
+
+// Wait for all of this wave's vector-memory operations (incl. LDS DMA).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Visited key tiles of the query block [q0, q1] ([FA] fc_attn_tile_in_window
 // over the union of the block's key sets): the causal walk has q1/BK + 1
@@ -116,8 +155,6 @@ void prefill_kernel(PrefillArgs a) {
     constexpr int NB = Sh::NB, RB = Sh::RB;
     constexpr int ROWS = Sh::W * Sh::R;
     extern __shared__ float lds[];
-    float *Ks = lds;
-    float *Vs = lds + BK * KS;
     __shared__ int scan_scratch[4];
     __shared__ int run_info[8];
 
@@ -236,23 +273,26 @@ void prefill_kernel(PrefillArgs a) {
     for (int n = 0; n < NT; n++) O[n] = f32x16{};
     float m_run = -INFINITY, l_run = 0.0f;
 
-    // ---- staging registers for the next tile
-    f32x4 pk[FMT == 0 ? Sh::NC : 1], pv[FMT == 0 ? Sh::NC : 1];
+    // ---- staging registers of a Q4_0 tile (fp32 tiles need none)
     uint32_t raw[FMT == 0 ? 1 : Sh::IPT][9];
 
-    auto load_tile = [&](int j0) {
+    // Starts loading the tile at key j0 into LDS buffer `buf` (fp32: DMA
+    // into LDS; Q4_0: raw blocks into registers). Rows past q1 (only in a
+    // block's diagonal tile) repeat row q1 (fp32) or are zero (Q4_0): their
+    // scores are masked, and V must stay finite so that p = 0 contributes 0.
+    auto issue_tile = [&](int j0, int buf) {
         if constexpr (FMT == 0) {
+            constexpr int LPR = HD / 4;           // lanes per row: 16-byte chunks
+            constexpr int RPW = BK / Sh::W;       // rows per wave per tensor
+            float *kd = lds + buf * Sh::BUF;
+            float *vd = kd + BK * KS;
+            if (lane < LPR) {
 #pragma unroll
-            for (int i = 0; i < Sh::NC; i++) {
-                const int c = tid + 256 * i;
-                const int row = c / (HD / 4), c4 = c % (HD / 4);
-                if (j0 + row <= q1) {
-                    const size_t off = (size_t)(j0 + row) * HD + 4 * c4;
-                    pk[i] = *(const f32x4 *)((const float *)kbase + off);
-                    pv[i] = *(const f32x4 *)((const float *)vbase + off);
-                } else {
-                    pk[i] = f32x4{};
-                    pv[i] = f32x4{};
+                for (int i = 0; i < RPW; i++) {
+                    const int row = w * RPW + i;
+                    const size_t off = (size_t)min(j0 + row, q1) * HD + 4 * lane;
+                    dma16((const float *)kbase + off, kd + row * KS);
+                    dma16((const float *)vbase + off, vd + row * KS);
                 }
             }
         } else {
@@ -275,23 +315,18 @@ void prefill_kernel(PrefillArgs a) {
         }
     };
 
-    auto store_tile = [&]() {
-        if constexpr (FMT == 0) {
-#pragma unroll
-            for (int i = 0; i < Sh::NC; i++) {
-                const int c = tid + 256 * i;
-                const int row = c / (HD / 4), c4 = c % (HD / 4);
-                *(f32x4 *)&Ks[row * KS + 4 * c4] = pk[i];
-                *(f32x4 *)&Vs[row * KS + 4 * c4] = pv[i];
-            }
-        } else {
+    // Q4_0 only: decode the staged blocks into LDS buffer `buf`.
+    auto store_tile = [&](int buf) {
+        if constexpr (FMT == 1) {
+            float *kd = lds + buf * Sh::BUF;
+            float *vd = kd + BK * KS;
 #pragma unroll
             for (int i = 0; i < Sh::IPT; i++) {
                 const int idx = tid + 256 * i;
                 if (idx < Sh::QITEMS) {
                     const int rem = idx % (BK * NB);
                     const int row = rem / NB, blk = rem % NB;
-                    float *dst = (idx < BK * NB ? Ks : Vs) + row * KS + blk * kQ4Block;
+                    float *dst = (idx < BK * NB ? kd : vd) + row * KS + blk * kQ4Block;
                     const float d = half_bits_to_float(raw[i][0]);
                     const float m8d = -8.0f * d;
 #pragma unroll
@@ -310,7 +345,9 @@ void prefill_kernel(PrefillArgs a) {
         }
     };
 
-    auto compute_tile = [&](int jc) {
+    auto compute_tile = [&](int jc, int buf) {
+        const float *Ks = lds + buf * Sh::BUF;
+        const float *Vs = Ks + BK * KS;
         // S^T = K Q^T: lane holds row r32, keys 8*(r/4) + 4*hlf + r%4
         f32x16 s = f32x16{};
         const float *krow = Ks + r32 * KS + hlf * HH;
@@ -320,30 +357,45 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
             for (int t = 0; t < 4; t++) s = mfma32(kv[t], qr[4 * i + t], s);
         }
-        float tmax = -INFINITY;
+        // every key of the tile is in the key set of every row of the wave
+        const bool full = jc + BK - 1 <= pw0 &&
+                          (a.win <= 0 || jc + BK - 1 < a.sink || jc >= pw1 - a.win + 1);
+        if (!full) {
+            // key j is live for this row iff lo_win <= j <= p_row or j < sink_end
+            const int hi_key = row_live ? p_row : -1;
+            const int lo_win = a.win > 0 ? p_row - a.win + 1 : 0;
+            const int sink_end = a.win > 0 ? min(a.sink, hi_key + 1) : 0;
 #pragma unroll
-        for (int r = 0; r < 16; r++) {
-            const int key = jc + 8 * (r >> 2) + 4 * hlf + (r & 3);
-            const bool ok = row_live && in_key_set(key, p_row, a.sink, a.win);
-            s[r] = ok ? s[r] : -INFINITY;
-            tmax = fmaxf(tmax, s[r]);
+            for (int r = 0; r < 16; r++) {
+                const int key = jc + 8 * (r >> 2) + 4 * hlf + (r & 3);
+                const bool ok = (key <= hi_key) & ((key >= lo_win) | (key < sink_end));
+                s[r] = ok ? s[r] : -INFINITY;
+            }
         }
+        float tmax = s[0];
+#pragma unroll
+        for (int r = 1; r < 16; r++) tmax = fmaxf(tmax, s[r]);
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-        const float m_new = fmaxf(m_run, tmax);
-        const float m_use = m_new == -INFINITY ? 0.0f : m_new;   // all-masked row: keep p = 0
-        const float corr = fast_exp2(m_run - m_use);
+        // move the reference max only when the tile max passes it by kTau
+        // (from -inf: whenever the tile has a live key)
+        const bool rebase = tmax > m_run + kTau;
+        if (__ballot(rebase)) {
+            const float corr = rebase ? fast_exp2(m_run - tmax) : 1.0f;
+            if (__ballot(rebase && m_run != -INFINITY)) {   // rows starting at -inf hold O = 0
+#pragma unroll
+                for (int n = 0; n < NT; n++) scale_acc(O[n], corr);
+            }
+            l_run *= corr;
+            m_run = rebase ? tmax : m_run;
+        }
+        const float m_use = m_run == -INFINITY ? 0.0f : m_run;   // all-masked row: keep p = 0
         float psum = 0.0f;
 #pragma unroll
         for (int r = 0; r < 16; r++) {
             s[r] = fast_exp2(s[r] - m_use);
             psum += s[r];
         }
-        l_run = l_run * corr + psum;
-        if (__ballot(m_new > m_run)) {
-#pragma unroll
-            for (int n = 0; n < NT; n++) O[n] *= corr;
-        }
-        m_run = m_new;
+        l_run += psum;
 
         // O^T += V^T P^T: contraction step kk covers keys 8*(kk/4) + 4*hlf + kk%4
 #pragma unroll
@@ -365,19 +417,27 @@ void prefill_kernel(PrefillArgs a) {
         }
     };
 
+    // Double-buffered walk, one barrier per tile: the barrier makes tile ti
+    // (buffer buf) visible and guarantees every wave is done with buf ^ 1,
+    // which then receives tile ti + 1 while tile ti is computed.
+    __syncthreads();              // the previous segment no longer reads either buffer
+    int buf = 0;
     int ti = t_lo;
-    if (ti < t_hi) load_tile(st.tile(ti) * BK);
+    issue_tile(st.tile(ti) * BK, 0);
+    store_tile(0);
     while (ti < t_hi) {
-        __syncthreads();          // previous tile fully consumed
-        store_tile();
+        wait_vmem();
         __syncthreads();
         const int jc = st.tile(ti) * BK;
         visited++;
         ti++;
-        if (ti < t_hi) load_tile(st.tile(ti) * BK);
+        const bool more = ti < t_hi;
+        if (more) issue_tile(st.tile(ti) * BK, buf ^ 1);
         const bool wave_do = wave_live && jc <= pw1 &&
                              (a.win <= 0 || jc < a.sink || jc + BK - 1 >= pw0 - a.win + 1);
-        if (wave_do) compute_tile(jc);
+        if (wave_do) compute_tile(jc, buf);
+        if (more) store_tile(buf ^ 1);
+        buf ^= 1;
     }
 
     // ---- finalise: out = acc / l (whole segment) or this piece's partial,

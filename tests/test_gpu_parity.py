@@ -145,6 +145,32 @@ def test_prefill_sweep(case):
     assert stats == oracle.prefill_tile_counts(n, pos0, Hkv, sink, win, bq, bk)
 
 
+GROWTH_CASES = [
+    # fmt, n, pos0, H, Hkv, hd, sink, win
+    (0, 300, 0, 8, 1, 256, 0, 0),
+    (1, 260, 5, 16, 2, 128, 0, 0),
+    (0, 333, 0, 4, 2, 64, 4, 100),
+    (1, 200, 0, 8, 8, 256, 0, 0),
+]
+
+
+@pytest.mark.parametrize("case", GROWTH_CASES, ids=[str(c) for c in GROWTH_CASES])
+def test_prefill_growing_scores(case):
+    """Key norms grow along the sequence (row j scaled by 1 + j/16), so a row's
+    running max keeps climbing far past its first value: the accumulator
+    rescale on a live O runs many times per row."""
+    fmt, n, pos0, H, Hkv, hd, sink, win = case
+    seed = 3000 + sum(case)
+    q, k, v = workloads.custom_prefill(seed, n, pos0, H, Hkv, hd)
+    k = (k * (1.0 + np.arange(k.shape[0], dtype=np.float32) / 16.0)[:, None, None]).astype(np.float32)
+    scale = 1.0 / np.sqrt(hd)
+    U.log(f"prefill growing scores {case} seed={seed}")
+    out, _, _ = run_prefill(fmt, q, k, v, pos0, H, sink, win, scale)
+    ref = oracle.prefill(q, U.oracle_kv(fmt, k, hd), U.oracle_kv(fmt, v, hd), pos0, sink, win,
+                         scale, threads=U.ORACLE_THREADS)
+    U.compare_rows(out, ref, U.TOL_Q4 if fmt else U.TOL_F32, f"prefill growth {case}")
+
+
 def test_prefill_repeat_is_bitwise_identical():
     q, k, v = workloads.custom_prefill(77, 180, 20, 16, 2, 256)
     U.log("prefill determinism, 2 runs")
