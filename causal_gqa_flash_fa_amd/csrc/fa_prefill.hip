@@ -31,7 +31,7 @@
 //     output directly.
 //   * K/V tiles are double-buffered in LDS with one barrier per tile: fp32
 //     rows go straight from global memory into the next buffer
-//     (global_load_lds_dwordx4, one row per wave instruction, so no staging
+//     (buffer_load_dwordx4 ... lds, one row per wave instruction, so no staging
 //     registers), Q4_0 blocks are staged in registers and decoded into the
 //     next buffer after the current tile's matrix work.
 //   * Lazy rescale: a row's reference max only moves when a tile's max
@@ -40,6 +40,8 @@
 //     runs a few times per row instead of on most tiles; the final acc / l
 //     is unchanged up to rounding because acc and l share the reference.
 //   * Tiles inside every row's key set skip the mask.
+#include <type_traits>
+
 #include "fa_device.hpp"
 #include "fa_internal.hpp"
 
@@ -69,11 +71,21 @@ struct PrefillShape {
 // Reference-max slack of the lazy rescale (log2 units): p <= 2^kTau.
 constexpr float kTau = 8.0f;
 
-// 16-byte global -> LDS copy: lane i writes lds_row[4i .. 4i+3] (the LDS
-// base is wave-uniform; inactive lanes write nothing).
-__device__ __forceinline__ void dma16(const float *g, float *lds_row) {
-    __builtin_amdgcn_global_load_lds((const void *)g,
-                                     (__attribute__((address_space(3))) void *)lds_row, 16, 0, 0);
+// Raw buffer descriptor over `bytes` bytes at `base` (dword 3: 32-bit data
+// format, as for plain dword loads). Loads past `bytes` return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void *base, unsigned bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
+}
+
+// 16-byte buffer -> LDS copy (buffer_load_dwordx4 ... lds): lane i writes
+// lds_row[4i .. 4i+3] from byte offset voff of the buffer; the LDS base is
+// wave-uniform and inactive lanes write nothing. The buffer form (rather
+// than the global one) matters for the compiler: its wait-count model
+// treats a pending global (flat-encoded) LDS load as touching both memory
+// paths and then waits for every outstanding LDS read before each use.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, unsigned voff, float *lds_row) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)lds_row,
+                                             16, voff, 0, 0, 0);
 }
 
 // acc *= c in place in the accumulation registers, one element at a time
@@ -286,13 +298,18 @@ void prefill_kernel(PrefillArgs a) {
             constexpr int RPW = BK / Sh::W;       // rows per wave per tensor
             float *kd = lds + buf * Sh::BUF;
             float *vd = kd + BK * KS;
+            // descriptors over the rows of this tile that exist (j0 .. q1)
+            const int nrows = min(q1 + 1 - j0, BK);
+            const size_t tile0 = (size_t)j0 * RB;
+            const __amdgpu_buffer_rsrc_t rk = raw_rsrc(kbase + tile0, (unsigned)(nrows * RB));
+            const __amdgpu_buffer_rsrc_t rv = raw_rsrc(vbase + tile0, (unsigned)(nrows * RB));
             if (lane < LPR) {
 #pragma unroll
                 for (int i = 0; i < RPW; i++) {
                     const int row = w * RPW + i;
-                    const size_t off = (size_t)min(j0 + row, q1) * HD + 4 * lane;
-                    dma16((const float *)kbase + off, kd + row * KS);
-                    dma16((const float *)vbase + off, vd + row * KS);
+                    const unsigned voff = (unsigned)(min(row, nrows - 1) * RB + 16 * lane);
+                    dma16(rk, voff, kd + row * KS);
+                    dma16(rv, voff, vd + row * KS);
                 }
             }
         } else {
@@ -349,13 +366,20 @@ void prefill_kernel(PrefillArgs a) {
         const float *Ks = lds + buf * Sh::BUF;
         const float *Vs = Ks + BK * KS;
         // S^T = K Q^T: lane holds row r32, keys 8*(r/4) + 4*hlf + r%4
+        // LDS reads run one step ahead of the MFMAs that consume them; the
+        // scheduling fences keep the compiler from sinking them back.
         f32x16 s = f32x16{};
         const float *krow = Ks + r32 * KS + hlf * HH;
+        f32x4 kc = *(const f32x4 *)krow;
 #pragma unroll
         for (int i = 0; i < HH / 4; i++) {
-            const f32x4 kv = *(const f32x4 *)(krow + 4 * i);
+            f32x4 kn = kc;
+            if (i + 1 < HH / 4) kn = *(const f32x4 *)(krow + 4 * (i + 1));
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int t = 0; t < 4; t++) s = mfma32(kv[t], qr[4 * i + t], s);
+            for (int t = 0; t < 4; t++) s = mfma32(kc[t], qr[4 * i + t], s);
+            __builtin_amdgcn_sched_barrier(0);
+            kc = kn;
         }
         // every key of the tile is in the key set of every row of the wave
         const bool full = jc + BK - 1 <= pw0 &&
@@ -398,22 +422,25 @@ void prefill_kernel(PrefillArgs a) {
         l_run += psum;
 
         // O^T += V^T P^T: contraction step kk covers keys 8*(kk/4) + 4*hlf + kk%4
-#pragma unroll
-        for (int kk = 0; kk < 16; kk++) {
+        // (reads one step ahead, as above)
+        constexpr int NG = NT / GS;
+        using VVec = typename std::conditional<GS == 4, f32x4, f32x2>::type;
+        auto vread = [&](int step) {
+            const int kk = step / NG, ng = step % NG;
             const int key = 8 * (kk >> 2) + 4 * hlf + (kk & 3);
-            const float *vrow = Vs + key * KS + GS * r32;
+            return *(const VVec *)(Vs + key * KS + GS * r32 + ng * 32 * GS);
+        };
+        VVec vc = vread(0);
 #pragma unroll
-            for (int ng = 0; ng < NT / GS; ng++) {
-                if constexpr (GS == 4) {
-                    const f32x4 vv = *(const f32x4 *)(vrow + ng * 32 * GS);
+        for (int step = 0; step < 16 * NG; step++) {
+            VVec vn = vc;
+            if (step + 1 < 16 * NG) vn = vread(step + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            const int kk = step / NG, ng = step % NG;
 #pragma unroll
-                    for (int u = 0; u < 4; u++) O[ng * 4 + u] = mfma32(vv[u], s[kk], O[ng * 4 + u]);
-                } else {
-                    const f32x2 vv = *(const f32x2 *)(vrow + ng * 32 * GS);
-#pragma unroll
-                    for (int u = 0; u < 2; u++) O[ng * 2 + u] = mfma32(vv[u], s[kk], O[ng * 2 + u]);
-                }
-            }
+            for (int u = 0; u < GS; u++) O[ng * GS + u] = mfma32(vc[u], s[kk], O[ng * GS + u]);
+            __builtin_amdgcn_sched_barrier(0);
+            vc = vn;
         }
     };
 
@@ -506,30 +533,40 @@ void prefill_kernel(PrefillArgs a) {
 
 // Merges the pieces of segments cut between work-groups:
 // out = sum_p exp2(m_p - M) acc_p / sum_p exp2(m_p - M) l_p, ascending p.
-// One work-group per (row, segment), one thread per output dim.
+// One work-group per (segment, chunk of kCombineRows rows); whole segments
+// return at once. Each thread owns 4 consecutive output dims of one row.
+constexpr int kCombineRows = 16;
+
 template <int HD, int G>
-__global__ __launch_bounds__(HD) void prefill_combine_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(256) void prefill_combine_kernel(PrefillArgs a) {
     constexpr int ROWS = kPrefillWaves * kPrefillRowsPerWave;
     constexpr int BQ = ROWS / G;
-    const int row = blockIdx.x;
-    const int seg = blockIdx.y;
+    constexpr int TPR = HD / 4;                    // threads per row
+    constexpr int RPP = 256 / TPR;                 // rows per pass
+    const int seg = blockIdx.x;
     const int np = a.seg_table[2 * seg + 1];
     if (np <= 1) return;
-    const int qb = seg % a.n_qblocks, kvh = seg / a.n_qblocks;
-    const int p = a.pos0 + qb * BQ + row / G;
-    if (p > a.pos0 + a.n - 1) return;
     const int P = a.seg_table[2 * seg];
-    const int dd = threadIdx.x;
-    float M = -INFINITY;
-    for (int k = 0; k < np; k++) M = fmaxf(M, a.ws_m[(size_t)(P + k) * ROWS + row]);
-    float o = 0.0f, L = 0.0f;
-    for (int k = 0; k < np; k++) {
-        const size_t pr = (size_t)(P + k) * ROWS + row;
-        const float wgt = fast_exp2(a.ws_m[pr] - M);
-        L += a.ws_l[pr] * wgt;
-        o += a.ws_acc[pr * HD + dd] * wgt;
+    const int qb = seg % a.n_qblocks, kvh = seg / a.n_qblocks;
+    const int c4 = threadIdx.x % TPR;
+#pragma unroll 1
+    for (int rr = threadIdx.x / TPR; rr < kCombineRows; rr += RPP) {
+        const int row = blockIdx.y * kCombineRows + rr;
+        const int p = a.pos0 + qb * BQ + row / G;
+        if (p > a.pos0 + a.n - 1) continue;
+        float M = -INFINITY;
+        for (int k = 0; k < np; k++) M = fmaxf(M, a.ws_m[(size_t)(P + k) * ROWS + row]);
+        f32x4 o = {};
+        float L = 0.0f;
+        for (int k = 0; k < np; k++) {
+            const size_t pr = (size_t)(P + k) * ROWS + row;
+            const float wgt = fast_exp2(a.ws_m[pr] - M);
+            L += a.ws_l[pr] * wgt;
+            o += *(const f32x4 *)(a.ws_acc + pr * HD + 4 * c4) * wgt;
+        }
+        *(f32x4 *)(a.out + ((size_t)(p - a.pos0) * a.n_head + kvh * G + row % G) * HD + 4 * c4) =
+            o * (1.0f / L);
     }
-    a.out[((size_t)(p - a.pos0) * a.n_head + kvh * G + row % G) * HD + dd] = o / L;
 }
 
 template <int HD, int G, int FMT>
@@ -547,8 +584,8 @@ hipError_t launch_one(const PrefillArgs &a, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((prefill_combine_kernel<HD, G>),
-                       dim3(kPrefillWaves * kPrefillRowsPerWave, a.n_qblocks * a.n_kv), dim3(HD), 0,
-                       s, a);
+                       dim3(a.n_qblocks * a.n_kv, kPrefillWaves * kPrefillRowsPerWave / kCombineRows),
+                       dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
