@@ -135,6 +135,18 @@ __device__ __forceinline__ SegTiles seg_tiles(int q0, int q1, int sink, int win,
     return t;
 }
 
+constexpr int kXcds = 8;   // XCDs of an MI355X; block b runs on XCD b % 8
+
+// Segment s of the schedule is query block seg_qblock(s) of kv head
+// s / n_qblocks. Within a head the causal segments alternate long and short
+// (last block, first block, second to last, second, ...), so that a
+// contiguous run of tiles spans few segments and no work-group collects a
+// long string of short segments with their fixed per-segment costs.
+__device__ __forceinline__ int seg_qblock(int s, int n_qblocks) {
+    const int i = s % n_qblocks;
+    return (i & 1) ? (i >> 1) : n_qblocks - 1 - (i >> 1);
+}
+
 // Block-wide exclusive scan of one int per thread (256 threads); also
 // returns the total. `scratch` holds 4 ints.
 __device__ __forceinline__ int block_excl_scan(int x, int tid, int *scratch, int *total) {
@@ -175,12 +187,16 @@ void prefill_kernel(PrefillArgs a) {
     const int w = tid >> 6;
     const int hlf = lane >> 5;        // which half of the contraction / key sub-block
     const int r32 = lane & 31;        // this lane's query row within the wave
-    const int wg = blockIdx.x;
     const int NWG = gridDim.x;
+    // Work-groups are dealt to the 8 XCDs round-robin (block b on XCD b % 8);
+    // give each XCD a contiguous stretch of runs so that its L2 holds the K/V
+    // rows of few kv heads.
+    const int wg = NWG % kXcds == 0 ? (blockIdx.x % kXcds) * (NWG / kXcds) + blockIdx.x / kXcds
+                                    : blockIdx.x;
     const int nsegs = a.n_kv * a.n_qblocks;
 
     auto seg_of = [&](int s, int *q0, int *q1) {
-        const int qb = s % a.n_qblocks;
+        const int qb = seg_qblock(s, a.n_qblocks);
         *q0 = a.pos0 + qb * Sh::BQ;
         *q1 = min(*q0 + Sh::BQ - 1, a.pos0 + a.n - 1);
     };
@@ -259,7 +275,6 @@ void prefill_kernel(PrefillArgs a) {
     const bool row_live = p_row <= q1;
     const int pw0 = q0 + w * Sh::PW;
     const int pw1 = min(pw0 + Sh::PW - 1, q1);
-    const bool wave_live = pw0 <= q1;
 
     const uint8_t *kbase = (const uint8_t *)a.k + (size_t)kvh * a.max_seq * RB;
     const uint8_t *vbase = (const uint8_t *)a.v + (size_t)kvh * a.max_seq * RB;
@@ -460,9 +475,10 @@ void prefill_kernel(PrefillArgs a) {
         ti++;
         const bool more = ti < t_hi;
         if (more) issue_tile(st.tile(ti) * BK, buf ^ 1);
-        const bool wave_do = wave_live && jc <= pw1 &&
-                             (a.win <= 0 || jc < a.sink || jc + BK - 1 >= pw0 - a.win + 1);
-        if (wave_do) compute_tile(jc, buf);
+        // Every wave computes every tile: for a wave whose rows need none of
+        // its keys the tile is fully masked (p = 0, nothing changes). A branch
+        // here would make the compiler carry O through VGPR copies.
+        compute_tile(jc, buf);
         if (more) store_tile(buf ^ 1);
         buf ^= 1;
     }
@@ -547,7 +563,7 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(PrefillArgs a) {
     const int np = a.seg_table[2 * seg + 1];
     if (np <= 1) return;
     const int P = a.seg_table[2 * seg];
-    const int qb = seg % a.n_qblocks, kvh = seg / a.n_qblocks;
+    const int qb = seg_qblock(seg, a.n_qblocks), kvh = seg / a.n_qblocks;
     const int c4 = threadIdx.x % TPR;
 #pragma unroll 1
     for (int rr = threadIdx.x / TPR; rr < kCombineRows; rr += RPP) {
