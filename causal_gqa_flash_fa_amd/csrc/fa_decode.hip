@@ -281,45 +281,54 @@ void decode_partial_kernel(DecodeArgs a) {
                 wave_lds_sync();
             }
         } else {
-            // ---------------- Q4_0 tiles: prefetch, LDS staging, fused dequant
-            chunk_t pk[9], pv[9];
-            auto fetch = [&](chunk_t (&dst)[9], const uint8_t *base, int j) {
-                const int nrows = min(BKD, k_hi - j);
-                const uint8_t *t = base + (size_t)j * RB;
+            // ---------------- Q4_0 tiles
+            // K: lane = key; each lane loads its key's raw row into
+            // registers, requested right after the previous tile's QK so it
+            // flies during that tile's softmax and PV. V: the raw tile goes
+            // straight into the wave's LDS buffer by DMA, requested at the
+            // start of the tile (after the K rows have landed) so it flies
+            // during QK and softmax. The descriptor covers exactly the rows
+            // that exist: the buffer range check (per dword) returns zeros
+            // past them, so rows past the end of a partial tile arrive as
+            // all-zero blocks (scale 0) and masked keys (p = 0) add exact
+            // zeros. The compiler does not count LDS DMA in its own
+            // vmcnt bookkeeping, hence the explicit waits and this order: no
+            // compiler-inserted wait for K ever sits behind a pending DMA.
+            constexpr int NI = (Sh::TILE_BYTES + 1023) / 1024;   // V DMA instructions per tile
+            chunk_t kr[9];
+            auto fetch_k = [&](int j) {
+                const chunk_t *src = (const chunk_t *)(kb + (size_t)min(j + lane, k_hi - 1) * RB);
 #pragma unroll
-                for (int i = 0; i < 9; i++) {
-                    const int c = lane + 64 * i;
-                    dst[i] = c / 9 < nrows ? *(const chunk_t *)(t + c * CB) : chunk_t{};
+                for (int i = 0; i < 9; i++) kr[i] = src[i];
+            };
+            auto dma_v = [&](int j) {
+                const unsigned bytes = (unsigned)(min(BKD, k_hi - j) * RB);
+                const __amdgpu_buffer_rsrc_t rs = raw_rsrc(vb + (size_t)j * RB, bytes);
+#pragma unroll
+                for (int c = 0; c < NI; c++) {
+                    const unsigned o = (unsigned)(1024 * c + 16 * lane);
+                    if (o < (unsigned)Sh::TILE_BYTES) dma16(rs, o, Rw + 1024 * c);
                 }
             };
             int j = next_visited(k_lo);
-            if (j < k_hi) {
-                fetch(pk, kb, j);
-                fetch(pv, vb, j);
-            }
+            if (j < k_hi) fetch_k(j);
             while (j < k_hi) {
                 const int tj = j;
                 vis++;
-#pragma unroll
-                for (int i = 0; i < 9; i++) *(chunk_t *)(Rw + (lane + 64 * i) * CB) = pk[i];
-                wave_lds_sync();
+                wait_vmem_le<0>();                    // this tile's K rows; nothing else in flight
+                dma_v(tj);                            // Rw is free: the last PV ended with a sync
                 uint32_t rw[RB / 4];
 #pragma unroll
                 for (int i = 0; i < 9; i++) {
-                    const chunk_t v = *(const chunk_t *)(Rw + lane * RB + i * CB);
                     if constexpr (CB == 16) {
-                        rw[4 * i] = v[0]; rw[4 * i + 1] = v[1]; rw[4 * i + 2] = v[2]; rw[4 * i + 3] = v[3];
+                        rw[4 * i] = kr[i][0]; rw[4 * i + 1] = kr[i][1];
+                        rw[4 * i + 2] = kr[i][2]; rw[4 * i + 3] = kr[i][3];
                     } else if constexpr (CB == 8) {
-                        rw[2 * i] = v[0]; rw[2 * i + 1] = v[1];
+                        rw[2 * i] = kr[i][0]; rw[2 * i + 1] = kr[i][1];
                     } else {
-                        rw[i] = v;
+                        rw[i] = kr[i];
                     }
                 }
-                wave_lds_sync();
-#pragma unroll
-                for (int i = 0; i < 9; i++) *(chunk_t *)(Rw + (lane + 64 * i) * CB) = pv[i];
-                j = next_visited(tj + BKD);
-                if (j < k_hi) fetch(pk, kb, j);       // next K flies during this QK
 
                 // QK: 2 accumulator chains per head group
                 const int key = tj + lane;
@@ -358,11 +367,20 @@ void decode_partial_kernel(DecodeArgs a) {
                         }
                     }
                 }
+                j = next_visited(tj + BKD);
+                const bool more = j < k_hi;
+                if (more) fetch_k(j);                 // next K rows fly during softmax and PV
                 f32x4 sacc[NHG];
 #pragma unroll
                 for (int hg = 0; hg < NHG; hg++) sacc[hg] = sacc2[hg][0] + sacc2[hg][1];
                 softmax_tile(sacc, kval, (lane & 1) * 32 + (lane >> 1));   // even keys, then odd
-                if (j < k_hi) fetch(pv, vb, j);       // next V flies during this PV
+
+                // this tile's V bytes were requested before the next tile's K
+                // rows; those take at least ceil(row bytes / 16) load
+                // instructions however the compiler merges them, so at most
+                // that many outstanding operations means the V tile is in
+                if (more) wait_vmem_le<(RB + 15) / 16>();
+                else wait_vmem_le<0>();
                 wave_lds_sync();
 
                 // PV: lanes 0-31 even keys, lanes 32-63 odd keys
@@ -413,7 +431,7 @@ void decode_partial_kernel(DecodeArgs a) {
                                 O[c][hg] = mfma4(pa[hg][u], vv[c], O[c][hg]);
                     }
                 }
-                wave_lds_sync();
+                wave_lds_sync();                      // Rw and Pw free again
             }
 #pragma unroll
             for (int c = 0; c < OD; c++)

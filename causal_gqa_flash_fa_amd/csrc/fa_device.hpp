@@ -30,6 +30,32 @@ __device__ __forceinline__ float half_bits_to_float(uint32_t bits) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)(bits & 0xffffu));
 }
 
+// Raw buffer descriptor over `bytes` bytes at `base` (dword 3: 32-bit data
+// format, as for plain dword loads). Loads past `bytes` return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void *base, unsigned bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
+}
+
+// 16-byte buffer -> LDS copy (buffer_load_dwordx4 ... lds): lane i writes
+// lds[16i .. 16i+15] from byte offset voff of the buffer; the LDS base is
+// wave-uniform and inactive lanes write nothing. Completion is counted by
+// vmcnt. The buffer form (rather than the global one) matters for the
+// compiler: its wait-count model treats a pending global (flat-encoded) LDS
+// load as touching both memory paths and then waits for every outstanding
+// LDS read before each use.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, unsigned voff, void *lds) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)lds,
+                                             16, voff, 0, 0, 0);
+}
+
+// Wait until at most `n` of this wave's vector-memory operations (loads,
+// LDS DMA, stores) are outstanding; they complete in issue order.
+template <int n>
+__device__ __forceinline__ void wait_vmem_le() {
+    static_assert(n >= 0 && n < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | 0x0F70);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) {
     return __builtin_amdgcn_exp2f(x);   // v_exp_f32; exp2(-inf) = 0
 }

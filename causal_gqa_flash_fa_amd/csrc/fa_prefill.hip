@@ -71,23 +71,6 @@ struct PrefillShape {
 // Reference-max slack of the lazy rescale (log2 units): p <= 2^kTau.
 constexpr float kTau = 8.0f;
 
-// Raw buffer descriptor over `bytes` bytes at `base` (dword 3: 32-bit data
-// format, as for plain dword loads). Loads past `bytes` return zero.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void *base, unsigned bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
-}
-
-// 16-byte buffer -> LDS copy (buffer_load_dwordx4 ... lds): lane i writes
-// lds_row[4i .. 4i+3] from byte offset voff of the buffer; the LDS base is
-// wave-uniform and inactive lanes write nothing. The buffer form (rather
-// than the global one) matters for the compiler: its wait-count model
-// treats a pending global (flat-encoded) LDS load as touching both memory
-// paths and then waits for every outstanding LDS read before each use.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, unsigned voff, float *lds_row) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)lds_row,
-                                             16, voff, 0, 0, 0);
-}
-
 // acc *= c in place in the accumulation registers, one element at a time
 // through a single temporary VGPR: keeps the O accumulators in AGPRs (a
 // plain multiply makes the compiler carry a VGPR copy of all of O).
@@ -105,7 +88,7 @@ __device__ __forceinline__ void scale_acc(f32x16 &acc, float c) {
 }
 
 // Wait for all of this wave's vector-memory operations (incl. LDS DMA).
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+__device__ __forceinline__ void wait_vmem() { wait_vmem_le<0>(); }
 
 // Visited key tiles of the query block [q0, q1] ([FA] fc_attn_tile_in_window
 // over the union of the block's key sets): the causal walk has q1/BK + 1
