@@ -91,15 +91,49 @@ __device__ __forceinline__ float byte_f(uint32_t w, int t) {
     return (float)((w >> (8 * t)) & 0xffu);   // v_cvt_f32_ubyte{t}
 }
 
-// Two nibbles of w (bits sh..sh+3 and sh+16..sh+19) as binary16 values 1024+c.
-__device__ __forceinline__ uint32_t nib_pair(uint32_t w, int sh) {
-    return ((w >> sh) & 0x000f000fu) | 0x64006400u;
-}
 __device__ __forceinline__ float lo_h(uint32_t r) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)(r & 0xffffu));
 }
 __device__ __forceinline__ float hi_h(uint32_t r) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)(r >> 16));
+}
+
+// The 8 elements held by one code word w (bytes b0..b3): element e = low
+// nibble of byte e, element 16 + e = high nibble of byte e (e = 0..3, relative
+// to the word). A nibble masked into a binary16 with exponent bits 0x6400
+// gives 1024 + c (low nibble, bits 0-3) or 1024 + 16 c (high nibble, bits
+// 4-7, still inside the 10-bit mantissa), so one and-or per two elements
+// builds fma_mix operands: (1024 + c) d - 1032 d and (1024 + 16 c) (d / 16)
+// - 72 d are both exactly (c - 8) d. `k` holds the masks and exponent bits in
+// registers so the and-or is a single three-operand instruction.
+struct NibConsts {
+    uint32_t lo, hi, ex;
+};
+__device__ __forceinline__ NibConsts nib_consts() {
+    NibConsts k;
+    // opaque to the compiler: kept in VGPRs instead of being folded as literals
+    asm volatile("v_mov_b32 %0, 0x000f000f" : "=v"(k.lo));
+    asm volatile("v_mov_b32 %0, 0x00f000f0" : "=v"(k.hi));
+    asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(k.ex));
+    return k;
+}
+// out[0..3] = elements e = 0..3 (low nibbles), out[4..7] = elements 16 + e.
+__device__ __forceinline__ void dequant_word(uint32_t w, float d, const NibConsts &k, float *out) {
+    const float d16 = d * 0.0625f;
+    const float blo = -1032.0f * d, bhi = -72.0f * d;
+    const uint32_t w8 = w >> 8;
+    const uint32_t a = (w & k.lo) | k.ex;     // bytes 0, 2 low nibbles
+    const uint32_t b = (w8 & k.lo) | k.ex;    // bytes 1, 3 low nibbles
+    const uint32_t c = (w & k.hi) | k.ex;     // bytes 0, 2 high nibbles (x16)
+    const uint32_t e = (w8 & k.hi) | k.ex;    // bytes 1, 3 high nibbles (x16)
+    out[0] = fmaf(lo_h(a), d, blo);
+    out[1] = fmaf(lo_h(b), d, blo);
+    out[2] = fmaf(hi_h(a), d, blo);
+    out[3] = fmaf(hi_h(b), d, blo);
+    out[4] = fmaf(lo_h(c), d16, bhi);
+    out[5] = fmaf(lo_h(e), d16, bhi);
+    out[6] = fmaf(hi_h(c), d16, bhi);
+    out[7] = fmaf(hi_h(e), d16, bhi);
 }
 
 __device__ __forceinline__ int wave_sum_i(int x) {
@@ -310,6 +344,7 @@ void decode_partial_kernel(DecodeArgs a) {
                     if (o < (unsigned)Sh::TILE_BYTES) dma16(rs, o, Rw + 1024 * c);
                 }
             };
+            const NibConsts nk = nib_consts();
             int j = next_visited(k_lo);
             if (j < k_hi) fetch_k(j);
             while (j < k_hi) {
@@ -330,40 +365,55 @@ void decode_partial_kernel(DecodeArgs a) {
                     }
                 }
 
-                // QK: 2 accumulator chains per head group
+                // QK: 2 accumulator chains per head group; step st covers
+                // code word q = st % 4 of block blk = st / 4. The q operands of
+                // the next step are read before this step's MFMAs (fenced so
+                // the scheduler keeps them there).
                 const int key = tj + lane;
                 const bool kval = key < k_hi && in_key_set(key, pos, a.sink, a.win);
                 f32x4 sacc2[NHG][2];
 #pragma unroll
                 for (int hg = 0; hg < NHG; hg++) sacc2[hg][0] = sacc2[hg][1] = f32x4{};
+                constexpr int NST = NB * 4;
+                auto qread = [&](int st, f32x4 (&qa)[NHG], f32x4 (&qh)[NHG]) {
+                    const int blk = st >> 2, q = st & 3;
 #pragma unroll
-                for (int blk = 0; blk < NB; blk++) {
+                    for (int hg = 0; hg < NHG; hg++) {
+                        const float *qb = qlane + hg * 4 * QS + blk * kQ4Block;
+                        qa[hg] = *(const f32x4 *)(qb + 4 * q);
+                        qh[hg] = *(const f32x4 *)(qb + 16 + 4 * q);
+                    }
+                };
+                f32x4 qa[NHG], qh[NHG];
+                qread(0, qa, qh);
+                float d = 0.0f;
+#pragma unroll
+                for (int st = 0; st < NST; st++) {
+                    const int blk = st >> 2, q = st & 3;
                     const int dw = blk * kQ4BlockBytes / 4;
                     const bool odd = (blk & 1) != 0;   // odd blocks start 2 bytes into a dword
-                    const uint32_t sbits = odd ? (rw[dw] >> 16) : (rw[dw] & 0xffffu);
-                    const float d = half_bits_to_float(sbits);
-                    const float bias = -1032.0f * d;  // (1024 + c) * d + bias == (c - 8) * d
+                    if (q == 0) d = half_bits_to_float(odd ? (rw[dw] >> 16) : (rw[dw] & 0xffffu));
+                    const uint32_t cw = odd ? rw[dw + 1 + q]
+                                            : __builtin_amdgcn_alignbyte(rw[dw + q + 1], rw[dw + q], 2);
+                    float kv[8];
+                    dequant_word(cw, d, nk, kv);       // elements blk*32 + 4q + t, blk*32 + 16 + 4q + t
+                    f32x4 na[NHG], nh[NHG];
+                    if (st + 1 < NST) qread(st + 1, na, nh);
+                    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                    for (int q = 0; q < 4; q++) {
-                        const uint32_t cw = odd ? rw[dw + 1 + q]
-                                                : __builtin_amdgcn_alignbyte(rw[dw + q + 1], rw[dw + q], 2);
-                        const uint32_t r0 = nib_pair(cw, 0), r1 = nib_pair(cw, 8);
-                        const uint32_t r2 = nib_pair(cw, 4), r3 = nib_pair(cw, 12);
-                        // elements blk*32 + 4q + t (low nibbles) and blk*32 + 16 + 4q + t (high)
-                        const float klo[4] = {fmaf(lo_h(r0), d, bias), fmaf(lo_h(r1), d, bias),
-                                              fmaf(hi_h(r0), d, bias), fmaf(hi_h(r1), d, bias)};
-                        const float khi[4] = {fmaf(lo_h(r2), d, bias), fmaf(lo_h(r3), d, bias),
-                                              fmaf(hi_h(r2), d, bias), fmaf(hi_h(r3), d, bias)};
+                    for (int hg = 0; hg < NHG; hg++) {
+#pragma unroll
+                        for (int t = 0; t < 4; t++) {
+                            sacc2[hg][t & 1] = mfma4(qa[hg][t], kv[t], sacc2[hg][t & 1]);
+                            sacc2[hg][t & 1] = mfma4(qh[hg][t], kv[4 + t], sacc2[hg][t & 1]);
+                        }
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (st + 1 < NST) {
 #pragma unroll
                         for (int hg = 0; hg < NHG; hg++) {
-                            const float *qb = qlane + hg * 4 * QS + blk * kQ4Block;
-                            const f32x4 qa = *(const f32x4 *)(qb + 4 * q);
-                            const f32x4 qh = *(const f32x4 *)(qb + 16 + 4 * q);
-#pragma unroll
-                            for (int t = 0; t < 4; t++) {
-                                sacc2[hg][t & 1] = mfma4(qa[t], klo[t], sacc2[hg][t & 1]);
-                                sacc2[hg][t & 1] = mfma4(qh[t], khi[t], sacc2[hg][t & 1]);
-                            }
+                            qa[hg] = na[hg];
+                            qh[hg] = nh[hg];
                         }
                     }
                 }
@@ -403,17 +453,7 @@ void decode_partial_kernel(DecodeArgs a) {
                         if constexpr (BPL == 4) {
                             const uint32_t cw = *(const uint16_t *)(vr + 2 + jb) |
                                                 ((uint32_t)*(const uint16_t *)(vr + 4 + jb) << 16);
-                            const float bias = -1032.0f * d;
-                            const uint32_t r0 = nib_pair(cw, 0), r1 = nib_pair(cw, 8);
-                            const uint32_t r2 = nib_pair(cw, 4), r3 = nib_pair(cw, 12);
-                            vv[0] = fmaf(lo_h(r0), d, bias);   // element jb
-                            vv[1] = fmaf(lo_h(r1), d, bias);   // jb + 1
-                            vv[2] = fmaf(hi_h(r0), d, bias);   // jb + 2
-                            vv[3] = fmaf(hi_h(r1), d, bias);   // jb + 3
-                            vv[4] = fmaf(lo_h(r2), d, bias);   // 16 + jb
-                            vv[5] = fmaf(lo_h(r3), d, bias);   // 16 + jb + 1
-                            vv[6] = fmaf(hi_h(r2), d, bias);   // 16 + jb + 2
-                            vv[7] = fmaf(hi_h(r3), d, bias);   // 16 + jb + 3
+                            dequant_word(cw, d, nk, vv);   // elements jb + t, 16 + jb + t
                         } else {
                             const uint32_t cw = BPL == 2 ? (uint32_t)*(const uint16_t *)(vr + 2 + jb)
                                                          : (uint32_t)vr[2 + jb];
