@@ -185,7 +185,7 @@ void decode_partial_kernel(DecodeArgs a) {
         const int s = base + lane;
         int sl;
         const int it = s < nsegs ? slot_items(a.pos[s / a.n_kv], a, &sl) : 0;
-        total += wave_sum_i(it);
+        total += __builtin_amdgcn_readfirstlane(wave_sum_i(it));
     }
     const long long lo = (long long)w * total / NW;
     const long long hi = (long long)(w + 1) * total / NW;
@@ -197,7 +197,7 @@ void decode_partial_kernel(DecodeArgs a) {
     // ---- per-segment fold of items [it_lo, it_hi) into one partial
     auto run_segment = [&](int seg, int it_lo, int it_hi, int pidx) {
         const int slot = seg / a.n_kv, kvh = seg % a.n_kv;
-        const int pos = a.pos[slot];
+        const int pos = __builtin_amdgcn_readfirstlane(a.pos[slot]);
         int split_len;
         slot_items(pos, a, &split_len);
         const int L = pos + 1;
@@ -341,7 +341,9 @@ void decode_partial_kernel(DecodeArgs a) {
 #pragma unroll
                 for (int c = 0; c < NI; c++) {
                     const unsigned o = (unsigned)(1024 * c + 16 * lane);
-                    if (o < (unsigned)Sh::TILE_BYTES) dma16(rs, o, Rw + 1024 * c);
+                    // only the last instruction can reach past the tile
+                    if (c < NI - 1 || Sh::TILE_BYTES % 1024 == 0 || o < (unsigned)Sh::TILE_BYTES)
+                        dma16(rs, o, Rw + 1024 * c);
                 }
             };
             const NibConsts nk = nib_consts();
@@ -527,13 +529,16 @@ void decode_partial_kernel(DecodeArgs a) {
         while (hit) {
             const int b = __builtin_ctzll(hit);
             hit &= hit - 1;
-            const int Fs = __shfl(F, b), its = __shfl(it, b), Ps = __shfl(P, b);
+            // lane b's values, as wave-uniform (scalar) values
+            const int Fs = __builtin_amdgcn_readfirstlane(__shfl(F, b));
+            const int its = __builtin_amdgcn_readfirstlane(__shfl(it, b));
+            const int Ps = __builtin_amdgcn_readfirstlane(__shfl(P, b));
             const int it_lo = (int)max(lo, (long long)Fs) - Fs;
             const int it_hi = (int)min(hi, (long long)Fs + its) - Fs;
             run_segment(base + b, it_lo, it_hi, Ps + (w - owner(Fs)));
         }
-        f_carry += __shfl(incl, 63);
-        p_carry += __shfl(inclw, 63);
+        f_carry += __builtin_amdgcn_readfirstlane(__shfl(incl, 63));
+        p_carry += __builtin_amdgcn_readfirstlane(__shfl(inclw, 63));
     }
 
     if (a.stats && lane == 0) {

@@ -167,7 +167,7 @@ void prefill_kernel(PrefillArgs a) {
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int w = tid >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index: uniform
     const int hlf = lane >> 5;        // which half of the contraction / key sub-block
     const int r32 = lane & 31;        // this lane's query row within the wave
     const int NWG = gridDim.x;
