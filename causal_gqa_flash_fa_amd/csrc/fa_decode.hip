@@ -421,18 +421,12 @@ void decode_partial_kernel(DecodeArgs a) {
                 }
                 j = next_visited(tj + BKD);
                 const bool more = j < k_hi;
-                if (more) fetch_k(j);                 // next K rows fly during softmax and PV
                 f32x4 sacc[NHG];
 #pragma unroll
                 for (int hg = 0; hg < NHG; hg++) sacc[hg] = sacc2[hg][0] + sacc2[hg][1];
                 softmax_tile(sacc, kval, (lane & 1) * 32 + (lane >> 1));   // even keys, then odd
 
-                // this tile's V bytes were requested before the next tile's K
-                // rows; those take at least ceil(row bytes / 16) load
-                // instructions however the compiler merges them, so at most
-                // that many outstanding operations means the V tile is in
-                if (more) wait_vmem_le<(RB + 15) / 16>();
-                else wait_vmem_le<0>();
+                wait_vmem_le<0>();                    // this tile's V bytes (nothing else in flight)
                 wave_lds_sync();
 
                 // PV: lanes 0-31 even keys, lanes 32-63 odd keys
@@ -440,8 +434,13 @@ void decode_partial_kernel(DecodeArgs a) {
                 const int ll = lane & 31;
                 const int bb = ll / Sh::LPB, jb = (ll % Sh::LPB) * BPL;
                 const float *plane = Pw + (lane & 3) * PS + hk * 32;
-#pragma unroll 1
+                // Fully unrolled: the compiler guards the first V read with a
+                // wait for all outstanding memory operations (it cannot tell
+                // the DMA is done), so the next tile's K rows are requested
+                // only after the first step, and fly during the rest of PV.
+#pragma unroll
                 for (int t4 = 0; t4 < 8; t4++) {
+                    if (t4 == 1 && more) fetch_k(j);
                     f32x4 pa[NHG];
 #pragma unroll
                     for (int hg = 0; hg < NHG; hg++)
