@@ -33,6 +33,43 @@ PEAK_FP32_MFMA_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 
 
+CSRC = os.path.join(ROOT, "causal_gqa_flash_fa_amd", "csrc")
+# Sources that define each measured launch: a change to any of them makes the
+# committed HBM counter figures stale.
+KERNEL_SOURCES = {
+    "prefill": ["fa_prefill.hip", "fa_device.hpp", "fa_internal.hpp", "fa_api.hip"],
+    "decode": ["fa_decode.hip", "fa_device.hpp", "fa_internal.hpp", "fa_api.hip"],
+}
+
+
+def kernel_source_digest(which: str) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[which]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read() + b"\0")
+    return h.hexdigest()
+
+
+def measured_traffic(which: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    summary (copy-calibrated), or None when the kernel sources have changed
+    since the counters were taken (or no summary exists)."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic__{workload}.md")
+    try:
+        text = open(path).read()
+    except OSError:
+        return None
+    rec = None
+    for line in text.splitlines():
+        line = line.strip()
+        if line.startswith("{") and "source_digest" in line:
+            rec = json.loads(line)
+    if rec is None or rec.get("source_digest") != kernel_source_digest(which):
+        return None
+    return rec
+
+
 def keyset_pairs(n: int, pos0: int, sink: int, win: int) -> int:
     """Sum over query positions p of |K(p)| (attended keys of one q head)."""
     p = np.arange(pos0, pos0 + n, dtype=np.int64)
@@ -145,6 +182,8 @@ def decode_leg(fa, torch, w, steps: int, warmup: int) -> dict:
         "frac_hbm_peak": gbs / PEAK_HBM_GBS, "tflops": flops / ms / 1e9,
         "fp32_compute_ceiling_gbs": compute_ceiling_gbs,
         "frac_of_min_ceiling": gbs / min(PEAK_HBM_GBS, compute_ceiling_gbs),
+        "traffic_bytes": (round(rec["traffic_bytes"]) if (rec := measured_traffic("decode", w.name))
+                          else None),
     }
 
 
@@ -235,6 +274,9 @@ def main() -> int:
         cpu = cpu_baseline(head)
 
     kern_tflops = main_leg["tflops_kernel"]
+    rec = measured_traffic("prefill", head.name)
+    traffic_bytes = round(rec["traffic_bytes"]) if rec else None
+    traffic_src = f"profiles/hbm_traffic__{head.name}.md" if rec else None
     line = {
         "metric": METRIC,
         "value": round(main_leg["tflops_step"], 3),
@@ -252,10 +294,12 @@ def main() -> int:
                    "n_head": head.n_head, "n_kv_head": head.n_kv_head,
                    "head_dim": head.head_dim, "kv": "f32", "attn_sink": head.attn_sink,
                    "attn_win": head.attn_win, "step": "fa_kv_append + fa_prefill"},
-        "roofline": {"bound": "mfma", "kernel": "prefill_kernel<256,8,f32>",
+        "roofline": {"bound": "mfma",
+                     "kernel": "fa_prefill: prefill_kernel<256,8,f32> + prefill_combine_kernel<256,8>",
                      "achieved": round(kern_tflops, 3), "peak": PEAK_FP32_MFMA_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(kern_tflops / PEAK_FP32_MFMA_TFLOPS, 4),
-                     "traffic": None,
+                     "traffic": traffic_bytes,
+                     "traffic_source": traffic_src,
                      "kernel_ms": round(main_leg["prefill_kernel_ms"], 5),
                      "flops_per_launch": main_leg["flops"]},
         "cpu_baseline": cpu,
