@@ -556,8 +556,12 @@ __global__ __launch_bounds__(HD) void decode_combine_kernel(DecodeArgs a) {
     const int P = a.seg_table[2 * seg], n = a.seg_table[2 * seg + 1];
     const int dd = threadIdx.x;
     float M = -INFINITY;
+#pragma unroll 8
     for (int r = 0; r < n; r++) M = fmaxf(M, a.ws_m[(size_t)(P + r) * G + g]);
+    // unrolled so that several partials' loads are in flight at once; the
+    // sums still run in ascending partial order
     float o = 0.0f, L = 0.0f;
+#pragma unroll 8
     for (int r = 0; r < n; r++) {
         const size_t pi = (size_t)(P + r) * G + g;
         const float wgt = fast_exp2(a.ws_m[pi] - M);
