@@ -119,6 +119,9 @@ __device__ __forceinline__ SegTiles seg_tiles(int q0, int q1, int sink, int win,
 }
 
 constexpr int kXcds = 8;   // XCDs of an MI355X; block b runs on XCD b % 8
+// Schedule units charged for starting a segment (about one tile's time,
+// measured: a run that starts a second segment takes ~7 us more at ~9 us per tile).
+constexpr int kSegUnits = 1;
 
 // Segment s of the schedule is query block seg_qblock(s) of kv head
 // s / n_qblocks. Within a head the causal segments alternate long and short
@@ -184,18 +187,24 @@ void prefill_kernel(PrefillArgs a) {
         *q1 = min(*q0 + Sh::BQ - 1, a.pos0 + a.n - 1);
     };
 
-    // ---- schedule: total tiles, this work-group's run, the piece table
+    // ---- schedule: total units, this work-group's run, the piece table.
+    // A segment with c visited tiles is kSegUnits + c units: the leading
+    // units stand for the fixed cost a run pays to start a segment (Q load,
+    // first-tile latency, output write), so runs that start more segments
+    // get fewer tiles. Pieces are defined by tile units only.
+    auto seg_units = [&](int s, int *cnt) {
+        int q0, q1;
+        seg_of(s, &q0, &q1);
+        *cnt = seg_tiles(q0, q1, a.sink, a.win, BK).count;
+        return *cnt > 0 ? *cnt + kSegUnits : 0;
+    };
     int total = 0;
     for (int base = 0; base < nsegs; base += 256) {
         const int s = base + tid;
         int cnt = 0;
-        if (s < nsegs) {
-            int q0, q1;
-            seg_of(s, &q0, &q1);
-            cnt = seg_tiles(q0, q1, a.sink, a.win, BK).count;
-        }
+        const int u = s < nsegs ? seg_units(s, &cnt) : 0;
         int chunk;
-        block_excl_scan(cnt, tid, scan_scratch, &chunk);
+        block_excl_scan(u, tid, scan_scratch, &chunk);
         total += chunk;
     }
     const long long lo = (long long)wg * total / NWG;
@@ -210,26 +219,23 @@ void prefill_kernel(PrefillArgs a) {
         for (int base = 0; base < nsegs; base += 256) {
             const int s = base + tid;
             int cnt = 0;
-            if (s < nsegs) {
-                int q0, q1;
-                seg_of(s, &q0, &q1);
-                cnt = seg_tiles(q0, q1, a.sink, a.win, BK).count;
-            }
+            const int u = s < nsegs ? seg_units(s, &cnt) : 0;
             int chunk, chunk_p;
-            const int F = f_carry + block_excl_scan(cnt, tid, scan_scratch, &chunk);
-            const int np = cnt > 0 ? owner(F + cnt - 1) - owner(F) + 1 : 0;
+            const int F = f_carry + block_excl_scan(u, tid, scan_scratch, &chunk);
+            const int T0 = F + kSegUnits;      // first tile unit
+            const int np = cnt > 0 ? owner(T0 + cnt - 1) - owner(T0) + 1 : 0;
             const int pc = np > 1 ? np : 0;
             const int P = p_carry + block_excl_scan(pc, tid, scan_scratch, &chunk_p);
             if (wg == 0 && s < nsegs) {
                 a.seg_table[2 * s] = P;
                 a.seg_table[2 * s + 1] = np;
             }
-            if (cnt > 0 && F <= lo && lo < F + cnt) {
+            if (u > 0 && F <= lo && lo < F + u) {
                 run_info[0] = s;
                 run_info[2] = F;
                 run_info[3] = P;
             }
-            if (cnt > 0 && F < hi && hi <= F + cnt) {
+            if (u > 0 && F < hi && hi <= F + u) {
                 run_info[1] = s;
                 run_info[4] = F;
                 run_info[5] = P;
@@ -504,14 +510,14 @@ void prefill_kernel(PrefillArgs a) {
     if (s_first >= 0 && lo < hi) {
         int F = run_info[2];
         for (int seg = s_first; seg <= s_last; seg++) {
-            int q0, q1;
-            seg_of(seg, &q0, &q1);
-            const int cnt = seg_tiles(q0, q1, a.sink, a.win, BK).count;
-            if (cnt > 0) {
-                const int t_lo = (int)max(lo - F, 0LL);
-                const int t_hi = (int)min(hi - F, (long long)cnt);
-                const int f_owner = owner(F);
-                const bool whole = owner(F + cnt - 1) == f_owner;
+            int cnt;
+            const int u = seg_units(seg, &cnt);
+            const int T0 = F + kSegUnits;
+            const int t_lo = (int)max(lo - T0, 0LL);
+            const int t_hi = (int)min(hi - T0, (long long)cnt);
+            if (t_lo < t_hi) {     // this run owns tiles of the segment
+                const int f_owner = owner(T0);
+                const bool whole = owner(T0 + cnt - 1) == f_owner;
                 int piece = 0;
                 if (!whole) {
                     // piece table offset of a cut segment: only the run's
@@ -519,9 +525,9 @@ void prefill_kernel(PrefillArgs a) {
                     const int P = seg == s_first ? run_info[3] : run_info[5];
                     piece = P + (wg - f_owner);
                 }
-                run_segment(seg, t_lo, t_hi, whole, piece, F >= lo);
+                run_segment(seg, t_lo, t_hi, whole, piece, f_owner == wg);
             }
-            F += cnt;
+            F += u;
         }
     }
     if (a.stats && tid == 0) {
