@@ -117,10 +117,17 @@ __device__ __forceinline__ NibConsts nib_consts() {
     asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(k.ex));
     return k;
 }
+// The per-block constants of dequant_word.
+struct BlockScale {
+    float d, d16, blo, bhi;
+};
+__device__ __forceinline__ BlockScale block_scale(float d) {
+    return BlockScale{d, d * 0.0625f, -1032.0f * d, -72.0f * d};
+}
 // out[0..3] = elements e = 0..3 (low nibbles), out[4..7] = elements 16 + e.
-__device__ __forceinline__ void dequant_word(uint32_t w, float d, const NibConsts &k, float *out) {
-    const float d16 = d * 0.0625f;
-    const float blo = -1032.0f * d, bhi = -72.0f * d;
+__device__ __forceinline__ void dequant_word(uint32_t w, const BlockScale &sc, const NibConsts &k,
+                                             float *out) {
+    const float d = sc.d, d16 = sc.d16, blo = sc.blo, bhi = sc.bhi;
     const uint32_t w8 = w >> 8;
     const uint32_t a = (w & k.lo) | k.ex;     // bytes 0, 2 low nibbles
     const uint32_t b = (w8 & k.lo) | k.ex;    // bytes 1, 3 low nibbles
@@ -388,17 +395,18 @@ void decode_partial_kernel(DecodeArgs a) {
                 };
                 f32x4 qa[NHG], qh[NHG];
                 qread(0, qa, qh);
-                float d = 0.0f;
+                BlockScale sc{};
 #pragma unroll
                 for (int st = 0; st < NST; st++) {
                     const int blk = st >> 2, q = st & 3;
                     const int dw = blk * kQ4BlockBytes / 4;
                     const bool odd = (blk & 1) != 0;   // odd blocks start 2 bytes into a dword
-                    if (q == 0) d = half_bits_to_float(odd ? (rw[dw] >> 16) : (rw[dw] & 0xffffu));
+                    if (q == 0)
+                        sc = block_scale(half_bits_to_float(odd ? (rw[dw] >> 16) : (rw[dw] & 0xffffu)));
                     const uint32_t cw = odd ? rw[dw + 1 + q]
                                             : __builtin_amdgcn_alignbyte(rw[dw + q + 1], rw[dw + q], 2);
                     float kv[8];
-                    dequant_word(cw, d, nk, kv);       // elements blk*32 + 4q + t, blk*32 + 16 + 4q + t
+                    dequant_word(cw, sc, nk, kv);      // elements blk*32 + 4q + t, blk*32 + 16 + 4q + t
                     f32x4 na[NHG], nh[NHG];
                     if (st + 1 < NST) qread(st + 1, na, nh);
                     __builtin_amdgcn_sched_barrier(0);
@@ -454,7 +462,7 @@ void decode_partial_kernel(DecodeArgs a) {
                         if constexpr (BPL == 4) {
                             const uint32_t cw = *(const uint16_t *)(vr + 2 + jb) |
                                                 ((uint32_t)*(const uint16_t *)(vr + 4 + jb) << 16);
-                            dequant_word(cw, d, nk, vv);   // elements jb + t, 16 + jb + t
+                            dequant_word(cw, block_scale(d), nk, vv);   // elements jb + t, 16 + jb + t
                         } else {
                             const uint32_t cw = BPL == 2 ? (uint32_t)*(const uint16_t *)(vr + 2 + jb)
                                                          : (uint32_t)vr[2 + jb];
