@@ -119,9 +119,12 @@ __device__ __forceinline__ SegTiles seg_tiles(int q0, int q1, int sink, int win,
 }
 
 constexpr int kXcds = 8;   // XCDs of an MI355X; block b runs on XCD b % 8
-// Schedule units charged for starting a segment (about one tile's time,
-// measured: a run that starts a second segment takes ~7 us more at ~9 us per tile).
-constexpr int kSegUnits = 1;
+// Schedule units: a tile is kTileUnits units and starting a segment costs
+// kSegUnits more (measured: switching segments costs ~11 us, about 1.2 times
+// a ~9 us tile, mostly the output stores and the next Q load hitting HBM at
+// once). A tile belongs to the run that holds its first unit.
+constexpr int kTileUnits = 4;
+constexpr int kSegUnits = 5;
 
 // Segment s of the schedule is query block seg_qblock(s) of kv head
 // s / n_qblocks. Within a head the causal segments alternate long and short
@@ -188,15 +191,18 @@ void prefill_kernel(PrefillArgs a) {
     };
 
     // ---- schedule: total units, this work-group's run, the piece table.
-    // A segment with c visited tiles is kSegUnits + c units: the leading
-    // units stand for the fixed cost a run pays to start a segment (Q load,
-    // first-tile latency, output write), so runs that start more segments
-    // get fewer tiles. Pieces are defined by tile units only.
+    // A segment with c visited tiles is kSegUnits + c * kTileUnits units:
+    // the leading units stand for the fixed cost a run pays to start a
+    // segment (Q load, first-tile latency, output write), so runs that start
+    // more segments get fewer tiles. Tile t of a segment whose tile units
+    // start at T0 belongs to owner(T0 + t * kTileUnits). Every run spans at
+    // least kTileUnits units (the host keeps work-groups <= tiles), so every
+    // run between a segment's first and last owner owns one of its tiles.
     auto seg_units = [&](int s, int *cnt) {
         int q0, q1;
         seg_of(s, &q0, &q1);
         *cnt = seg_tiles(q0, q1, a.sink, a.win, BK).count;
-        return *cnt > 0 ? *cnt + kSegUnits : 0;
+        return *cnt > 0 ? *cnt * kTileUnits + kSegUnits : 0;
     };
     int total = 0;
     for (int base = 0; base < nsegs; base += 256) {
@@ -223,7 +229,7 @@ void prefill_kernel(PrefillArgs a) {
             int chunk, chunk_p;
             const int F = f_carry + block_excl_scan(u, tid, scan_scratch, &chunk);
             const int T0 = F + kSegUnits;      // first tile unit
-            const int np = cnt > 0 ? owner(T0 + cnt - 1) - owner(T0) + 1 : 0;
+            const int np = cnt > 0 ? owner(T0 + (cnt - 1) * kTileUnits) - owner(T0) + 1 : 0;
             const int pc = np > 1 ? np : 0;
             const int P = p_carry + block_excl_scan(pc, tid, scan_scratch, &chunk_p);
             if (wg == 0 && s < nsegs) {
@@ -513,11 +519,15 @@ void prefill_kernel(PrefillArgs a) {
             int cnt;
             const int u = seg_units(seg, &cnt);
             const int T0 = F + kSegUnits;
-            const int t_lo = (int)max(lo - T0, 0LL);
-            const int t_hi = (int)min(hi - T0, (long long)cnt);
+            // tiles whose first unit lies in [lo, hi)
+            auto first_tile_at_or_after = [&](long long x) -> long long {
+                return x <= T0 ? 0 : (x - T0 + kTileUnits - 1) / kTileUnits;
+            };
+            const int t_lo = (int)min(first_tile_at_or_after(lo), (long long)cnt);
+            const int t_hi = (int)min(first_tile_at_or_after(hi), (long long)cnt);
             if (t_lo < t_hi) {     // this run owns tiles of the segment
                 const int f_owner = owner(T0);
-                const bool whole = owner(T0 + cnt - 1) == f_owner;
+                const bool whole = owner(T0 + (cnt - 1) * kTileUnits) == f_owner;
                 int piece = 0;
                 if (!whole) {
                     // piece table offset of a cut segment: only the run's
