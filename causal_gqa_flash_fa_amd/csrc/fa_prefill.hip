@@ -296,7 +296,10 @@ void prefill_kernel(PrefillArgs a) {
     float m_run = -INFINITY, l_run = 0.0f;
 
     // ---- staging registers of a Q4_0 tile (fp32 tiles need none)
-    uint32_t raw[FMT == 0 ? 1 : Sh::IPT][9];
+    // A Q4_0 block (18 bytes) is staged as 5 dwords: from the block start
+    // when it is 4-byte aligned (even blocks), else from 2 bytes before it.
+    // Both stay inside the row, which holds an even number of blocks.
+    uint32_t raw[FMT == 0 ? 1 : Sh::IPT][5];
 
     // Starts loading the tile at key j0 into LDS buffer `buf` (fp32: DMA
     // into LDS; Q4_0: raw blocks into registers). Rows past q1 (only in a
@@ -330,13 +333,13 @@ void prefill_kernel(PrefillArgs a) {
                 const int row = rem / NB, blk = rem % NB;
                 const uint8_t *base = idx < BK * NB ? kbase : vbase;
                 if (idx < Sh::QITEMS && j0 + row <= q1) {
-                    const uint16_t *src =
-                        (const uint16_t *)(base + (size_t)(j0 + row) * RB + blk * kQ4BlockBytes);
+                    const uint32_t *src = (const uint32_t *)(base + (size_t)(j0 + row) * RB +
+                                                             blk * kQ4BlockBytes - 2 * (blk & 1));
 #pragma unroll
-                    for (int u = 0; u < 9; u++) raw[i][u] = src[u];
+                    for (int u = 0; u < 5; u++) raw[i][u] = src[u];
                 } else {
 #pragma unroll
-                    for (int u = 0; u < 9; u++) raw[i][u] = 0;
+                    for (int u = 0; u < 5; u++) raw[i][u] = 0;
                 }
             }
         }
@@ -354,11 +357,14 @@ void prefill_kernel(PrefillArgs a) {
                     const int rem = idx % (BK * NB);
                     const int row = rem / NB, blk = rem % NB;
                     float *dst = (idx < BK * NB ? kd : vd) + row * KS + blk * kQ4Block;
-                    const float d = half_bits_to_float(raw[i][0]);
+                    const bool odd = (blk & 1) != 0;
+                    const float d = half_bits_to_float(odd ? raw[i][0] >> 16 : raw[i][0]);
                     const float m8d = -8.0f * d;
 #pragma unroll
                     for (int q = 0; q < 4; q++) {
-                        const uint32_t cw = raw[i][1 + 2 * q] | (raw[i][2 + 2 * q] << 16);
+                        // code bytes 4q..4q+3 of the block
+                        const uint32_t cw = odd ? raw[i][q + 1]
+                                                : __builtin_amdgcn_alignbyte(raw[i][q + 1], raw[i][q], 2);
                         // (c - 8) * d == c*d - 8d exactly: c*d has <= 15 significant bits
                         const f32x4 lo = {fmaf(nib(cw, 0), d, m8d), fmaf(nib(cw, 8), d, m8d),
                                           fmaf(nib(cw, 16), d, m8d), fmaf(nib(cw, 24), d, m8d)};
