@@ -91,58 +91,6 @@ __device__ __forceinline__ float byte_f(uint32_t w, int t) {
     return (float)((w >> (8 * t)) & 0xffu);   // v_cvt_f32_ubyte{t}
 }
 
-__device__ __forceinline__ float lo_h(uint32_t r) {
-    return (float)__builtin_bit_cast(_Float16, (uint16_t)(r & 0xffffu));
-}
-__device__ __forceinline__ float hi_h(uint32_t r) {
-    return (float)__builtin_bit_cast(_Float16, (uint16_t)(r >> 16));
-}
-
-// The 8 elements held by one code word w (bytes b0..b3): element e = low
-// nibble of byte e, element 16 + e = high nibble of byte e (e = 0..3, relative
-// to the word). A nibble masked into a binary16 with exponent bits 0x6400
-// gives 1024 + c (low nibble, bits 0-3) or 1024 + 16 c (high nibble, bits
-// 4-7, still inside the 10-bit mantissa), so one and-or per two elements
-// builds fma_mix operands: (1024 + c) d - 1032 d and (1024 + 16 c) (d / 16)
-// - 72 d are both exactly (c - 8) d. `k` holds the masks and exponent bits in
-// registers so the and-or is a single three-operand instruction.
-struct NibConsts {
-    uint32_t lo, hi, ex;
-};
-__device__ __forceinline__ NibConsts nib_consts() {
-    NibConsts k;
-    // opaque to the compiler: kept in VGPRs instead of being folded as literals
-    asm volatile("v_mov_b32 %0, 0x000f000f" : "=v"(k.lo));
-    asm volatile("v_mov_b32 %0, 0x00f000f0" : "=v"(k.hi));
-    asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(k.ex));
-    return k;
-}
-// The per-block constants of dequant_word.
-struct BlockScale {
-    float d, d16, blo, bhi;
-};
-__device__ __forceinline__ BlockScale block_scale(float d) {
-    return BlockScale{d, d * 0.0625f, -1032.0f * d, -72.0f * d};
-}
-// out[0..3] = elements e = 0..3 (low nibbles), out[4..7] = elements 16 + e.
-__device__ __forceinline__ void dequant_word(uint32_t w, const BlockScale &sc, const NibConsts &k,
-                                             float *out) {
-    const float d = sc.d, d16 = sc.d16, blo = sc.blo, bhi = sc.bhi;
-    const uint32_t w8 = w >> 8;
-    const uint32_t a = (w & k.lo) | k.ex;     // bytes 0, 2 low nibbles
-    const uint32_t b = (w8 & k.lo) | k.ex;    // bytes 1, 3 low nibbles
-    const uint32_t c = (w & k.hi) | k.ex;     // bytes 0, 2 high nibbles (x16)
-    const uint32_t e = (w8 & k.hi) | k.ex;    // bytes 1, 3 high nibbles (x16)
-    out[0] = fmaf(lo_h(a), d, blo);
-    out[1] = fmaf(lo_h(b), d, blo);
-    out[2] = fmaf(hi_h(a), d, blo);
-    out[3] = fmaf(hi_h(b), d, blo);
-    out[4] = fmaf(lo_h(c), d16, bhi);
-    out[5] = fmaf(lo_h(e), d16, bhi);
-    out[6] = fmaf(hi_h(c), d16, bhi);
-    out[7] = fmaf(hi_h(e), d16, bhi);
-}
-
 __device__ __forceinline__ int wave_sum_i(int x) {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);

@@ -350,6 +350,7 @@ void prefill_kernel(PrefillArgs a) {
         if constexpr (FMT == 1) {
             float *kd = lds + buf * Sh::BUF;
             float *vd = kd + BK * KS;
+            const NibConsts nk = nib_consts();
 #pragma unroll
             for (int i = 0; i < Sh::IPT; i++) {
                 const int idx = tid + 256 * i;
@@ -358,20 +359,17 @@ void prefill_kernel(PrefillArgs a) {
                     const int row = rem / NB, blk = rem % NB;
                     float *dst = (idx < BK * NB ? kd : vd) + row * KS + blk * kQ4Block;
                     const bool odd = (blk & 1) != 0;
-                    const float d = half_bits_to_float(odd ? raw[i][0] >> 16 : raw[i][0]);
-                    const float m8d = -8.0f * d;
+                    const BlockScale sc =
+                        block_scale(half_bits_to_float(odd ? raw[i][0] >> 16 : raw[i][0]));
 #pragma unroll
                     for (int q = 0; q < 4; q++) {
                         // code bytes 4q..4q+3 of the block
                         const uint32_t cw = odd ? raw[i][q + 1]
                                                 : __builtin_amdgcn_alignbyte(raw[i][q + 1], raw[i][q], 2);
-                        // (c - 8) * d == c*d - 8d exactly: c*d has <= 15 significant bits
-                        const f32x4 lo = {fmaf(nib(cw, 0), d, m8d), fmaf(nib(cw, 8), d, m8d),
-                                          fmaf(nib(cw, 16), d, m8d), fmaf(nib(cw, 24), d, m8d)};
-                        const f32x4 hi = {fmaf(nib(cw, 4), d, m8d), fmaf(nib(cw, 12), d, m8d),
-                                          fmaf(nib(cw, 20), d, m8d), fmaf(nib(cw, 28), d, m8d)};
-                        *(f32x4 *)&dst[4 * q] = lo;
-                        *(f32x4 *)&dst[16 + 4 * q] = hi;
+                        float v[8];
+                        dequant_word(cw, sc, nk, v);
+                        *(f32x4 *)&dst[4 * q] = f32x4{v[0], v[1], v[2], v[3]};
+                        *(f32x4 *)&dst[16 + 4 * q] = f32x4{v[4], v[5], v[6], v[7]};
                     }
                 }
             }
