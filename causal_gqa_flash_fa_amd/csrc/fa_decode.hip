@@ -125,8 +125,8 @@ void decode_partial_kernel(DecodeArgs a) {
     constexpr float TAU = 8.0f;
     typedef typename Chunk<CB>::T chunk_t;
 
-    __shared__ float Qs[HP * QS];
-    __shared__ float Pw[HP * PS];
+    __shared__ __attribute__((aligned(16))) float Qs[HP * QS];
+    __shared__ __attribute__((aligned(16))) float Pw[HP * PS];
     __shared__ __attribute__((aligned(16))) uint8_t Rw[Sh::TILE_BYTES];
 
     const int lane = threadIdx.x;

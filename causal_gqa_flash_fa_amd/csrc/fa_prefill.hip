@@ -167,7 +167,7 @@ void prefill_kernel(PrefillArgs a) {
     constexpr int BK = Sh::BK, KS = Sh::KS, NT = Sh::NT, GS = Sh::GS, HH = Sh::HH;
     constexpr int NB = Sh::NB, RB = Sh::RB;
     constexpr int ROWS = Sh::W * Sh::R;
-    extern __shared__ float lds[];
+    extern __shared__ __attribute__((aligned(16))) float lds[];   // 16-byte LDS accesses need 16-byte alignment
     __shared__ int scan_scratch[4];
     __shared__ int run_info[8];
 
@@ -300,6 +300,17 @@ void prefill_kernel(PrefillArgs a) {
     // when it is 4-byte aligned (even blocks), else from 2 bytes before it.
     // Both stay inside the row, which holds an even number of blocks.
     uint32_t raw[FMT == 0 ? 1 : Sh::IPT][5];
+    // Q4_0 item idx -> (row, block) of the K tile (idx < BK*NB) or V tile:
+    // 8 consecutive items take 8 consecutive rows of one block, then the
+    // next block. A wave thus reads 8 whole rows (contiguous in memory),
+    // and its 16-byte LDS writes land on rows KS floats apart (16 bytes
+    // apart modulo 128), one bank group per lane: no bank conflicts.
+    auto q4_item = [](int idx, int &row, int &blk) {
+        const int rem = idx % (BK * NB);
+        const int g = rem / (8 * NB), w8 = rem % (8 * NB);
+        blk = w8 >> 3;
+        row = 8 * g + (w8 & 7);
+    };
 
     // Starts loading the tile at key j0 into LDS buffer `buf` (fp32: DMA
     // into LDS; Q4_0: raw blocks into registers). Rows past q1 (only in a
@@ -329,8 +340,8 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
             for (int i = 0; i < Sh::IPT; i++) {
                 const int idx = tid + 256 * i;
-                const int rem = idx % (BK * NB);
-                const int row = rem / NB, blk = rem % NB;
+                int row, blk;
+                q4_item(idx, row, blk);
                 const uint8_t *base = idx < BK * NB ? kbase : vbase;
                 if (idx < Sh::QITEMS && j0 + row <= q1) {
                     const uint32_t *src = (const uint32_t *)(base + (size_t)(j0 + row) * RB +
@@ -355,8 +366,8 @@ void prefill_kernel(PrefillArgs a) {
             for (int i = 0; i < Sh::IPT; i++) {
                 const int idx = tid + 256 * i;
                 if (idx < Sh::QITEMS) {
-                    const int rem = idx % (BK * NB);
-                    const int row = rem / NB, blk = rem % NB;
+                    int row, blk;
+                    q4_item(idx, row, blk);
                     float *dst = (idx < BK * NB ? kd : vd) + row * KS + blk * kQ4Block;
                     const bool odd = (blk & 1) != 0;
                     const BlockScale sc =
