@@ -159,11 +159,23 @@ void decode_partial_kernel(DecodeArgs a) {
         const int k_lo = it_lo * split_len;
         const int k_hi = min(L, it_hi * split_len);
 
-        wave_lds_sync();          // previous segment done with Qs
-        for (int idx = lane; idx < HP * HD; idx += 64) {
-            const int hr = idx / HD, e = idx % HD;
-            Qs[hr * QS + e] =
-                hr < G ? a.q[((size_t)slot * a.n_head + kvh * G + hr) * HD + e] * a.qscale : 0.0f;
+        // q rows of the group (contiguous in memory) -> Qs, scaled; rows
+        // past G are zero. All loads are issued before the first store.
+        {
+            constexpr int NQ = HP * HD / 256;   // float4 per lane
+            const float *qg = a.q + ((size_t)slot * a.n_head + kvh * G) * HD;
+            f32x4 qv[NQ];
+#pragma unroll
+            for (int i = 0; i < NQ; i++) {
+                const int f = 4 * (lane + 64 * i);
+                qv[i] = f / HD < G ? *(const f32x4 *)(qg + f) : f32x4{};
+            }
+            wave_lds_sync();      // previous segment done with Qs
+#pragma unroll
+            for (int i = 0; i < NQ; i++) {
+                const int f = 4 * (lane + 64 * i);
+                *(f32x4 *)&Qs[(f / HD) * QS + f % HD] = qv[i] * a.qscale;
+            }
         }
         wave_lds_sync();
 
