@@ -33,14 +33,14 @@
 // Scores are kept in base-2 units (q pre-scaled by scale*log2 e), so partial
 // m values are log2-scaled and the combine uses exp2.
 //
-// Q4_0 tiles: the next tile's K and V bytes (64 contiguous rows each) are
-// fetched with coalesced loads into registers while the current tile
-// computes, then go through a per-wave LDS buffer (K first: each lane reads
-// back its own key's row; then V). A code nibble c becomes (c - 8) * d with
-// one v_fma_mix_f32: the nibble is placed in a binary16 whose value is
-// 1024 + c, and (1024 + c) * d - 1032 * d is exact. PV takes two keys per
-// instruction (lanes 0-31 even keys, 32-63 odd keys), each lane owning dims
-// that share one block's code bytes; the two halves are summed at the end.
+// Q4_0 tiles: each lane loads its own key's raw K row into registers (the
+// next tile's rows fly during this tile's PV); the raw V tile goes into a
+// per-wave LDS buffer by LDS DMA, in flight during QK and softmax. A code
+// nibble c becomes (c - 8) * d with one v_fma_mix_f32: the nibble is placed
+// in a binary16 whose value is 1024 + c, and (1024 + c) * d - 1032 * d is
+// exact. PV takes two keys per instruction (lanes 0-31 even keys, 32-63 odd
+// keys), each lane owning dims that share one block's code bytes, with its
+// LDS operands read one step ahead; the two halves are summed at the end.
 // fp32 tiles: each lane reads its key's K row and, in PV, 4 dims of each V
 // row straight from memory.
 //
@@ -402,42 +402,71 @@ void decode_partial_kernel(DecodeArgs a) {
                 const int ll = lane & 31;
                 const int bb = ll / Sh::LPB, jb = (ll % Sh::LPB) * BPL;
                 const float *plane = Pw + (lane & 3) * PS + hk * 32;
-                // Fully unrolled: the compiler guards the first V read with a
-                // wait for all outstanding memory operations (it cannot tell
-                // the DMA is done), so the next tile's K rows are requested
-                // only after the first step, and fly during the rest of PV.
-#pragma unroll
-                for (int t4 = 0; t4 < 8; t4++) {
-                    if (t4 == 1 && more) fetch_k(j);
-                    f32x4 pa[NHG];
+                // Step i (t4 = i / 4, u = i % 4) takes key 2 i + hk. Its LDS
+                // operands (block scale, code bytes; P values at each t4) are
+                // read one step ahead, fenced so the scheduler keeps them
+                // there, so LDS latency hides behind the previous step's
+                // MFMAs. Fully unrolled: the compiler guards the first V read
+                // with a wait for all outstanding memory operations (it
+                // cannot tell the DMA is done), so the next tile's K rows are
+                // requested only after the first t4 block, and fly during the
+                // rest of PV.
+                // raw LDS values only: any arithmetic on them here would make
+                // the compiler wait for the reads just issued
+                auto vread = [&](int i, uint32_t (&r)[3]) {
+                    const uint8_t *vr = Rw + (2 * i + hk) * RB + bb * kQ4BlockBytes;
+                    r[0] = *(const uint16_t *)vr;
+                    if constexpr (BPL == 4) {
+                        r[1] = *(const uint16_t *)(vr + 2 + jb);
+                        r[2] = *(const uint16_t *)(vr + 4 + jb);
+                    } else if constexpr (BPL == 2) {
+                        r[1] = *(const uint16_t *)(vr + 2 + jb);
+                    } else {
+                        r[1] = vr[2 + jb];
+                    }
+                };
+                auto pread = [&](int t4, f32x4 (&pa)[NHG]) {
 #pragma unroll
                     for (int hg = 0; hg < NHG; hg++)
                         pa[hg] = *(const f32x4 *)(plane + hg * 4 * PS + 4 * t4);
+                };
+                uint32_t vr_c[3] = {0, 0, 0};
+                f32x4 pa_c[NHG];
+                vread(0, vr_c);
+                pread(0, pa_c);
 #pragma unroll
-                    for (int u = 0; u < 4; u++) {
-                        const int kl = 2 * (4 * t4 + u) + hk;
-                        const uint8_t *vr = Rw + kl * RB + bb * kQ4BlockBytes;
-                        const float d = half_bits_to_float(*(const uint16_t *)vr);
-                        float vv[OD];
-                        if constexpr (BPL == 4) {
-                            const uint32_t cw = *(const uint16_t *)(vr + 2 + jb) |
-                                                ((uint32_t)*(const uint16_t *)(vr + 4 + jb) << 16);
-                            dequant_word(cw, block_scale(d), nk, vv);   // elements jb + t, 16 + jb + t
-                        } else {
-                            const uint32_t cw = BPL == 2 ? (uint32_t)*(const uint16_t *)(vr + 2 + jb)
-                                                         : (uint32_t)vr[2 + jb];
-                            const float m8d = -8.0f * d;
+                for (int i = 0; i < 32; i++) {
+                    const int t4 = i >> 2, u = i & 3;
+                    if (i == 4 && more) fetch_k(j);
+                    uint32_t vr_n[3] = {0, 0, 0};
+                    f32x4 pa_n[NHG];
+                    if (i + 1 < 32) vread(i + 1, vr_n);
+                    if (u == 3 && t4 + 1 < 8) pread(t4 + 1, pa_n);
+                    __builtin_amdgcn_sched_barrier(0);
+                    const float d = half_bits_to_float(vr_c[0]);
+                    const uint32_t cw_c = BPL == 4 ? vr_c[1] | (vr_c[2] << 16) : vr_c[1];
+                    float vv[OD];
+                    if constexpr (BPL == 4) {
+                        dequant_word(cw_c, block_scale(d), nk, vv);   // elements jb + t, 16 + jb + t
+                    } else {
+                        const float m8d = -8.0f * d;
 #pragma unroll
-                            for (int b = 0; b < BPL; b++) {
-                                vv[b] = fmaf(byte_f(cw & 0x0f0f0f0fu, b), d, m8d);
-                                vv[BPL + b] = fmaf(byte_f((cw >> 4) & 0x0f0f0f0fu, b), d, m8d);
-                            }
+                        for (int b = 0; b < BPL; b++) {
+                            vv[b] = fmaf(byte_f(cw_c & 0x0f0f0f0fu, b), d, m8d);
+                            vv[BPL + b] = fmaf(byte_f((cw_c >> 4) & 0x0f0f0f0fu, b), d, m8d);
                         }
+                    }
 #pragma unroll
-                        for (int c = 0; c < OD; c++)
+                    for (int c = 0; c < OD; c++)
 #pragma unroll
-                            for (int hg = 0; hg < NHG; hg++)
-                                O[c][hg] = mfma4(pa[hg][u], vv[c], O[c][hg]);
+                        for (int hg = 0; hg < NHG; hg++)
+                            O[c][hg] = mfma4(pa_c[hg][u], vv[c], O[c][hg]);
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int r = 0; r < 3; r++) vr_c[r] = vr_n[r];
+                    if (u == 3 && t4 + 1 < 8) {
+#pragma unroll
+                        for (int hg = 0; hg < NHG; hg++) pa_c[hg] = pa_n[hg];
                     }
                 }
                 wave_lds_sync();                      // Rw and Pw free again
