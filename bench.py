@@ -202,9 +202,33 @@ def cpu_baseline(w) -> dict:
     t0 = time.perf_counter()
     oracle.prefill(q, kt, vt, w.pos0, w.attn_sink, w.attn_win, w.scale, threads=threads)
     dt = time.perf_counter() - t0
-    return {"value": prefill_flops(w) / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
+    value = prefill_flops(w) / dt / 1e12
+    # one thread on a fixed subset: every 16th (position, head) row
+    sel = np.arange(0, w.n * w.n_head, 16, dtype=np.int64)
+    pos = w.pos0 + sel // w.n_head
+    sel_flops = 4.0 * w.head_dim * sum(keyset_pairs(1, int(p), w.attn_sink, w.attn_win) for p in pos)
+    t0 = time.perf_counter()
+    oracle.prefill(q, kt, vt, w.pos0, w.attn_sink, w.attn_win, w.scale, sel=sel, threads=1)
+    dt1 = time.perf_counter() - t0
+    return {"value": value, "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle", "seconds": dt,
-            "sample": f"all {w.n * w.n_head} rows of {w.name} (fp64 global-max softmax)"}
+            "sample": f"all {w.n * w.n_head} rows of {w.name} (fp64 global-max softmax)",
+            "per_core_gflops": value * 1e3 / threads,
+            "single_thread": {"gflops": sel_flops / dt1 / 1e9, "seconds": dt1,
+                              "sample": f"every 16th row ({sel.size} rows) of {w.name}"},
+            "cpu_model": cpu_model()}
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (Linux /proc/cpuinfo), or ""."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return ""
 
 
 def copy_calibration(torch, nbytes: int = 1 << 30) -> dict:
