@@ -28,9 +28,10 @@ FA_KV_F32 = 0
 FA_KV_Q4_0 = 1
 
 EXPORTS = [
-    "fa_cache_row_bytes", "fa_cache_bytes", "fa_init", "fa_kv_append", "fa_prefill",
+    "fa_cache_row_bytes", "fa_cache_bytes", "fa_init", "fa_kv_append", "fa_kv_append_slots",
+    "fa_prefill",
     "fa_prefill_tile_shape", "fa_prefill_workspace_bytes", "fa_decode_plan", "fa_decode_plan_params",
-    "fa_decode_workspace_bytes", "fa_decode", "fa_strerror",
+    "fa_decode_workspace_bytes", "fa_decode", "fa_strerror", "fa_last_hip_error",
 ]
 
 
@@ -44,7 +45,10 @@ class fa_cache(ctypes.Structure):
 class FaError(RuntimeError):
     def __init__(self, code: int, where: str):
         self.code = code
-        super().__init__(f"{where}: {fa_strerror(code)} (code {code})")
+        msg = f"{where}: {fa_strerror(code)} (code {code})"
+        if code == FA_EHIP:
+            msg += f" [{lib.fa_last_hip_error().decode()}]"
+        super().__init__(msg)
 
 
 def _load() -> ctypes.CDLL:
@@ -52,6 +56,10 @@ def _load() -> ctypes.CDLL:
         raise ImportError(
             f"{LIB_PATH} is not built; run `python causal_gqa_flash_fa_amd/build.py` "
             "(there is no CPU fallback)")
+    # torch first: its HIP runtime (soname libamdhip64.so.7) is then the one
+    # libfa.so binds to. Loaded the other way round, torch pulls in a second
+    # copy of the runtime, and its stream handles mean nothing to libfa's.
+    import torch  # noqa: F401
     L = ctypes.CDLL(LIB_PATH)
     P, I, Z, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_float
     PI = ctypes.POINTER(ctypes.c_int)
@@ -64,6 +72,10 @@ def _load() -> ctypes.CDLL:
     L.fa_init.restype = I
     L.fa_kv_append.argtypes = [C, I, I, I, P, P, P]
     L.fa_kv_append.restype = I
+    L.fa_kv_append_slots.argtypes = [C, P, I, P, P, P]
+    L.fa_kv_append_slots.restype = I
+    L.fa_last_hip_error.argtypes = []
+    L.fa_last_hip_error.restype = ctypes.c_char_p
     L.fa_prefill.argtypes = [C, I, P, I, I, I, I, I, F, P, P, Z, P, P]
     L.fa_prefill.restype = I
     L.fa_prefill_workspace_bytes.argtypes = [I, I, I, I]
@@ -131,6 +143,12 @@ def fa_kv_append(cache: fa_cache, slot: int, pos0: int, n: int, k_new, v_new,
                  stream=None) -> None:
     _check(lib.fa_kv_append(ctypes.byref(cache), slot, pos0, n, _ptr(k_new), _ptr(v_new),
                             _stream(stream)), "fa_kv_append")
+
+
+def fa_kv_append_slots(cache: fa_cache, d_pos, n_slots: int, k_new, v_new,
+                       stream=None) -> None:
+    _check(lib.fa_kv_append_slots(ctypes.byref(cache), _ptr(d_pos), n_slots, _ptr(k_new),
+                                  _ptr(v_new), _stream(stream)), "fa_kv_append_slots")
 
 
 def fa_prefill(cache: fa_cache, slot: int, q, pos0: int, n: int, n_head: int,

@@ -41,7 +41,14 @@ size_t slot_stride_bytes(const fa_cache *c) {
     return (size_t)c->n_kv_head * c->max_seq * fa_cache_row_bytes(c->format, c->head_dim);
 }
 
-int hip_rc(hipError_t e) { return e == hipSuccess ? FA_OK : FA_EHIP; }
+// The HIP error behind this thread's most recent FA_EHIP.
+thread_local hipError_t g_last_hip_error = hipSuccess;
+
+int hip_rc(hipError_t e) {
+    if (e == hipSuccess) return FA_OK;
+    g_last_hip_error = e;
+    return FA_EHIP;
+}
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -64,11 +71,11 @@ size_t fa_cache_bytes(const fa_cache *c) {
 
 int fa_init(void) {
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return FA_EHIP;
+    if (hip_rc(hipGetDevice(&dev))) return FA_EHIP;
     if (dev < 0 || dev >= kMaxDevices) return FA_EDEVICE;
     if (g_device_ok[dev] == 0) {
         hipDeviceProp_t prop;
-        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return FA_EHIP;
+        if (hip_rc(hipGetDeviceProperties(&prop, dev))) return FA_EHIP;
         g_device_ok[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
         g_device_cus[dev] = prop.multiProcessorCount;
     }
@@ -94,6 +101,31 @@ int fa_kv_append(const fa_cache *cache, int slot, int pos0, int n, const float *
     a.head_dim = cache->head_dim;
     a.max_seq = cache->max_seq;
     a.pos0 = pos0;
+    a.d_pos = nullptr;
+    a.slot_bytes = 0;
+    return hip_rc(fa::launch_append(cache->format, a, (hipStream_t)stream));
+}
+
+int fa_kv_append_slots(const fa_cache *cache, const int *d_pos, int n_slots, const float *k_new,
+                       const float *v_new, void *stream) {
+    int rc = check_cache(cache);
+    if (rc) return rc;
+    if (n_slots < 0 || n_slots > cache->n_slots) return FA_EINVAL;
+    if (n_slots == 0) return FA_OK;
+    if (!d_pos || !k_new || !v_new) return FA_ENULL;
+    if ((rc = fa_init())) return rc;
+    fa::AppendArgs a;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.k = cache->k;
+    a.v = cache->v;
+    a.n = n_slots;
+    a.n_kv = cache->n_kv_head;
+    a.head_dim = cache->head_dim;
+    a.max_seq = cache->max_seq;
+    a.pos0 = 0;
+    a.d_pos = d_pos;
+    a.slot_bytes = slot_stride_bytes(cache);
     return hip_rc(fa::launch_append(cache->format, a, (hipStream_t)stream));
 }
 
@@ -173,7 +205,7 @@ int fa_prefill(const fa_cache *cache, int slot, const float *q, int pos0, int n,
     if (ws_bytes < lay.total) return FA_EWORKSPACE;
     if ((rc = fa_init())) return rc;
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return FA_EHIP;
+    if (hip_rc(hipGetDevice(&dev))) return FA_EHIP;
     const int group = n_head / cache->n_kv_head;
     const int bq = fa::prefill_q_positions(group);
     const int sink = attn_sink < 0 ? 0 : attn_sink;
@@ -293,6 +325,8 @@ int fa_decode(const fa_cache *cache, const float *q, const int *d_pos, int n_slo
     return hip_rc(fa::launch_decode(cache->format, cache->head_dim, n_head / cache->n_kv_head,
                                     a, lay.waves, (hipStream_t)stream));
 }
+
+const char *fa_last_hip_error(void) { return hipGetErrorName(g_last_hip_error); }
 
 const char *fa_strerror(int code) {
     switch (code) {

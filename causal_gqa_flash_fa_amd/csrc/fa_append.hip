@@ -1,6 +1,9 @@
 // KV-cache append: fp32 copy and fp32 -> Q4_0 block quantisation.
 //
 // [FA] fc_attn_kv_append: rows [n][n_kv][hd] land at cache[kv][pos0+t][:].
+// [FA] fc_attn_kv_append_slots ("Multi-user decode attention (slots)"
+// section): row t of [n_slots][n_kv][hd] lands in slot t at the position held
+// in device memory, so the enqueued work does not depend on the position.
 // [FA] fc_kvq4_quant_block: per 32-element block, amax fold from 0,
 // d = amax / -8 (negative scale), id = 1/d or 0, code = clamp(rint(x*id)+8,
 // 0, 15) (convert, then +8, then clamp), binary16 d in bytes 0-1 (LE), byte
@@ -20,10 +23,25 @@ namespace {
 
 constexpr int kAppendThreads = 256;
 
+// Cache row (h, position) of input row t and the byte offset of its slot;
+// false when a device position lies outside the cache (nothing is written).
+__device__ __forceinline__ bool dest_row(const AppendArgs &a, int t, int h, int64_t *row,
+                                         size_t *slot_off) {
+    int pos = a.pos0 + t;
+    *slot_off = 0;
+    if (a.d_pos) {
+        pos = a.d_pos[t];
+        if (pos < 0 || pos >= a.max_seq) return false;
+        *slot_off = (size_t)t * a.slot_bytes;
+    }
+    *row = (int64_t)h * a.max_seq + pos;
+    return true;
+}
+
 __global__ __launch_bounds__(kAppendThreads) void append_f32_kernel(AppendArgs a) {
     const int tensor = blockIdx.y;                    // 0: K, 1: V
     const float *src = tensor ? a.v_new : a.k_new;
-    float *dst = (float *)(tensor ? a.v : a.k);
+    uint8_t *base = (uint8_t *)(tensor ? a.v : a.k);
     const int c4_per_row = a.head_dim / 4;
     const int64_t total = (int64_t)a.n * a.n_kv * c4_per_row;
     const int64_t i = (int64_t)blockIdx.x * kAppendThreads + threadIdx.x;
@@ -32,8 +50,11 @@ __global__ __launch_bounds__(kAppendThreads) void append_f32_kernel(AppendArgs a
     const int64_t th = i / c4_per_row;                // t * n_kv + h
     const int h = (int)(th % a.n_kv);
     const int t = (int)(th / a.n_kv);
+    int64_t row;
+    size_t slot_off;
+    if (!dest_row(a, t, h, &row, &slot_off)) return;
     const f32x4 x = *(const f32x4 *)(src + 4 * i);
-    const int64_t row = (int64_t)h * a.max_seq + a.pos0 + t;
+    float *dst = (float *)(base + slot_off);
     *(f32x4 *)(dst + row * a.head_dim + 4 * c4) = x;
 }
 
@@ -44,7 +65,7 @@ __device__ __forceinline__ int clamp_code(int c) {
 __global__ __launch_bounds__(kAppendThreads) void append_q4_kernel(AppendArgs a) {
     const int tensor = blockIdx.y;
     const float *src = tensor ? a.v_new : a.k_new;
-    uint8_t *dst = (uint8_t *)(tensor ? a.v : a.k);
+    uint8_t *base = (uint8_t *)(tensor ? a.v : a.k);
     const int nb = a.head_dim / kQ4Block;
     const int64_t total = (int64_t)a.n * a.n_kv * nb;
     const int64_t i = (int64_t)blockIdx.x * kAppendThreads + threadIdx.x;
@@ -53,6 +74,9 @@ __global__ __launch_bounds__(kAppendThreads) void append_q4_kernel(AppendArgs a)
     const int64_t th = i / nb;
     const int h = (int)(th % a.n_kv);
     const int t = (int)(th / a.n_kv);
+    int64_t row;
+    size_t slot_off;
+    if (!dest_row(a, t, h, &row, &slot_off)) return;
 
     float x[kQ4Block];
     const f32x4 *xs = (const f32x4 *)(src + i * kQ4Block);
@@ -72,8 +96,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_q4_kernel(AppendArgs a)
     const float id = (d != 0.0f) ? 1.0f / d : 0.0f;
 
     const int rb = q4_row_bytes(a.head_dim);
-    const int64_t row = (int64_t)h * a.max_seq + a.pos0 + t;
-    uint16_t *out = (uint16_t *)(dst + row * rb + blk * kQ4BlockBytes);
+    uint16_t *out = (uint16_t *)(base + slot_off + row * rb + blk * kQ4BlockBytes);
     // A zero scale is stored as binary16 -0.0 (0x8000), the sign of amax/-8.
     // Spelled out because the compiler folds the divide-by-(-8) and the fp16
     // conversion into one fused multiply-add whose +0 addend would turn -0

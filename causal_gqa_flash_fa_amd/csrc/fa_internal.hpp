@@ -13,6 +13,11 @@ struct AppendArgs {
     const float *k_new, *v_new;   // [n][n_kv][hd]
     void *k, *v;                  // slot base of the cache: [n_kv][max_seq][row]
     int n, n_kv, head_dim, max_seq, pos0;
+    // NULL: input row t goes to position pos0 + t of the slot at k/v.
+    // Else input row t belongs to slot t (base k/v + t * slot_bytes) and goes
+    // to position d_pos[t], read on the device; out-of-range positions skip.
+    const int *d_pos;
+    size_t slot_bytes;
 };
 
 struct PrefillArgs {

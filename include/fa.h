@@ -91,6 +91,24 @@ int fa_init(void);
 int fa_kv_append(const fa_cache *cache, int slot, int pos0, int n,
                  const float *k_new, const float *v_new, void *stream);
 
+/* One new row per slot at a position held in device memory ([FA] "Multi-user
+ * decode attention (slots)" section, fc_attn_kv_append_slots and the per-slot
+ * Q4_0 append; the device-resident position of fc_attn_kv_append_dev). For
+ * every slot s in [0, n_slots), row s of k_new/v_new is written to cache
+ * position d_pos[s] of slot s, converted exactly as fa_kv_append converts it
+ * (fp32 copy, or the same Q4_0 block quantisation, byte for byte). The
+ * positions are read on the device, so the enqueued work does not depend on
+ * them: with fa_decode (which also reads d_pos on the device) and a device-
+ * side position increment, one captured HIP graph replays a decode step at
+ * every position.
+ *   k_new, v_new: device [n_slots][n_kv_head][head_dim] fp32 (finite values).
+ *   d_pos: device int32[n_slots]. A slot whose d_pos[s] is outside
+ *   [0, max_seq) is left unchanged (the cache never wraps; fa_decode returns
+ *   NaN rows for such a slot). 0 <= n_slots <= cache->n_slots; n_slots == 0
+ *   enqueues nothing. One launch on `stream`. */
+int fa_kv_append_slots(const fa_cache *cache, const int *d_pos, int n_slots,
+                       const float *k_new, const float *v_new, void *stream);
+
 /* -------------------------------------------------------------- prefill */
 /* Causal GQA attention for n query rows of one slot at absolute positions
  * pos0 .. pos0+n-1, against cache rows [0, pos0+n) of that slot, which must
@@ -182,6 +200,10 @@ int fa_decode(const fa_cache *cache, const float *q, const int *d_pos, int n_slo
 
 /* Message for a return code (static storage). */
 const char *fa_strerror(int code);
+
+/* Name of the HIP runtime error behind the calling thread's most recent
+ * FA_EHIP return ("hipSuccess" if there was none); static storage. */
+const char *fa_last_hip_error(void);
 
 #ifdef __cplusplus
 }

@@ -30,6 +30,17 @@ def test_every_declared_function_is_exported():
     assert sorted(fa.EXPORTS) == names
 
 
+def test_one_hip_runtime_in_the_process():
+    # torch and libfa must share one HIP runtime: streams and errors are
+    # per-runtime objects
+    paths = set()
+    with open("/proc/self/maps") as f:
+        for line in f:
+            if "libamdhip64" in line:
+                paths.add(os.path.realpath(line.split()[-1]))
+    assert len(paths) == 1, paths
+
+
 def test_strerror_names_every_code():
     for code in range(0, -8, -1):
         assert fa.fa_strerror(code) != "unknown error code"
@@ -43,6 +54,11 @@ def cache(fmt=fa.FA_KV_F32, n_slots=2, n_kv=2, hd=128, max_seq=100, k=FAKE, v=FA
 def rc_append(c, slot=0, pos0=0, n=1, kn=FAKE, vn=FAKE):
     return fa.lib.fa_kv_append(ctypes.byref(c) if c is not None else None, slot, pos0, n, kn, vn,
                                None)
+
+
+def rc_append_slots(c, pos=FAKE, n_slots=1, kn=FAKE, vn=FAKE):
+    return fa.lib.fa_kv_append_slots(ctypes.byref(c) if c is not None else None, pos, n_slots,
+                                     kn, vn, None)
 
 
 def rc_prefill(c, slot=0, q=FAKE, pos0=0, n=1, n_head=4, sink=0, win=0, scale=0.1, out=FAKE,
@@ -81,6 +97,19 @@ def test_append_validation():
     assert rc_append(cache(), pos0=0, n=0) == fa.FA_OK            # empty: nothing enqueued
     assert rc_append(cache(), pos0=100, n=0) == fa.FA_OK
     assert rc_append(cache(), kn=0) == fa.FA_ENULL
+
+
+def test_append_slots_validation():
+    assert rc_append_slots(None) == fa.FA_ENULL
+    assert rc_append_slots(cache(hd=96)) == fa.FA_EUNSUPPORTED
+    assert rc_append_slots(cache(fmt=5)) == fa.FA_EUNSUPPORTED
+    assert rc_append_slots(cache(v=0)) == fa.FA_ENULL
+    assert rc_append_slots(cache(), n_slots=3) == fa.FA_EINVAL      # more slots than the cache
+    assert rc_append_slots(cache(), n_slots=-1) == fa.FA_EINVAL
+    assert rc_append_slots(cache(), n_slots=0) == fa.FA_OK          # empty: nothing enqueued
+    assert rc_append_slots(cache(), pos=0) == fa.FA_ENULL
+    assert rc_append_slots(cache(), kn=0) == fa.FA_ENULL
+    assert rc_append_slots(cache(), vn=0) == fa.FA_ENULL
 
 
 def test_prefill_validation():
