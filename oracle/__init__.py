@@ -55,6 +55,11 @@ def lib() -> ctypes.CDLL:
         L.oracle_gqa_rows.argtypes = [P, P, i32, P, P, i32, i32, i32, i32, i32, i32,
                                       dbl, P, i64, P]
         L.oracle_gqa_rows.restype = i32
+        L.oracle_key_is_fp16.argtypes = [i32, i32, i32, i32, i32]
+        L.oracle_key_is_fp16.restype = i32
+        L.oracle_gqa_rows_shadow.argtypes = [P, P, i32, P, P, P, P, i32, i32, i32, i32, i32,
+                                             i32, dbl, i32, i32, i32, P, i64, P]
+        L.oracle_gqa_rows_shadow.restype = i32
         L.oracle_decode_plan.argtypes = [i32, i32, i32, i32, P, P]
         L.oracle_decode_plan.restype = i32
         L.oracle_tile_walk.argtypes = [i32, i32, i32, i32, i32, i32, i32, P, P]
@@ -139,6 +144,55 @@ def gqa_rows(q: np.ndarray, q_pos, k: np.ndarray, v: np.ndarray, attn_sink: int,
                                    _ptr(part), part.size, out[lo:hi].ctypes.data)
         if rc != 0:
             raise ValueError("oracle_gqa_rows rejected its arguments")
+
+    if threads <= 1 or sel.size < 2:
+        run(0, sel.size)
+    else:
+        bounds = np.linspace(0, sel.size, threads + 1).astype(int)
+        with concurrent.futures.ThreadPoolExecutor(threads) as ex:
+            list(ex.map(lambda i: run(bounds[i], bounds[i + 1]), range(threads)))
+    return out
+
+
+def key_is_fp16(s: int, p: int, shadow_sink: int, shadow_win: int, live_lo: int) -> bool:
+    return bool(lib().oracle_key_is_fp16(s, p, shadow_sink, shadow_win, live_lo))
+
+
+def f16_round(x: np.ndarray) -> np.ndarray:
+    """float32 values rounded to binary16 (round-to-nearest-even), as float32."""
+    return np.asarray(x, dtype=np.float32).astype(np.float16).astype(np.float32)
+
+
+def gqa_rows_shadow(q: np.ndarray, q_pos, k: np.ndarray, v: np.ndarray, k16: np.ndarray,
+                    v16: np.ndarray, attn_sink: int, attn_win: int, scale: float,
+                    shadow_sink: int, shadow_win: int, live_lo: int, sel=None,
+                    threads: int = 1) -> np.ndarray:
+    """gqa_rows where key s of a query at p comes from k16/v16 (the fp16
+    shadow, as float32) when key_is_fp16(s, p, ...) and from k/v (the
+    dequantised Q4_0 body) otherwise. All four are [n_kv][kv_rows][hd]."""
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    k, v, k16, v16 = (np.ascontiguousarray(a, dtype=np.float32) for a in (k, v, k16, v16))
+    q_pos = np.ascontiguousarray(q_pos, dtype=np.int32)
+    n_q, n_head, hd = q.shape
+    n_kv, kv_rows, hd2 = k.shape
+    if hd2 != hd or q_pos.shape != (n_q,) or any(a.shape != k.shape for a in (v, k16, v16)):
+        raise ValueError("shape mismatch")
+    if sel is None:
+        sel = np.arange(n_q * n_head, dtype=np.int64)
+    sel = np.ascontiguousarray(sel, dtype=np.int64)
+    out = np.empty((sel.size, hd), dtype=np.float64)
+
+    def run(lo: int, hi: int) -> None:
+        if hi <= lo:
+            return
+        part = sel[lo:hi]
+        rc = lib().oracle_gqa_rows_shadow(_ptr(q), _ptr(q_pos), n_q, _ptr(k), _ptr(v), _ptr(k16),
+                                          _ptr(v16), kv_rows, n_head, n_kv, hd, attn_sink,
+                                          attn_win, float(scale), shadow_sink, shadow_win,
+                                          live_lo, _ptr(part), part.size,
+                                          out[lo:hi].ctypes.data)
+        if rc != 0:
+            raise ValueError("oracle_gqa_rows_shadow rejected its arguments")
 
     if threads <= 1 or sel.size < 2:
         run(0, sel.size)

@@ -219,6 +219,93 @@ int oracle_gqa_rows(const float *q, const int *q_pos, int n_q,
 
 /* ------------------------------------------------------- plans and tiles */
 
+int oracle_key_is_fp16(int s, int p, int shadow_sink, int shadow_win, int live_lo)
+{
+    if (s < shadow_sink)
+        return 1;
+    return shadow_win > 0 && s > p - shadow_win && s > live_lo;
+}
+
+/* attend_one with the K/V row of key j taken from the shadow (k16/v16) or
+ * the Q4_0 body (k/v) by oracle_key_is_fp16. */
+static void attend_one_shadow(const float *qv, const float *kb, const float *vb,
+                              const float *kb16, const float *vb16, int head_dim, int p,
+                              int attn_sink, int attn_win, int shadow_sink,
+                              int shadow_win, int live_lo, double scale, double *sc,
+                              double *out)
+{
+    double m = -INFINITY;
+    for (int j = 0; j <= p; j++) {
+        if (!oracle_key_in_set(j, p, attn_sink, attn_win))
+            continue;
+        const int f16 = oracle_key_is_fp16(j, p, shadow_sink, shadow_win, live_lo);
+        const float *kj = (f16 ? kb16 : kb) + (size_t)j * head_dim;
+        double dot = 0.0;
+        for (int e = 0; e < head_dim; e++)
+            dot += (double)qv[e] * (double)kj[e];
+        sc[j] = scale * dot;
+        if (sc[j] > m)
+            m = sc[j];
+    }
+    double sum = 0.0;
+    for (int e = 0; e < head_dim; e++)
+        out[e] = 0.0;
+    for (int j = 0; j <= p; j++) {
+        if (!oracle_key_in_set(j, p, attn_sink, attn_win))
+            continue;
+        const int f16 = oracle_key_is_fp16(j, p, shadow_sink, shadow_win, live_lo);
+        const double w = exp(sc[j] - m);
+        const float *vj = (f16 ? vb16 : vb) + (size_t)j * head_dim;
+        sum += w;
+        for (int e = 0; e < head_dim; e++)
+            out[e] += w * (double)vj[e];
+    }
+    for (int e = 0; e < head_dim; e++)
+        out[e] /= sum;
+}
+
+int oracle_gqa_rows_shadow(const float *q, const int *q_pos, int n_q,
+                           const float *k, const float *v,
+                           const float *k16, const float *v16, int kv_rows,
+                           int n_head, int n_kv_head, int head_dim,
+                           int attn_sink, int attn_win, double scale,
+                           int shadow_sink, int shadow_win, int live_lo,
+                           const int64_t *sel, int64_t n_sel, double *out)
+{
+    if (n_q < 0 || n_head <= 0 || n_kv_head <= 0 || head_dim <= 0 ||
+        n_head % n_kv_head != 0)
+        return -1;
+    const int group = n_head / n_kv_head;
+    const int64_t total = sel ? n_sel : (int64_t)n_q * n_head;
+    int max_p = -1;
+    for (int i = 0; i < n_q; i++) {
+        if (q_pos[i] < 0 || q_pos[i] >= kv_rows)
+            return -1;
+        if (q_pos[i] > max_p)
+            max_p = q_pos[i];
+    }
+    double *sc = (double *)malloc(sizeof(double) * (size_t)(max_p + 1 > 0 ? max_p + 1 : 1));
+    if (!sc)
+        return -1;
+    for (int64_t r = 0; r < total; r++) {
+        const int64_t flat = sel ? sel[r] : r;
+        if (flat < 0 || flat >= (int64_t)n_q * n_head) {
+            free(sc);
+            return -1;
+        }
+        const int qi = (int)(flat / n_head);
+        const int h = (int)(flat % n_head);
+        const int kvh = h / group;
+        const size_t kv_off = (size_t)kvh * kv_rows * head_dim;
+        attend_one_shadow(q + (size_t)flat * head_dim, k + kv_off, v + kv_off, k16 + kv_off,
+                          v16 + kv_off, head_dim, q_pos[qi], attn_sink, attn_win,
+                          shadow_sink, shadow_win, live_lo, scale, sc,
+                          out + (size_t)r * head_dim);
+    }
+    free(sc);
+    return 0;
+}
+
 int oracle_decode_plan(int seq_len, int kps, int cap, int tile,
                        int *n_splits, int *split_len)
 {

@@ -68,6 +68,25 @@ int oracle_gqa_rows(const float *q, const int *q_pos, int n_q,
                     int attn_sink, int attn_win, double scale,
                     const int64_t *sel, int64_t n_sel, double *out);
 
+/* fp16 shadow of a Q4_0 cache ([FA] "fp16 sink + recent-window exemption",
+ * fc_kvq4_is_fp16, and the win_live_lo guard of fc_attn_flash_prefill_q4):
+ * a query at position p reads key s at fp16 iff s < shadow_sink, or
+ * shadow_win > 0 and s > p - shadow_win and s > live_lo, where live_lo is the
+ * highest position appended so far minus the ring size (older ring rows were
+ * overwritten). Otherwise it reads the Q4_0 body. */
+int oracle_key_is_fp16(int s, int p, int shadow_sink, int shadow_win, int live_lo);
+
+/* oracle_gqa_rows with that choice per (query, key): k, v hold the Q4_0 body
+ * (dequantised) and k16, v16 the fp16 shadow values (as fp32), both
+ * [n_kv_head][kv_rows][head_dim]. */
+int oracle_gqa_rows_shadow(const float *q, const int *q_pos, int n_q,
+                           const float *k, const float *v,
+                           const float *k16, const float *v16, int kv_rows,
+                           int n_head, int n_kv_head, int head_dim,
+                           int attn_sink, int attn_win, double scale,
+                           int shadow_sink, int shadow_win, int live_lo,
+                           const int64_t *sel, int64_t n_sel, double *out);
+
 /* Decode split plan. [FA] fc_attn_dec_plan: n = clamp(ceil(L/kps), 1, cap);
  * split_len = ceil(L/n) rounded up to a multiple of `tile`; returns the live
  * split count ceil(L/split_len). */
