@@ -35,11 +35,19 @@ EXPORTS = [
 ]
 
 
+SHADOW_SINK_MAX = 8
+SHADOW_WIN_MAX = 256
+
+
 class fa_cache(ctypes.Structure):
     """Mirror of `struct fa_cache` in include/fa.h."""
     _fields_ = [("format", ctypes.c_int), ("n_slots", ctypes.c_int),
                 ("n_kv_head", ctypes.c_int), ("head_dim", ctypes.c_int),
-                ("max_seq", ctypes.c_int), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p)]
+                ("max_seq", ctypes.c_int), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("shadow_sink", ctypes.c_int), ("shadow_win", ctypes.c_int),
+                ("k_sink", ctypes.c_void_p), ("v_sink", ctypes.c_void_p),
+                ("k_win", ctypes.c_void_p), ("v_win", ctypes.c_void_p),
+                ("win_pos", ctypes.c_void_p)]
 
 
 class FaError(RuntimeError):
@@ -213,3 +221,22 @@ def make_cache(fmt: int, n_slots: int, n_kv_head: int, head_dim: int, max_seq: i
     k = torch.empty(nbytes, dtype=torch.uint8, device=device)
     v = torch.empty(nbytes, dtype=torch.uint8, device=device)
     return fa_cache(fmt, n_slots, n_kv_head, head_dim, max_seq, k.data_ptr(), v.data_ptr()), k, v
+
+
+def add_shadow(cache: fa_cache, sink: int, win: int, device="cuda"):
+    """Allocate the fp16 sink / recent-window shadow of a Q4_0 cache with torch
+    and record it in `cache` (win_pos filled with -1: no ring row holds a
+    position yet). Returns the tensors (k_sink, v_sink, k_win, v_win, win_pos);
+    keep them alive as long as the struct is used."""
+    import torch
+    n, h, d = cache.n_slots, cache.n_kv_head, cache.head_dim
+    ks = torch.zeros((n, h, SHADOW_SINK_MAX, d), dtype=torch.float16, device=device)
+    vs = torch.zeros_like(ks)
+    kw = torch.zeros((n, h, SHADOW_WIN_MAX, d), dtype=torch.float16, device=device)
+    vw = torch.zeros_like(kw)
+    wp = torch.full((n, SHADOW_WIN_MAX), -1, dtype=torch.int32, device=device)
+    cache.shadow_sink, cache.shadow_win = sink, win
+    cache.k_sink, cache.v_sink = ks.data_ptr(), vs.data_ptr()
+    cache.k_win, cache.v_win = kw.data_ptr(), vw.data_ptr()
+    cache.win_pos = wp.data_ptr()
+    return ks, vs, kw, vw, wp

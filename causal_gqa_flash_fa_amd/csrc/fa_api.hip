@@ -24,6 +24,14 @@ int check_cache(const fa_cache *c) {
     if (!dim_ok(c->head_dim)) return FA_EUNSUPPORTED;
     if (c->n_slots < 1 || c->n_kv_head < 1 || c->max_seq < 1) return FA_EINVAL;
     if (!c->k || !c->v) return FA_ENULL;
+    if (c->shadow_sink < 0 || c->shadow_sink > FA_SHADOW_SINK_MAX || c->shadow_win < 0 ||
+        c->shadow_win > FA_SHADOW_WIN_MAX)
+        return FA_EINVAL;
+    if (c->shadow_sink > 0 || c->shadow_win > 0) {
+        if (c->format != FA_KV_Q4_0) return FA_EUNSUPPORTED;   // the shadow exempts Q4_0 rows
+        if (c->shadow_sink > 0 && (!c->k_sink || !c->v_sink)) return FA_ENULL;
+        if (c->shadow_win > 0 && (!c->k_win || !c->v_win || !c->win_pos)) return FA_ENULL;
+    }
     return FA_OK;
 }
 
@@ -35,6 +43,31 @@ int check_heads(const fa_cache *c, int n_head) {
 
 int check_scale(float scale) {
     return (isfinite(scale) && scale > 0.0f) ? FA_OK : FA_EINVAL;
+}
+
+static_assert(fa::kShadowSinkMax == FA_SHADOW_SINK_MAX && fa::kShadowWinMax == FA_SHADOW_WIN_MAX,
+              "shadow capacity");
+
+// The cache's fp16 shadow with its buffers offset to `slot` (all zero if the
+// cache has none).
+fa::ShadowArgs shadow_args(const fa_cache *c, int slot) {
+    fa::ShadowArgs sh{};
+    if (c->shadow_sink <= 0 && c->shadow_win <= 0) return sh;
+    const size_t hd = (size_t)c->head_dim, nkv = (size_t)c->n_kv_head;
+    sh.sink = c->shadow_sink;
+    sh.win = c->shadow_win;
+    if (sh.sink > 0) {
+        const size_t off = (size_t)slot * nkv * fa::kShadowSinkMax * hd;
+        sh.k_sink = (uint16_t *)c->k_sink + off;
+        sh.v_sink = (uint16_t *)c->v_sink + off;
+    }
+    if (sh.win > 0) {
+        const size_t off = (size_t)slot * nkv * fa::kShadowWinMax * hd;
+        sh.k_win = (uint16_t *)c->k_win + off;
+        sh.v_win = (uint16_t *)c->v_win + off;
+        sh.win_pos = c->win_pos + (size_t)slot * fa::kShadowWinMax;
+    }
+    return sh;
 }
 
 size_t slot_stride_bytes(const fa_cache *c) {
@@ -103,6 +136,7 @@ int fa_kv_append(const fa_cache *cache, int slot, int pos0, int n, const float *
     a.pos0 = pos0;
     a.d_pos = nullptr;
     a.slot_bytes = 0;
+    a.sh = shadow_args(cache, slot);
     return hip_rc(fa::launch_append(cache->format, a, (hipStream_t)stream));
 }
 
@@ -126,6 +160,7 @@ int fa_kv_append_slots(const fa_cache *cache, const int *d_pos, int n_slots, con
     a.pos0 = 0;
     a.d_pos = d_pos;
     a.slot_bytes = slot_stride_bytes(cache);
+    a.sh = shadow_args(cache, 0);
     return hip_rc(fa::launch_append(cache->format, a, (hipStream_t)stream));
 }
 
@@ -142,7 +177,9 @@ namespace {
 // Stream-K prefill layout: pieces of cut segments and the segment table.
 struct PrefillLayout {
     int n_qblocks;
-    size_t pieces, table_bytes, m_off, l_off, acc_off, total;
+    size_t pieces, table_bytes, m_off, l_off, acc_off;
+    size_t sh_m_off, sh_l_off;    // fp16-shadow partial of every row: m, l ([n][n_head])
+    size_t total;
 };
 
 PrefillLayout prefill_layout(int n, int n_head, int n_kv_head, int head_dim) {
@@ -157,7 +194,10 @@ PrefillLayout prefill_layout(int n, int n_head, int n_kv_head, int head_dim) {
     p.m_off = p.table_bytes;
     p.l_off = p.m_off + align256(p.pieces * rows * sizeof(float));
     p.acc_off = p.l_off + align256(p.pieces * rows * sizeof(float));
-    p.total = p.acc_off + p.pieces * rows * (size_t)head_dim * sizeof(float);
+    const size_t qrows = (size_t)n * n_head;
+    p.sh_m_off = align256(p.acc_off + p.pieces * rows * (size_t)head_dim * sizeof(float));
+    p.sh_l_off = p.sh_m_off + align256(qrows * sizeof(float));
+    p.total = p.sh_l_off + qrows * sizeof(float);
     return p;
 }
 
@@ -235,6 +275,32 @@ int fa_prefill(const fa_cache *cache, int slot, const float *q, int pos0, int n,
     a.qscale = scale * fa::kLog2e;
     a.n_qblocks = lay.n_qblocks;
     a.n_wg = (int)n_wg;
+    a.sh = shadow_args(cache, slot);
+    a.sh_m = (const float *)(wsb + lay.sh_m_off);
+    a.sh_l = (const float *)(wsb + lay.sh_l_off);
+    if (a.sh.sink > 0 || a.sh.win > 0) {
+        // each row's shadow-key partial: m, l to the workspace, acc to out
+        fa::ShadowPassArgs sp;
+        sp.q = q;
+        sp.d_pos = nullptr;
+        sp.pos0 = pos0;
+        sp.n_q = n;
+        sp.n_head = n_head;
+        sp.n_kv = cache->n_kv_head;
+        sp.max_seq = cache->max_seq;
+        sp.sink = a.sink;
+        sp.win = a.win;
+        sp.qscale = a.qscale;
+        sp.sh = a.sh;
+        sp.chunk_groups = 1;
+        sp.chunks_per_group = (fa::kShadowSinkMax + fa::kShadowWinMax + 63) / 64;
+        sp.m_out = (float *)a.sh_m;
+        sp.l_out = (float *)a.sh_l;
+        sp.acc_out = out;
+        if ((rc = hip_rc(fa::launch_shadow_pass(cache->head_dim, group, sp,
+                                                n * cache->n_kv_head, (hipStream_t)stream))))
+            return rc;
+    }
     return hip_rc(fa::launch_prefill(cache->format, cache->head_dim, group, a,
                                      (hipStream_t)stream));
 }
@@ -259,8 +325,17 @@ namespace {
 // Decode work distribution for a launch: waves and the workspace layout.
 struct DecodeLayout {
     int waves;
-    size_t max_partials, table_bytes, m_off, l_off, acc_off, total;
+    size_t max_partials, table_bytes, m_off, l_off, acc_off;
+    int sh_groups;                // fp16-shadow partials per segment (0: no shadow)
+    size_t sh_m_off, sh_l_off, sh_acc_off, total;
 };
+
+// Shadow-pass work-groups per (query, kv head) in decode: one per 64-key chunk
+// of the largest shadow key set.
+int shadow_groups(const fa_cache *c) {
+    if (c->shadow_sink <= 0 && c->shadow_win <= 0) return 0;
+    return (c->shadow_sink + c->shadow_win + 63) / 64;
+}
 
 DecodeLayout decode_layout(const fa_cache *c, int n_slots, int n_head, int max_ctx) {
     DecodeLayout d;
@@ -274,7 +349,13 @@ DecodeLayout decode_layout(const fa_cache *c, int n_slots, int n_head, int max_c
     d.m_off = d.table_bytes;
     d.l_off = d.m_off + align256(d.max_partials * group * sizeof(float));
     d.acc_off = d.l_off + align256(d.max_partials * group * sizeof(float));
-    d.total = d.acc_off + d.max_partials * group * (size_t)c->head_dim * sizeof(float);
+    size_t end = d.acc_off + d.max_partials * group * (size_t)c->head_dim * sizeof(float);
+    d.sh_groups = shadow_groups(c);
+    const size_t sh_rows = nsegs * (size_t)d.sh_groups * group;
+    d.sh_m_off = align256(end);
+    d.sh_l_off = d.sh_m_off + align256(sh_rows * sizeof(float));
+    d.sh_acc_off = d.sh_l_off + align256(sh_rows * sizeof(float));
+    d.total = d.sh_groups ? d.sh_acc_off + sh_rows * (size_t)c->head_dim * sizeof(float) : end;
     return d;
 }
 }  // namespace
@@ -322,8 +403,36 @@ int fa_decode(const fa_cache *cache, const float *q, const int *d_pos, int n_slo
     a.qscale = scale * fa::kLog2e;
     a.kps = fa::kDecodeKps;
     a.cap = fa::kDecodeSplitCap;
-    return hip_rc(fa::launch_decode(cache->format, cache->head_dim, n_head / cache->n_kv_head,
-                                    a, lay.waves, (hipStream_t)stream));
+    a.sh = shadow_args(cache, 0);
+    a.sh_groups = lay.sh_groups;
+    a.sh_m = (float *)(wsb + lay.sh_m_off);
+    a.sh_l = (float *)(wsb + lay.sh_l_off);
+    a.sh_acc = (float *)(wsb + lay.sh_acc_off);
+    const int group = n_head / cache->n_kv_head;
+    if (lay.sh_groups) {
+        fa::ShadowPassArgs sp;
+        sp.q = q;
+        sp.d_pos = d_pos;
+        sp.pos0 = 0;
+        sp.n_q = n_slots;
+        sp.n_head = n_head;
+        sp.n_kv = cache->n_kv_head;
+        sp.max_seq = cache->max_seq;
+        sp.sink = a.sink;
+        sp.win = a.win;
+        sp.qscale = a.qscale;
+        sp.sh = a.sh;
+        sp.chunk_groups = lay.sh_groups;
+        sp.chunks_per_group = 1;
+        sp.m_out = (float *)a.sh_m;
+        sp.l_out = (float *)a.sh_l;
+        sp.acc_out = (float *)a.sh_acc;
+        if ((rc = hip_rc(fa::launch_shadow_pass(cache->head_dim, group, sp,
+                                                n_slots * cache->n_kv_head, (hipStream_t)stream))))
+            return rc;
+    }
+    return hip_rc(fa::launch_decode(cache->format, cache->head_dim, group, a, lay.waves,
+                                    (hipStream_t)stream));
 }
 
 const char *fa_last_hip_error(void) { return hipGetErrorName(g_last_hip_error); }

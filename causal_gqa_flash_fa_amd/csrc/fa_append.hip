@@ -26,7 +26,7 @@ constexpr int kAppendThreads = 256;
 // Cache row (h, position) of input row t and the byte offset of its slot;
 // false when a device position lies outside the cache (nothing is written).
 __device__ __forceinline__ bool dest_row(const AppendArgs &a, int t, int h, int64_t *row,
-                                         size_t *slot_off) {
+                                         size_t *slot_off, int *pos_out) {
     int pos = a.pos0 + t;
     *slot_off = 0;
     if (a.d_pos) {
@@ -35,7 +35,49 @@ __device__ __forceinline__ bool dest_row(const AppendArgs &a, int t, int h, int6
         *slot_off = (size_t)t * a.slot_bytes;
     }
     *row = (int64_t)h * a.max_seq + pos;
+    *pos_out = pos;
     return true;
+}
+
+// fp16 shadow of one 32-element block of row `pos` ([FA] fc_attn_kv_append_q4
+// mirror): the sink copy while pos < sink, the ring copy at row pos % ring
+// size. A range append writes the ring only for its last kShadowWinMax rows,
+// so no two threads of one call write the same ring row; one thread per row
+// records the position the ring row now holds.
+__device__ __forceinline__ void mirror_block(const AppendArgs &a, int tensor, int t, int h,
+                                             int blk, int pos, const float *x) {
+    const ShadowArgs &sh = a.sh;
+    const int slot = a.d_pos ? t : 0;   // a range append's shadow bases are its slot's
+    const size_t hd = (size_t)a.head_dim;
+    u32x4 w[kQ4Block / 8];
+#pragma unroll
+    for (int c = 0; c < kQ4Block / 8; c++) {
+        uint32_t hw[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const uint32_t lo = __builtin_bit_cast(uint16_t, (_Float16)x[8 * c + 2 * i]);
+            const uint32_t hi = __builtin_bit_cast(uint16_t, (_Float16)x[8 * c + 2 * i + 1]);
+            hw[i] = lo | (hi << 16);
+        }
+        w[c] = u32x4{hw[0], hw[1], hw[2], hw[3]};
+    }
+    if (pos < sh.sink) {
+        uint16_t *base = tensor ? sh.v_sink : sh.k_sink;
+        u32x4 *d = (u32x4 *)(base + (((size_t)slot * a.n_kv + h) * kShadowSinkMax + pos) * hd +
+                             blk * kQ4Block);
+#pragma unroll
+        for (int c = 0; c < kQ4Block / 8; c++) d[c] = w[c];
+    }
+    const bool ring = sh.win > 0 && (a.d_pos || pos > a.pos0 + a.n - 1 - kShadowWinMax);
+    if (ring) {
+        uint16_t *base = tensor ? sh.v_win : sh.k_win;
+        const int r = pos % kShadowWinMax;
+        u32x4 *d = (u32x4 *)(base + (((size_t)slot * a.n_kv + h) * kShadowWinMax + r) * hd +
+                             blk * kQ4Block);
+#pragma unroll
+        for (int c = 0; c < kQ4Block / 8; c++) d[c] = w[c];
+        if (tensor == 0 && h == 0 && blk == 0) sh.win_pos[(size_t)slot * kShadowWinMax + r] = pos;
+    }
 }
 
 __global__ __launch_bounds__(kAppendThreads) void append_f32_kernel(AppendArgs a) {
@@ -52,7 +94,8 @@ __global__ __launch_bounds__(kAppendThreads) void append_f32_kernel(AppendArgs a
     const int t = (int)(th / a.n_kv);
     int64_t row;
     size_t slot_off;
-    if (!dest_row(a, t, h, &row, &slot_off)) return;
+    int pos;
+    if (!dest_row(a, t, h, &row, &slot_off, &pos)) return;
     const f32x4 x = *(const f32x4 *)(src + 4 * i);
     float *dst = (float *)(base + slot_off);
     *(f32x4 *)(dst + row * a.head_dim + 4 * c4) = x;
@@ -76,7 +119,8 @@ __global__ __launch_bounds__(kAppendThreads) void append_q4_kernel(AppendArgs a)
     const int t = (int)(th / a.n_kv);
     int64_t row;
     size_t slot_off;
-    if (!dest_row(a, t, h, &row, &slot_off)) return;
+    int pos;
+    if (!dest_row(a, t, h, &row, &slot_off, &pos)) return;
 
     float x[kQ4Block];
     const f32x4 *xs = (const f32x4 *)(src + i * kQ4Block);
@@ -112,6 +156,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_q4_kernel(AppendArgs a)
         const uint32_t b1 = (uint32_t)(c1 | (c17 << 4));
         out[1 + j / 2] = (uint16_t)(b0 | (b1 << 8));   // bytes 2+j, 3+j (little-endian)
     }
+    if (a.sh.sink > 0 || a.sh.win > 0) mirror_block(a, tensor, t, h, blk, pos, x);
 }
 
 }  // namespace

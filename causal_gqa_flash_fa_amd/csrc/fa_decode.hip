@@ -153,6 +153,8 @@ void decode_partial_kernel(DecodeArgs a) {
     auto run_segment = [&](int seg, int it_lo, int it_hi, int pidx) {
         const int slot = seg / a.n_kv, kvh = seg % a.n_kv;
         const int pos = __builtin_amdgcn_readfirstlane(a.pos[slot]);
+        const bool shadowed = a.sh.sink > 0 || a.sh.win > 0;
+        const int *wpos = a.sh.win_pos + (size_t)slot * kShadowWinMax;
         int split_len;
         slot_items(pos, a, &split_len);
         const int L = pos + 1;
@@ -223,7 +225,9 @@ void decode_partial_kernel(DecodeArgs a) {
 #pragma unroll
                         for (int c = 0; c < OD; c++) O[c][hg][i] *= corr;
                     }
-                    const float p = fast_exp2(s - m[h]);
+                    // a masked key adds nothing, also while no key has been seen
+                    // (m = -inf; fp16-shadow keys can mask whole tiles)
+                    const float p = kval ? fast_exp2(s - m[h]) : 0.0f;
                     l[h] += p;
                     Pw[h * PS + pslot] = p;
                 }
@@ -339,7 +343,9 @@ void decode_partial_kernel(DecodeArgs a) {
                 // the next step are read before this step's MFMAs (fenced so
                 // the scheduler keeps them there).
                 const int key = tj + lane;
-                const bool kval = key < k_hi && in_key_set(key, pos, a.sink, a.win);
+                // fp16-shadow keys are folded by the shadow pass, not here
+                const bool kval = key < k_hi && in_key_set(key, pos, a.sink, a.win) &&
+                                  !(shadowed && shadow_key(a.sh, wpos, key, pos));
                 f32x4 sacc2[NHG][2];
 #pragma unroll
                 for (int hg = 0; hg < NHG; hg++) sacc2[hg][0] = sacc2[hg][1] = f32x4{};
@@ -555,6 +561,8 @@ __global__ __launch_bounds__(HD) void decode_combine_kernel(DecodeArgs a) {
     float M = -INFINITY;
 #pragma unroll 8
     for (int r = 0; r < n; r++) M = fmaxf(M, a.ws_m[(size_t)(P + r) * G + g]);
+    for (int c = 0; c < a.sh_groups; c++)   // fp16-shadow partials of the segment
+        M = fmaxf(M, a.sh_m[((size_t)seg * a.sh_groups + c) * G + g]);
     // unrolled so that several partials' loads are in flight at once; the
     // sums still run in ascending partial order
     float o = 0.0f, L = 0.0f;
@@ -564,6 +572,12 @@ __global__ __launch_bounds__(HD) void decode_combine_kernel(DecodeArgs a) {
         const float wgt = fast_exp2(a.ws_m[pi] - M);
         L += a.ws_l[pi] * wgt;
         o += a.ws_acc[pi * HD + dd] * wgt;
+    }
+    for (int c = 0; c < a.sh_groups; c++) {
+        const size_t pi = ((size_t)seg * a.sh_groups + c) * G + g;
+        const float wgt = a.sh_m[pi] == -INFINITY ? 0.0f : fast_exp2(a.sh_m[pi] - M);
+        L += a.sh_l[pi] * wgt;
+        o += a.sh_acc[pi * HD + dd] * wgt;
     }
     a.out[(size_t)gh * HD + dd] = o / L;   // no partial (bad position): 0/0 = NaN
 }

@@ -9,6 +9,44 @@
 
 namespace fa {
 
+// Capacity of the fp16 shadow of a Q4_0 cache (equal to FA_SHADOW_*_MAX).
+constexpr int kShadowSinkMax = 8;
+constexpr int kShadowWinMax = 256;
+
+// fp16 shadow of a Q4_0 cache; sink == win == 0 means none. Buffers hold
+// [n_slots][n_kv][kShadowSinkMax | kShadowWinMax][hd] binary16 values and
+// win_pos [n_slots][kShadowWinMax] the position held by each ring row.
+struct ShadowArgs {
+    uint16_t *k_sink, *v_sink, *k_win, *v_win;
+    int *win_pos;
+    int sink, win;
+};
+
+// Key s of a query at position p is read from the shadow (not the Q4_0
+// body): sink rows always, ring rows while recent and not overwritten.
+__device__ __forceinline__ bool shadow_key(const ShadowArgs &sh, const int *win_pos, int s,
+                                           int p) {
+    if (s < sh.sink) return true;
+    return sh.win > 0 && s > p - sh.win && win_pos[s % kShadowWinMax] == s;
+}
+
+// Shadow pass (fa_shadow.hip): the softmax partial of each query row over its
+// fp16 shadow keys. Work item = (query i, kv head) x chunk group; query i sits
+// at d_pos[i] (decode: one per slot, shadow buffers of slot i) or pos0 + i
+// (prefill: shadow buffers of one slot). Partial of head g of item it, chunk
+// group cg: row (it * chunk_groups + cg) * G + g of m_out, l_out, acc_out.
+struct ShadowPassArgs {
+    const float *q;               // [n_q][n_head][hd]
+    const int *d_pos;             // decode positions, or NULL
+    int pos0, n_q, n_head, n_kv, max_seq;
+    int sink, win;                // key set
+    float qscale;                 // scale * log2(e)
+    ShadowArgs sh;
+    int chunk_groups;             // work-groups per (query, kv head)
+    int chunks_per_group;         // 64-key chunks folded by each
+    float *m_out, *l_out, *acc_out;
+};
+
 struct AppendArgs {
     const float *k_new, *v_new;   // [n][n_kv][hd]
     void *k, *v;                  // slot base of the cache: [n_kv][max_seq][row]
@@ -18,6 +56,7 @@ struct AppendArgs {
     // to position d_pos[t], read on the device; out-of-range positions skip.
     const int *d_pos;
     size_t slot_bytes;
+    ShadowArgs sh;                // Q4_0 only: mirror rows into the fp16 shadow
 };
 
 struct PrefillArgs {
@@ -32,6 +71,11 @@ struct PrefillArgs {
     float qscale;                 // scale * log2(e)
     int n_qblocks;
     int n_wg;                     // work-groups of the stream-K grid
+    // fp16 shadow (Q4_0): buffers of this slot. Its keys are skipped here;
+    // the shadow pass left each row's partial in sh_m, sh_l ([n][n_head]) and
+    // out (acc), and the first piece of every segment starts from it.
+    ShadowArgs sh;
+    const float *sh_m, *sh_l;
 };
 
 struct DecodeArgs {
@@ -46,6 +90,12 @@ struct DecodeArgs {
     int sink, win;
     float qscale;
     int kps, cap;                 // split plan constants
+    // fp16 shadow (Q4_0): buffers of slot 0; its keys are skipped here and
+    // folded by the shadow pass into sh_groups partials per segment, rows
+    // (seg * sh_groups + c) * G + g of sh_m, sh_l, sh_acc.
+    ShadowArgs sh;
+    const float *sh_m, *sh_l, *sh_acc;
+    int sh_groups;
 };
 
 // Geometry of the prefill work-group: 4 waves of 32 (position, head) rows.
@@ -68,6 +118,8 @@ inline int prefill_q_positions(int group) {
 }
 
 hipError_t launch_append(int format, const AppendArgs &a, hipStream_t s);
+hipError_t launch_shadow_pass(int head_dim, int group, const ShadowPassArgs &a, int items,
+                              hipStream_t s);
 hipError_t launch_prefill(int format, int head_dim, int group, const PrefillArgs &a,
                           hipStream_t s);
 hipError_t launch_decode(int format, int head_dim, int group, const DecodeArgs &a, int waves,

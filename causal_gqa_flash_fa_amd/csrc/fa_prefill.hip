@@ -294,6 +294,27 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int n = 0; n < NT; n++) O[n] = f32x16{};
     float m_run = -INFINITY, l_run = 0.0f;
+    // fp16 shadow: one piece per segment (the first) starts from the row's
+    // shadow-key partial, its acc read through the d permutation of the
+    // output stores below
+    // (only a Q4_0 cache has a shadow)
+    const bool shadowed = FMT == 1 && (a.sh.sink > 0 || a.sh.win > 0);
+    if (FMT == 1 && shadowed && first_owner && row_live) {
+        const size_t rf = (size_t)(p_row - a.pos0) * a.n_head + kvh * G + g;
+        const float *sp = a.out + rf * HD;
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+            const int mi = 8 * (r >> 2) + 4 * hlf + (r & 3);
+#pragma unroll
+            for (int ng = 0; ng < NT / GS; ng++) {
+                const float *src = sp + ng * 32 * GS + GS * mi;
+#pragma unroll
+                for (int u = 0; u < GS; u++) O[ng * GS + u][r] = src[u];
+            }
+        }
+        m_run = a.sh_m[rf];
+        l_run = hlf == 0 ? a.sh_l[rf] : 0.0f;
+    }
 
     // ---- staging registers of a Q4_0 tile (fp32 tiles need none)
     // A Q4_0 block (18 bytes) is staged as 5 dwords: from the block start
@@ -407,7 +428,10 @@ void prefill_kernel(PrefillArgs a) {
             kc = kn;
         }
         // every key of the tile is in the key set of every row of the wave
-        const bool full = jc + BK - 1 <= pw0 &&
+        // no key of the tile is an fp16-shadow key for any row of the wave
+        const bool shadow_free =
+            !shadowed || (jc >= a.sh.sink && (a.sh.win <= 0 || jc + BK - 1 <= pw0 - a.sh.win));
+        const bool full = jc + BK - 1 <= pw0 && shadow_free &&
                           (a.win <= 0 || jc + BK - 1 < a.sink || jc >= pw1 - a.win + 1);
         if (!full) {
             // key j is live for this row iff lo_win <= j <= p_row or j < sink_end
@@ -417,7 +441,9 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
             for (int r = 0; r < 16; r++) {
                 const int key = jc + 8 * (r >> 2) + 4 * hlf + (r & 3);
-                const bool ok = (key <= hi_key) & ((key >= lo_win) | (key < sink_end));
+                bool ok = (key <= hi_key) & ((key >= lo_win) | (key < sink_end));
+                if (FMT == 1 && !shadow_free)
+                    ok = ok && !shadow_key(a.sh, a.sh.win_pos, key, p_row);
                 s[r] = ok ? s[r] : -INFINITY;
             }
         }

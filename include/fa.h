@@ -54,10 +54,31 @@ extern "C" {
  * (c - 8) * d. [FA] "4-bit KV cache (Q4_0 blocks)" and fc_kvq4_quant_block. */
 #define FA_KV_Q4_0  1
 
+/* Capacity of the optional fp16 shadow of a Q4_0 cache ([FA] "fp16 sink +
+ * recent-window exemption": the first positions and a ring of recent rows per
+ * (slot, kv head) are also kept at fp16). The ring laps at
+ * FA_SHADOW_WIN_MAX rows whatever the window width. */
+#define FA_SHADOW_SINK_MAX 8
+#define FA_SHADOW_WIN_MAX  256
+
 /* A KV cache of n_slots independent sequences.
  * k and v each hold [n_slots][n_kv_head][max_seq][row] where row is
  * fa_cache_row_bytes(format, head_dim) bytes ([FA] slots section: one ring
- * per slot, each slot's slice laid out like the single-user cache). */
+ * per slot, each slot's slice laid out like the single-user cache).
+ *
+ * fp16 shadow (Q4_0 only; all zero / NULL = none). [FA] "fp16 sink +
+ * recent-window exemption" and fc_kvq4_is_fp16: every appended row also goes,
+ * rounded to binary16 (round-to-nearest-even), to
+ *   k_sink/v_sink [n_slots][n_kv_head][FA_SHADOW_SINK_MAX][head_dim] if its
+ *     position p < shadow_sink;
+ *   k_win/v_win   [n_slots][n_kv_head][FA_SHADOW_WIN_MAX][head_dim] at ring
+ *     row p % FA_SHADOW_WIN_MAX if shadow_win > 0, with win_pos
+ *     [n_slots][FA_SHADOW_WIN_MAX] (int32) recording the position each ring
+ *     row holds (the caller fills win_pos with -1 before first use).
+ * Attention for a query at position p then reads key s from the shadow
+ * instead of the Q4_0 body iff s < shadow_sink, or shadow_win > 0 and
+ * s > p - shadow_win and win_pos holds s (the row was not overwritten by a
+ * later position); otherwise from the Q4_0 body, which holds every row. */
 typedef struct fa_cache {
     int format;      /* FA_KV_F32 or FA_KV_Q4_0 */
     int n_slots;     /* >= 1 */
@@ -66,6 +87,11 @@ typedef struct fa_cache {
     int max_seq;     /* rows per (slot, kv head), >= 1 */
     void *k;         /* device, fa_cache_bytes() bytes */
     void *v;         /* device, fa_cache_bytes() bytes */
+    int shadow_sink; /* 0 .. FA_SHADOW_SINK_MAX */
+    int shadow_win;  /* 0 .. FA_SHADOW_WIN_MAX */
+    void *k_sink, *v_sink;   /* device fp16, required if shadow_sink > 0 */
+    void *k_win, *v_win;     /* device fp16, required if shadow_win > 0 */
+    int *win_pos;            /* device int32, required if shadow_win > 0 */
 } fa_cache;
 
 /* Bytes of one cache row (head_dim*4 for fp32, head_dim/32*18 for Q4_0);
