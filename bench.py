@@ -96,6 +96,8 @@ def prefill_leg(fa, torch, w, steps: int, warmup: int) -> dict:
     kd, vd = torch.from_numpy(k_np).to(dev), torch.from_numpy(v_np).to(dev)
     del k_np, v_np
     cache, kt, vt = fa.make_cache(w.kv_format, 1, w.n_kv_head, w.head_dim, w.max_seq, dev)
+    shadow = fa.add_shadow(cache, w.shadow_sink, w.shadow_win, dev) \
+        if (w.shadow_sink or w.shadow_win) else None   # holds the shadow tensors alive
     out = torch.empty_like(q)
     rows = w.pos0 + w.n
     ws_bytes = fa.fa_prefill_workspace_bytes(w.n, w.n_head, w.n_kv_head, w.head_dim)
@@ -127,6 +129,7 @@ def prefill_leg(fa, torch, w, steps: int, warmup: int) -> dict:
         "workload": w.name, "kind": "prefill", "kv": "q4_0" if w.kv_format else "f32",
         "n": w.n, "n_head": w.n_head, "n_kv_head": w.n_kv_head, "head_dim": w.head_dim,
         "attn_sink": w.attn_sink, "attn_win": w.attn_win,
+        "shadow_sink": w.shadow_sink, "shadow_win": w.shadow_win,
         "flops": flops, "ms_per_step": step_ms, "tflops_step": flops / step_ms / 1e9,
         "prefill_kernel_ms": kern_ms, "prefill_kernel_ms_min": float(np.min(kms)),
         "tflops_kernel": flops / kern_ms / 1e9,
@@ -138,6 +141,8 @@ def decode_leg(fa, torch, w, steps: int, warmup: int) -> dict:
     dev = torch.device("cuda:0")
     ctx = workloads.decode_ctx(w)
     cache, kt, vt = fa.make_cache(w.kv_format, w.n_slots, w.n_kv_head, w.head_dim, w.max_seq, dev)
+    shadow = fa.add_shadow(cache, w.shadow_sink, w.shadow_win, dev) \
+        if (w.shadow_sink or w.shadow_win) else None   # holds the shadow tensors alive
     for s in range(w.n_slots):
         k, v = workloads.decode_kv(w, s, int(ctx[s]))
         fa.fa_kv_append(cache, s, 0, int(ctx[s]), torch.from_numpy(k).to(dev),
@@ -177,6 +182,7 @@ def decode_leg(fa, torch, w, steps: int, warmup: int) -> dict:
         "workload": w.name, "kind": "decode", "kv": "q4_0" if w.kv_format else "f32",
         "n_slots": w.n_slots, "ctx_sum": int(ctx.sum()), "ctx_min": int(ctx.min()),
         "ctx_max": int(ctx.max()), "launch_splits": fa.fa_decode_plan(hint)[0],
+        "shadow_sink": w.shadow_sink, "shadow_win": w.shadow_win,
         "kv_bytes": kv_bytes, "bytes": kv_bytes + qo_bytes, "flops": flops,
         "decode_ms": ms, "decode_ms_min": float(np.min(kms)), "gbs": gbs,
         "frac_hbm_peak": gbs / PEAK_HBM_GBS, "tflops": flops / ms / 1e9,

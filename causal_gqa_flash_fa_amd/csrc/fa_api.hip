@@ -409,8 +409,9 @@ int fa_decode(const fa_cache *cache, const float *q, const int *d_pos, int n_slo
     a.sh_l = (float *)(wsb + lay.sh_l_off);
     a.sh_acc = (float *)(wsb + lay.sh_acc_off);
     const int group = n_head / cache->n_kv_head;
+    a.sh_waves = 0;
     if (lay.sh_groups) {
-        fa::ShadowPassArgs sp;
+        fa::ShadowPassArgs &sp = a.shp;
         sp.q = q;
         sp.d_pos = d_pos;
         sp.pos0 = 0;
@@ -427,9 +428,7 @@ int fa_decode(const fa_cache *cache, const float *q, const int *d_pos, int n_slo
         sp.m_out = (float *)a.sh_m;
         sp.l_out = (float *)a.sh_l;
         sp.acc_out = (float *)a.sh_acc;
-        if ((rc = hip_rc(fa::launch_shadow_pass(cache->head_dim, group, sp,
-                                                n_slots * cache->n_kv_head, (hipStream_t)stream))))
-            return rc;
+        a.sh_waves = n_slots * cache->n_kv_head * lay.sh_groups;   // run inside the partial launch
     }
     return hip_rc(fa::launch_decode(cache->format, cache->head_dim, group, a, lay.waves,
                                     (hipStream_t)stream));

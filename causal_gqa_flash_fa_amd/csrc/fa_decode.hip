@@ -49,6 +49,7 @@
 // softmax, and the bound keeps every exp2(s - m) <= 256.
 #include "fa_device.hpp"
 #include "fa_internal.hpp"
+#include "fa_shadow.hpp"
 
 namespace fa {
 namespace {
@@ -130,8 +131,16 @@ void decode_partial_kernel(DecodeArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t Rw[Sh::TILE_BYTES];
 
     const int lane = threadIdx.x;
-    const int w = blockIdx.x;
-    const int NW = gridDim.x;
+    // fp16-shadow work items first (Q4_0 only), with this work-group's LDS:
+    // they are short and finish while the stream-K waves below run
+    if constexpr (FMT == 1) {
+        if ((int)blockIdx.x < a.sh_waves) {
+            shadow_pass_wave<HD, G>(a.shp, blockIdx.x, Qs, Pw, (int *)Rw);
+            return;
+        }
+    }
+    const int w = blockIdx.x - (FMT == 1 ? a.sh_waves : 0);
+    const int NW = gridDim.x - (FMT == 1 ? a.sh_waves : 0);
     const int nsegs = a.n_slots * a.n_kv;
 
     // ---- pass 1: total number of items
@@ -584,7 +593,8 @@ __global__ __launch_bounds__(HD) void decode_combine_kernel(DecodeArgs a) {
 
 template <int HD, int G, int FMT>
 hipError_t launch_one(const DecodeArgs &a, int waves, hipStream_t s) {
-    hipLaunchKernelGGL((decode_partial_kernel<HD, G, FMT>), dim3(waves), dim3(64), 0, s, a);
+    hipLaunchKernelGGL((decode_partial_kernel<HD, G, FMT>), dim3(waves + a.sh_waves), dim3(64), 0,
+                       s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((decode_combine_kernel<HD, G>), dim3(a.n_slots * a.n_head), dim3(HD), 0, s,

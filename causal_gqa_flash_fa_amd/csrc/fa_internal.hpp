@@ -96,6 +96,10 @@ struct DecodeArgs {
     ShadowArgs sh;
     const float *sh_m, *sh_l, *sh_acc;
     int sh_groups;
+    // The shadow pass's work items run as the first sh_waves work-groups of
+    // the partial launch (shp.m_out/l_out/acc_out = sh_m/sh_l/sh_acc).
+    ShadowPassArgs shp;
+    int sh_waves;
 };
 
 // Geometry of the prefill work-group: 4 waves of 32 (position, head) rows.

@@ -181,3 +181,64 @@ def test_shadow_changes_the_result_only_where_it_should():
         del bufs
     assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
     assert np.abs(outs[2] - outs[0]).max() > 1e-3
+
+
+def test_prefill_workload_with_shadow():
+    import workloads
+    w = workloads.BY_NAME["prefill-q4kv-8k-shadow"]
+    q = workloads.prefill_q(w)
+    k, v = workloads.prefill_kv(w)
+    U.log(f"workload {w.name}: n={w.n}, shadow ({w.shadow_sink}, {w.shadow_win})")
+    cache, kt, vt = fa.make_cache(w.kv_format, 1, w.n_kv_head, w.head_dim, w.max_seq, U.device())
+    bufs = fa.add_shadow(cache, w.shadow_sink, w.shadow_win, U.device())
+    fa.fa_kv_append(cache, 0, 0, w.n, U.to_dev(k), U.to_dev(v))
+    ws_bytes = fa.fa_prefill_workspace_bytes(w.n, w.n_head, w.n_kv_head, w.head_dim)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=U.device())
+    out = torch.full((w.n, w.n_head, w.head_dim), float("nan"), device=U.device())
+    fa.fa_prefill(cache, 0, U.to_dev(q), 0, w.n, w.n_head, 0, 0, w.scale, out, ws, ws_bytes)
+    torch.cuda.synchronize()
+    gpu = out.cpu().numpy()
+    assert np.all(np.isfinite(gpu))
+    rng = np.random.Generator(np.random.PCG64(w.index))
+    pos = U.sample_positions(w.n, rng, extra=(255, 256, 257, w.n - 257, w.n - 256), count=24)
+    sel = (pos[:, None] * w.n_head + np.arange(w.n_head)[None, :]).reshape(-1)
+    kq, vq = U.oracle_kv(1, k, w.head_dim), U.oracle_kv(1, v, w.head_dim)
+    k16 = oracle.f16_round(np.ascontiguousarray(k.transpose(1, 0, 2)))
+    v16 = oracle.f16_round(np.ascontiguousarray(v.transpose(1, 0, 2)))
+    ref = oracle.gqa_rows_shadow(q, np.arange(w.n, dtype=np.int32), kq, vq, k16, v16, 0, 0,
+                                 w.scale, w.shadow_sink, w.shadow_win, w.n - 1 - RING, sel=sel,
+                                 threads=U.ORACLE_THREADS)
+    U.compare_rows(gpu.reshape(-1, w.head_dim)[sel], ref, U.TOL_Q4, w.name)
+    del bufs
+
+
+def test_decode_workload_with_shadow():
+    import workloads
+    w = workloads.BY_NAME["decode-64slots-q4kv-shadow"]
+    ctx = workloads.decode_ctx(w)
+    q = workloads.decode_q(w)
+    U.log(f"workload {w.name}: {w.n_slots} slots, shadow ({w.shadow_sink}, {w.shadow_win})")
+    cache, kt, vt = fa.make_cache(w.kv_format, w.n_slots, w.n_kv_head, w.head_dim, w.max_seq,
+                                  U.device())
+    bufs = fa.add_shadow(cache, w.shadow_sink, w.shadow_win, U.device())
+    check = sorted({int(np.argmin(ctx)), int(np.argmax(ctx)), 7, 40})
+    kept = {}
+    for s in range(w.n_slots):
+        k, v = workloads.decode_kv(w, s, int(ctx[s]))
+        fa.fa_kv_append(cache, s, 0, int(ctx[s]), U.to_dev(k), U.to_dev(v))
+        if s in check:
+            kept[s] = (k, v)
+    hint = int(ctx.max())
+    ws_bytes = fa.fa_decode_workspace_bytes(cache, w.n_slots, w.n_head, hint)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=U.device())
+    out = torch.full((w.n_slots, w.n_head, w.head_dim), float("nan"), device=U.device())
+    fa.fa_decode(cache, U.to_dev(q), U.to_dev(ctx - 1), w.n_slots, hint, w.n_head, 0, 0, w.scale,
+                 out, ws, ws_bytes)
+    torch.cuda.synchronize()
+    gpu = out.cpu().numpy()
+    assert np.all(np.isfinite(gpu))
+    ref = np.stack([shadow_reference(q[s:s + 1], [ctx[s] - 1], kept[s][0], kept[s][1],
+                                     w.head_dim, 0, 0, w.scale, w.shadow_sink, w.shadow_win,
+                                     int(ctx[s]) - 1) for s in check])
+    U.compare_rows(gpu[check], ref.reshape(len(check), w.n_head, w.head_dim), U.TOL_Q4, w.name)
+    del bufs

@@ -44,6 +44,8 @@ class Workload:
     n_slots: int = 1      # decode: sequence slots
     ctx_lo: int = 0       # decode: context length range, inclusive
     ctx_hi: int = 0
+    shadow_sink: int = 0  # Q4_0: fp16 shadow of the first positions ...
+    shadow_win: int = 0   # ... and of the recent window (0, 0: no shadow)
 
     @property
     def group(self) -> int:
@@ -63,7 +65,16 @@ WORKLOADS = [
     Workload(4, "decode-64slots-q4kv", "decode", 16, 2, 256, KV_Q4_0, n_slots=64,
              ctx_lo=4096, ctx_hi=32768, max_seq=32768),
 ]
-BY_NAME = {w.name: w for w in WORKLOADS}
+# The Q4_0 workloads again with the fp16 sink + recent-window shadow (the
+# Foundry page's 4-position sink and its 256-row window ring), on the same
+# seeded inputs (same index).
+SHADOW_WORKLOADS = [
+    dataclasses.replace(WORKLOADS[2], name="prefill-q4kv-8k-shadow", shadow_sink=4,
+                        shadow_win=256),
+    dataclasses.replace(WORKLOADS[4], name="decode-64slots-q4kv-shadow", shadow_sink=4,
+                        shadow_win=256),
+]
+BY_NAME = {w.name: w for w in WORKLOADS + SHADOW_WORKLOADS}
 
 
 def _rng(seed: int) -> np.random.Generator:
