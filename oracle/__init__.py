@@ -60,6 +60,8 @@ def lib() -> ctypes.CDLL:
         L.oracle_gqa_rows_shadow.argtypes = [P, P, i32, P, P, P, P, i32, i32, i32, i32, i32,
                                              i32, dbl, i32, i32, i32, P, i64, P]
         L.oracle_gqa_rows_shadow.restype = i32
+        L.oracle_gqa_lse.argtypes = [P, P, i32, P, i32, i32, i32, i32, i32, i32, dbl, P, i64, P]
+        L.oracle_gqa_lse.restype = i32
         L.oracle_decode_plan.argtypes = [i32, i32, i32, i32, P, P]
         L.oracle_decode_plan.restype = i32
         L.oracle_tile_walk.argtypes = [i32, i32, i32, i32, i32, i32, i32, P, P]
@@ -201,6 +203,65 @@ def gqa_rows_shadow(q: np.ndarray, q_pos, k: np.ndarray, v: np.ndarray, k16: np.
         with concurrent.futures.ThreadPoolExecutor(threads) as ex:
             list(ex.map(lambda i: run(bounds[i], bounds[i + 1]), range(threads)))
     return out
+
+
+def gqa_lse(q: np.ndarray, q_pos, k: np.ndarray, attn_sink: int, attn_win: int, scale: float,
+            sel=None) -> np.ndarray:
+    """Natural-log log-sum-exp of each row's scaled scores over its key set,
+    float64 [len(sel)] (all n_q * n_head rows by default, flat index qi*H + h)."""
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    k = np.ascontiguousarray(k, dtype=np.float32)
+    q_pos = np.ascontiguousarray(q_pos, dtype=np.int32)
+    n_q, n_head, hd = q.shape
+    n_kv, kv_rows, _ = k.shape
+    if sel is None:
+        sel = np.arange(n_q * n_head, dtype=np.int64)
+    sel = np.ascontiguousarray(sel, dtype=np.int64)
+    out = np.empty(sel.size, dtype=np.float64)
+    rc = lib().oracle_gqa_lse(_ptr(q), _ptr(q_pos), n_q, _ptr(k), kv_rows, n_head, n_kv, hd,
+                              attn_sink, attn_win, float(scale), _ptr(sel), sel.size,
+                              out.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle_gqa_lse rejected its arguments")
+    return out
+
+
+def paged_rows(cache: np.ndarray, block_row, seq_len: int) -> np.ndarray:
+    """Contiguous [n_kv][seq_len][hd] rows of one request from a paged cache
+    [num_blocks][block_size][n_kv][hd] ([VT] PagedAttention): key position j
+    lives in block block_row[j // block_size] at offset j % block_size."""
+    bs = cache.shape[1]
+    j = np.arange(seq_len)
+    blocks = np.asarray(block_row)[j // bs]
+    return np.ascontiguousarray(cache[blocks, j % bs].transpose(1, 0, 2))
+
+
+def merge_attn_states(prefix_out, prefix_lse, suffix_out, suffix_lse,
+                      prefill_tokens_with_context: int = -1):
+    """[VT] MergeAttnStates on float64 arrays: outputs [T][H][D], lse [H][T].
+    Two results over disjoint key sets combine by their log-sum-exps; +inf LSE
+    counts as -inf; if both are -inf the prefix output and -inf are kept;
+    tokens at index >= prefill_tokens_with_context (when >= 0) take the suffix
+    verbatim."""
+    po, so = np.asarray(prefix_out, np.float64), np.asarray(suffix_out, np.float64)
+    pl = np.where(np.isposinf(prefix_lse), -np.inf, np.asarray(prefix_lse, np.float64))
+    sl = np.where(np.isposinf(suffix_lse), -np.inf, np.asarray(suffix_lse, np.float64))
+    T, H, D = po.shape
+    out, lse = np.empty_like(po), np.empty((H, T))
+    for t in range(T):
+        for h in range(H):
+            if 0 <= prefill_tokens_with_context <= t:
+                out[t, h], lse[h, t] = so[t, h], sl[h, t]
+                continue
+            a, b = pl[h, t], sl[h, t]
+            if a == -np.inf and b == -np.inf:
+                out[t, h], lse[h, t] = po[t, h], -np.inf
+                continue
+            m = max(a, b)
+            pa, pb = np.exp(a - m), np.exp(b - m)
+            out[t, h] = po[t, h] * (pa / (pa + pb)) + so[t, h] * (pb / (pa + pb))
+            lse[h, t] = np.log(pa + pb) + m
+    return out, lse
 
 
 def prefill(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, pos0: int,

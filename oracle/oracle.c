@@ -306,6 +306,51 @@ int oracle_gqa_rows_shadow(const float *q, const int *q_pos, int n_q,
     return 0;
 }
 
+int oracle_gqa_lse(const float *q, const int *q_pos, int n_q,
+                   const float *k, int kv_rows, int n_head, int n_kv_head, int head_dim,
+                   int attn_sink, int attn_win, double scale,
+                   const int64_t *sel, int64_t n_sel, double *lse)
+{
+    if (n_q < 0 || n_head <= 0 || n_kv_head <= 0 || head_dim <= 0 ||
+        n_head % n_kv_head != 0)
+        return -1;
+    const int group = n_head / n_kv_head;
+    const int64_t total = sel ? n_sel : (int64_t)n_q * n_head;
+    for (int i = 0; i < n_q; i++)
+        if (q_pos[i] < 0 || q_pos[i] >= kv_rows)
+            return -1;
+    for (int64_t r = 0; r < total; r++) {
+        const int64_t flat = sel ? sel[r] : r;
+        if (flat < 0 || flat >= (int64_t)n_q * n_head)
+            return -1;
+        const int p = q_pos[flat / n_head];
+        const float *qv = q + (size_t)flat * head_dim;
+        const float *kb = k + (size_t)((flat % n_head) / group) * kv_rows * head_dim;
+        /* max first, then ln sum exp(s - max) + max */
+        double m = -INFINITY;
+        for (int j = 0; j <= p; j++) {
+            if (!oracle_key_in_set(j, p, attn_sink, attn_win))
+                continue;
+            double dot = 0.0;
+            for (int e = 0; e < head_dim; e++)
+                dot += (double)qv[e] * (double)kb[(size_t)j * head_dim + e];
+            if (scale * dot > m)
+                m = scale * dot;
+        }
+        double sum = 0.0;
+        for (int j = 0; j <= p; j++) {
+            if (!oracle_key_in_set(j, p, attn_sink, attn_win))
+                continue;
+            double dot = 0.0;
+            for (int e = 0; e < head_dim; e++)
+                dot += (double)qv[e] * (double)kb[(size_t)j * head_dim + e];
+            sum += exp(scale * dot - m);
+        }
+        lse[r] = m + log(sum);
+    }
+    return 0;
+}
+
 int oracle_decode_plan(int seq_len, int kps, int cap, int tile,
                        int *n_splits, int *split_len)
 {

@@ -87,6 +87,14 @@ int oracle_gqa_rows_shadow(const float *q, const int *q_pos, int n_q,
                            int shadow_sink, int shadow_win, int live_lo,
                            const int64_t *sel, int64_t n_sel, double *out);
 
+/* Log-sum-exp of each row's scaled scores over its key set (natural log):
+ * lse = ln sum_j exp(scale * q.k_j), the state [VT] MergeAttnStates combines.
+ * Same arguments and row selection as oracle_gqa_rows; lse[r] per row. */
+int oracle_gqa_lse(const float *q, const int *q_pos, int n_q,
+                   const float *k, int kv_rows, int n_head, int n_kv_head, int head_dim,
+                   int attn_sink, int attn_win, double scale,
+                   const int64_t *sel, int64_t n_sel, double *lse);
+
 /* Decode split plan. [FA] fc_attn_dec_plan: n = clamp(ceil(L/kps), 1, cap);
  * split_len = ceil(L/n) rounded up to a multiple of `tile`; returns the live
  * split count ceil(L/split_len). */
