@@ -32,6 +32,7 @@ EXPORTS = [
     "fa_prefill",
     "fa_prefill_tile_shape", "fa_prefill_workspace_bytes", "fa_decode_plan", "fa_decode_plan_params",
     "fa_decode_workspace_bytes", "fa_decode", "fa_strerror", "fa_last_hip_error",
+    "fa_paged_append", "fa_paged_workspace_bytes", "fa_paged_attention", "fa_merge_attn_states",
 ]
 
 
@@ -48,6 +49,14 @@ class fa_cache(ctypes.Structure):
                 ("k_sink", ctypes.c_void_p), ("v_sink", ctypes.c_void_p),
                 ("k_win", ctypes.c_void_p), ("v_win", ctypes.c_void_p),
                 ("win_pos", ctypes.c_void_p)]
+
+
+class fa_paged_cache(ctypes.Structure):
+    """Mirror of `struct fa_paged_cache` in include/fa.h."""
+    _fields_ = [("num_blocks", ctypes.c_int), ("block_size", ctypes.c_int),
+                ("n_kv_head", ctypes.c_int), ("head_dim", ctypes.c_int),
+                ("block_stride", ctypes.c_longlong),
+                ("k", ctypes.c_void_p), ("v", ctypes.c_void_p)]
 
 
 class FaError(RuntimeError):
@@ -98,6 +107,15 @@ def _load() -> ctypes.CDLL:
     L.fa_decode_workspace_bytes.restype = Z
     L.fa_decode.argtypes = [C, P, P, I, I, I, I, I, F, P, P, Z, P, P]
     L.fa_decode.restype = I
+    PC = ctypes.POINTER(fa_paged_cache)
+    L.fa_paged_append.argtypes = [PC, P, P, P, I, P]
+    L.fa_paged_append.restype = I
+    L.fa_paged_workspace_bytes.argtypes = [I]
+    L.fa_paged_workspace_bytes.restype = Z
+    L.fa_paged_attention.argtypes = [PC, P, I, I, P, P, I, P, I, I, I, F, P, P, P, Z, P]
+    L.fa_paged_attention.restype = I
+    L.fa_merge_attn_states.argtypes = [P, P, P, P, P, P, I, I, I, I, P]
+    L.fa_merge_attn_states.restype = I
     L.fa_strerror.argtypes = [I]
     L.fa_strerror.restype = ctypes.c_char_p
     return L
@@ -240,3 +258,57 @@ def add_shadow(cache: fa_cache, sink: int, win: int, device="cuda"):
     cache.k_win, cache.v_win = kw.data_ptr(), vw.data_ptr()
     cache.win_pos = wp.data_ptr()
     return ks, vs, kw, vw, wp
+
+
+def fa_paged_append(cache: fa_paged_cache, k, v, slot_mapping, num_slots: int,
+                    stream=None) -> None:
+    _check(lib.fa_paged_append(ctypes.byref(cache), _ptr(k), _ptr(v), _ptr(slot_mapping),
+                               num_slots, _stream(stream)), "fa_paged_append")
+
+
+def fa_paged_workspace_bytes(head_dim: int) -> int:
+    return lib.fa_paged_workspace_bytes(head_dim)
+
+
+def fa_paged_attention(cache: fa_paged_cache, q, num_tokens: int, n_head: int,
+                       query_start_loc, seq_lens, num_reqs: int, block_table,
+                       max_blocks_per_seq: int, window_left: int, window_right: int,
+                       scale: float, out, lse, ws, ws_bytes: int, stream=None) -> None:
+    _check(lib.fa_paged_attention(ctypes.byref(cache), _ptr(q), num_tokens, n_head,
+                                  _ptr(query_start_loc), _ptr(seq_lens), num_reqs,
+                                  _ptr(block_table), max_blocks_per_seq, window_left,
+                                  window_right, scale, _ptr(out), _ptr(lse), _ptr(ws), ws_bytes,
+                                  _stream(stream)), "fa_paged_attention")
+
+
+def fa_merge_attn_states(out, out_lse, prefix_out, prefix_lse, suffix_out, suffix_lse,
+                         num_tokens: int, n_head: int, head_dim: int,
+                         prefill_tokens_with_context: int = -1, stream=None) -> None:
+    _check(lib.fa_merge_attn_states(_ptr(out), _ptr(out_lse), _ptr(prefix_out),
+                                    _ptr(prefix_lse), _ptr(suffix_out), _ptr(suffix_lse),
+                                    num_tokens, n_head, head_dim, prefill_tokens_with_context,
+                                    _stream(stream)), "fa_merge_attn_states")
+
+
+def make_paged_cache(num_blocks: int, block_size: int, n_kv_head: int, head_dim: int,
+                     device="cuda", interleaved: bool = False):
+    """Allocate a paged fp32 cache with torch and describe it.
+
+    interleaved=False: separate k and v tensors [num_blocks][block_size][n_kv][hd].
+    interleaved=True: one [num_blocks][2][block_size][n_kv][hd] tensor whose two
+    halves are k and v (block stride 2 * block_size * n_kv * hd).
+    Returns (fa_paged_cache, k_view, v_view), the views shaped
+    [num_blocks][block_size][n_kv][hd]; keep them alive as long as the struct is used.
+    """
+    import torch
+    shape = (num_blocks, block_size, n_kv_head, head_dim)
+    if interleaved:
+        kv = torch.empty((num_blocks, 2) + shape[1:], dtype=torch.float32, device=device)
+        k, v = kv[:, 0], kv[:, 1]
+        stride = 2 * block_size * n_kv_head * head_dim
+    else:
+        k = torch.empty(shape, dtype=torch.float32, device=device)
+        v = torch.empty(shape, dtype=torch.float32, device=device)
+        stride = 0
+    return fa_paged_cache(num_blocks, block_size, n_kv_head, head_dim, stride, k.data_ptr(),
+                          v.data_ptr()), k, v

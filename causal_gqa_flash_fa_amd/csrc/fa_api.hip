@@ -174,7 +174,7 @@ int fa_prefill_tile_shape(int n_head, int n_kv_head, int head_dim, int *q_positi
 }
 
 namespace {
-// Stream-K prefill layout: pieces of cut segments and the segment table.
+// Stream-K prefill layout: the list of cut segments and their pieces.
 struct PrefillLayout {
     int n_qblocks;
     size_t pieces, table_bytes, m_off, l_off, acc_off;
@@ -186,11 +186,11 @@ PrefillLayout prefill_layout(int n, int n_head, int n_kv_head, int head_dim) {
     PrefillLayout p;
     const int bq = fa::prefill_q_positions(n_head / n_kv_head);
     const size_t rows = (size_t)fa::kPrefillWaves * fa::kPrefillRowsPerWave;
+    (void)n_kv_head;
     p.n_qblocks = (n + bq - 1) / bq;
-    const size_t nsegs = (size_t)n_kv_head * p.n_qblocks;
     // cut segments own at most 2 * (work-groups - 1) pieces in total
     p.pieces = 2 * (size_t)fa::kPrefillMaxWorkGroups;
-    p.table_bytes = align256(nsegs * 2 * sizeof(int));
+    p.table_bytes = align256(sizeof(fa::CutList));
     p.m_off = p.table_bytes;
     p.l_off = p.m_off + align256(p.pieces * rows * sizeof(float));
     p.acc_off = p.l_off + align256(p.pieces * rows * sizeof(float));
@@ -255,13 +255,14 @@ int fa_prefill(const fa_cache *cache, int slot, const float *q, int pos0, int n,
     if (tiles < n_wg) n_wg = tiles;
     if (n_wg < 1) n_wg = 1;
     uint8_t *wsb = (uint8_t *)ws;
-    fa::PrefillArgs a;
+    fa::PrefillArgs a{};
     a.q = q;
     a.out = out;
+    a.lse = nullptr;
     a.k = (const uint8_t *)cache->k + (size_t)slot * slot_stride_bytes(cache);
     a.v = (const uint8_t *)cache->v + (size_t)slot * slot_stride_bytes(cache);
     a.stats = tile_stats;
-    a.seg_table = (int *)wsb;
+    a.cuts = (fa::CutList *)wsb;
     a.ws_m = (float *)(wsb + lay.m_off);
     a.ws_l = (float *)(wsb + lay.l_off);
     a.ws_acc = (float *)(wsb + lay.acc_off);
@@ -432,6 +433,158 @@ int fa_decode(const fa_cache *cache, const float *q, const int *d_pos, int n_slo
     }
     return hip_rc(fa::launch_decode(cache->format, cache->head_dim, group, a, lay.waves,
                                     (hipStream_t)stream));
+}
+
+// ---------------------------------------------------------------- paged
+namespace {
+int check_paged_cache(const fa_paged_cache *c) {
+    if (!c) return FA_ENULL;
+    if (!dim_ok(c->head_dim)) return FA_EUNSUPPORTED;
+    if (c->num_blocks < 1 || c->block_size < 1 || c->n_kv_head < 1) return FA_EINVAL;
+    if (!c->k || !c->v) return FA_ENULL;
+    const long long page = (long long)c->block_size * c->n_kv_head * c->head_dim;
+    if (c->block_stride != 0 && (c->block_stride < page || c->block_stride % 4 != 0))
+        return FA_EINVAL;
+    if (((uintptr_t)c->k | (uintptr_t)c->v) % 16 != 0) return FA_EINVAL;
+    return FA_OK;
+}
+
+long long paged_block_stride(const fa_paged_cache *c) {
+    return c->block_stride ? c->block_stride
+                           : (long long)c->block_size * c->n_kv_head * c->head_dim;
+}
+
+struct PagedLayout {
+    size_t table_bytes, m_off, l_off, acc_off, total;
+};
+
+PagedLayout paged_layout(int head_dim) {
+    PagedLayout p;
+    const size_t rows = (size_t)fa::kPrefillWaves * fa::kPrefillRowsPerWave;
+    const size_t pieces = 2 * (size_t)fa::kPrefillMaxWorkGroups;
+    p.table_bytes = align256(sizeof(fa::CutList));
+    p.m_off = p.table_bytes;
+    p.l_off = p.m_off + align256(pieces * rows * sizeof(float));
+    p.acc_off = p.l_off + align256(pieces * rows * sizeof(float));
+    p.total = p.acc_off + pieces * rows * (size_t)head_dim * sizeof(float);
+    return p;
+}
+}  // namespace
+
+int fa_paged_append(const fa_paged_cache *cache, const float *k, const float *v,
+                    const int64_t *slot_mapping, int num_slots, void *stream) {
+    int rc = check_paged_cache(cache);
+    if (rc) return rc;
+    if (num_slots < 0) return FA_EINVAL;
+    if (num_slots == 0) return FA_OK;
+    if (!k || !v || !slot_mapping) return FA_ENULL;
+    if (((uintptr_t)k | (uintptr_t)v) % 16 != 0) return FA_EINVAL;
+    if ((rc = fa_init())) return rc;
+    fa::PagedAppendArgs a;
+    a.k_new = k;
+    a.v_new = v;
+    a.k = cache->k;
+    a.v = cache->v;
+    a.slot_mapping = (const long long *)slot_mapping;
+    a.n = num_slots;
+    a.n_kv = cache->n_kv_head;
+    a.head_dim = cache->head_dim;
+    a.block_size = cache->block_size;
+    a.num_blocks = cache->num_blocks;
+    a.blk_stride = paged_block_stride(cache);
+    return hip_rc(fa::launch_paged_append(a, (hipStream_t)stream));
+}
+
+size_t fa_paged_workspace_bytes(int head_dim) {
+    if (!dim_ok(head_dim)) return 0;
+    return paged_layout(head_dim).total;
+}
+
+int fa_paged_attention(const fa_paged_cache *cache, const float *q, int num_tokens, int n_head,
+                       const int *query_start_loc, const int *seq_lens, int num_reqs,
+                       const int *block_table, int max_blocks_per_seq, int window_left,
+                       int window_right, float scale, float *out, float *lse, void *ws,
+                       size_t ws_bytes, void *stream) {
+    int rc = check_paged_cache(cache);
+    if (rc) return rc;
+    if (n_head < 1 || n_head % cache->n_kv_head != 0) return FA_EINVAL;
+    if (!group_ok(n_head / cache->n_kv_head)) return FA_EUNSUPPORTED;
+    if ((rc = check_scale(scale))) return rc;
+    if (num_tokens < 0 || num_reqs < 0 || num_reqs > fa::kPagedMaxReqs) return FA_EINVAL;
+    if (max_blocks_per_seq < 1 ||
+        (long long)max_blocks_per_seq * cache->block_size > 0x7fffffffLL)
+        return FA_EINVAL;
+    if (window_left >= 0 && window_right < 0) return FA_EINVAL;
+    if (num_tokens == 0 || num_reqs == 0) return FA_OK;
+    if (!q || !out || !query_start_loc || !seq_lens || !block_table || !ws) return FA_ENULL;
+    if (((uintptr_t)q | (uintptr_t)out) % 16 != 0) return FA_EINVAL;
+    const PagedLayout lay = paged_layout(cache->head_dim);
+    if (ws_bytes < lay.total) return FA_EWORKSPACE;
+    if ((rc = fa_init())) return rc;
+    int dev = 0;
+    if (hip_rc(hipGetDevice(&dev))) return FA_EHIP;
+    uint8_t *wsb = (uint8_t *)ws;
+    fa::PrefillArgs a{};
+    a.q = q;
+    a.out = out;
+    a.lse = lse;
+    a.k = cache->k;
+    a.v = cache->v;
+    a.stats = nullptr;
+    a.cuts = (fa::CutList *)wsb;
+    a.ws_m = (float *)(wsb + lay.m_off);
+    a.ws_l = (float *)(wsb + lay.l_off);
+    a.ws_acc = (float *)(wsb + lay.acc_off);
+    a.n = num_tokens;
+    a.pos0 = 0;
+    a.n_head = n_head;
+    a.n_kv = cache->n_kv_head;
+    a.max_seq = 0;
+    // causal window (left, right): keys [p - left, p]; right adds nothing
+    // under the causal bound. A window wider than any context is none.
+    const long long cap = (long long)max_blocks_per_seq * cache->block_size;
+    a.sink = 0;
+    a.win = window_left < 0 || window_left >= cap ? 0 : window_left + 1;
+    a.qscale = scale * fa::kLog2e;
+    a.n_qblocks = 1;
+    a.n_wg = g_device_cus[dev] < fa::kPrefillMaxWorkGroups ? g_device_cus[dev]
+                                                           : fa::kPrefillMaxWorkGroups;
+    a.qsl = query_start_loc;
+    a.seq_lens = seq_lens;
+    a.block_table = block_table;
+    a.n_req = num_reqs;
+    a.bt_stride = max_blocks_per_seq;
+    a.block_size = cache->block_size;
+    a.num_blocks = cache->num_blocks;
+    a.blk_stride = paged_block_stride(cache);
+    return hip_rc(fa::launch_paged_prefill(cache->head_dim, n_head / cache->n_kv_head, a,
+                                           (hipStream_t)stream));
+}
+
+int fa_merge_attn_states(float *out, float *out_lse, const float *prefix_out,
+                         const float *prefix_lse, const float *suffix_out,
+                         const float *suffix_lse, int num_tokens, int n_head, int head_dim,
+                         int prefill_tokens_with_context, void *stream) {
+    if (num_tokens < 0 || n_head < 1 || head_dim < 4 || head_dim % 4 != 0 || head_dim > 4096)
+        return FA_EINVAL;
+    if (num_tokens == 0) return FA_OK;
+    if (!out || !prefix_out || !prefix_lse || !suffix_out || !suffix_lse) return FA_ENULL;
+    if (((uintptr_t)out | (uintptr_t)prefix_out | (uintptr_t)suffix_out) % 16 != 0)
+        return FA_EINVAL;
+    int rc;
+    if ((rc = fa_init())) return rc;
+    fa::MergeArgs a;
+    a.out = out;
+    a.out_lse = out_lse;
+    a.p_out = prefix_out;
+    a.p_lse = prefix_lse;
+    a.s_out = suffix_out;
+    a.s_lse = suffix_lse;
+    a.T = num_tokens;
+    a.H = n_head;
+    a.D = head_dim;
+    a.prefill_tokens_with_context = prefill_tokens_with_context;
+    return hip_rc(fa::launch_merge(a, (hipStream_t)stream));
 }
 
 const char *fa_last_hip_error(void) { return hipGetErrorName(g_last_hip_error); }

@@ -25,6 +25,7 @@ __host__ __device__ constexpr int q4_row_bytes(int head_dim) {
 // log2(e): scores are kept in base-2 units (s * log2 e) so the softmax
 // exponentials are single v_exp_f32 instructions.
 constexpr float kLog2e = 1.44269504088896340736f;
+constexpr float kLn2 = 0.69314718055994530942f;
 
 __device__ __forceinline__ float half_bits_to_float(uint32_t bits) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)(bits & 0xffffu));

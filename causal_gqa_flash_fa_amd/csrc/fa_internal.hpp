@@ -59,18 +59,59 @@ struct AppendArgs {
     ShadowArgs sh;                // Q4_0 only: mirror rows into the fp16 shadow
 };
 
+// Geometry of the prefill work-group: 4 waves of 32 (position, head) rows.
+constexpr int kPrefillWaves = 4;
+constexpr int kPrefillRowsPerWave = 32;
+constexpr int kPrefillKeyTile = 32;
+// Stream-K prefill grid: at most one work-group per CU of a 256-CU MI355X.
+constexpr int kPrefillMaxWorkGroups = 256;
+// Decode: single-wave work-groups folding tiles of 64 keys (one per lane).
+constexpr int kDecodeKeyTile = 64;
+// Split plan constants: about kDecodeKps keys per split, at most
+// kDecodeSplitCap splits per slot. Splits are the schedulable work items.
+constexpr int kDecodeKps = 128;
+constexpr int kDecodeSplitCap = 512;
+// Work-groups of the decode partial pass: 8 waves per CU of a 256-CU MI355X.
+constexpr int kDecodeMaxWaves = 2048;
+
+// Requests of one paged prefill launch (their table sits in LDS).
+constexpr int kPagedMaxReqs = 1024;
+
+// A query block cut between work-groups: its pieces and where its rows go
+// (position p of the block is query token p + tok). Filled by the prefill
+// kernel, read by its combine launch.
+struct CutSeg {
+    int piece0, n_pieces, q0, q1, kvh, tok, pad0, pad1;
+};
+// Cut segments of one prefill launch: every cut sits at a run boundary, so
+// there are fewer than kPrefillMaxWorkGroups of them.
+struct CutList {
+    int count;
+    int pad[7];
+    CutSeg seg[kPrefillMaxWorkGroups];
+};
+
 struct PrefillArgs {
     const float *q;               // [n][n_head][hd]
     float *out;                   // [n][n_head][hd]
-    const void *k, *v;            // slot base: [n_kv][max_seq][row]
+    float *lse;                   // NULL or [n_head][n]: ln sum_j exp(scale q.k_j)
+    const void *k, *v;            // slot base: [n_kv][max_seq][row]; paged: page 0
     unsigned long long *stats;    // NULL or [2]
     float *ws_m, *ws_l, *ws_acc;  // pieces of cut segments: [piece][rows](+[hd])
-    int *seg_table;               // [n_kv * n_qblocks][2]: first piece, piece count
+    CutList *cuts;
     int n, pos0, n_head, n_kv, max_seq;
     int sink, win;
     float qscale;                 // scale * log2(e)
     int n_qblocks;
     int n_wg;                     // work-groups of the stream-K grid
+    // Paged varlen batch (paged instances; n = total query tokens): request
+    // r holds query tokens [qsl[r], qsl[r+1]) at positions
+    // seq_lens[r] - qlen_r + i, and its key row j sits in page
+    // block_table[r * bt_stride + j / block_size], row j % block_size, at
+    // float page * blk_stride + (row * n_kv + kv head) * hd of k / v.
+    const int *qsl, *seq_lens, *block_table;
+    int n_req, bt_stride, block_size, num_blocks;
+    long long blk_stride;
     // fp16 shadow (Q4_0): buffers of this slot. Its keys are skipped here;
     // the shadow pass left each row's partial in sh_m, sh_l ([n][n_head]) and
     // out (acc), and the first piece of every segment starts from it.
@@ -102,21 +143,6 @@ struct DecodeArgs {
     int sh_waves;
 };
 
-// Geometry of the prefill work-group: 4 waves of 32 (position, head) rows.
-constexpr int kPrefillWaves = 4;
-constexpr int kPrefillRowsPerWave = 32;
-constexpr int kPrefillKeyTile = 32;
-// Stream-K prefill grid: at most one work-group per CU of a 256-CU MI355X.
-constexpr int kPrefillMaxWorkGroups = 256;
-// Decode: single-wave work-groups folding tiles of 64 keys (one per lane).
-constexpr int kDecodeKeyTile = 64;
-// Split plan constants: about kDecodeKps keys per split, at most
-// kDecodeSplitCap splits per slot. Splits are the schedulable work items.
-constexpr int kDecodeKps = 128;
-constexpr int kDecodeSplitCap = 512;
-// Work-groups of the decode partial pass: 8 waves per CU of a 256-CU MI355X.
-constexpr int kDecodeMaxWaves = 2048;
-
 inline int prefill_q_positions(int group) {
     return kPrefillWaves * kPrefillRowsPerWave / group;
 }
@@ -126,6 +152,27 @@ hipError_t launch_shadow_pass(int head_dim, int group, const ShadowPassArgs &a, 
                               hipStream_t s);
 hipError_t launch_prefill(int format, int head_dim, int group, const PrefillArgs &a,
                           hipStream_t s);
+hipError_t launch_paged_prefill(int head_dim, int group, const PrefillArgs &a, hipStream_t s);
+
+// Paged KV append ([VT] ReshapeAndCache): token t < n goes to slot
+// slot_mapping[t] (page slot / block_size, row slot % block_size); slots < 0
+// or past the cache are skipped.
+struct PagedAppendArgs {
+    const float *k_new, *v_new;   // [n][n_kv][hd]
+    float *k, *v;
+    const long long *slot_mapping;
+    int n, n_kv, head_dim, block_size, num_blocks;
+    long long blk_stride;
+};
+hipError_t launch_paged_append(const PagedAppendArgs &a, hipStream_t s);
+
+// LSE merge of two attention states ([VT] MergeAttnStates).
+struct MergeArgs {
+    float *out, *out_lse;         // [T][H][D], [H][T] or NULL
+    const float *p_out, *p_lse, *s_out, *s_lse;
+    int T, H, D, prefill_tokens_with_context;
+};
+hipError_t launch_merge(const MergeArgs &a, hipStream_t s);
 hipError_t launch_decode(int format, int head_dim, int group, const DecodeArgs &a, int waves,
                          hipStream_t s);
 

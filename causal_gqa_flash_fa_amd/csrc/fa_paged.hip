@@ -1,0 +1,94 @@
+// Paged KV append and the LSE merge of two attention states.
+//
+// Paged append ([VT] ReshapeAndCache): the new K and V rows of a token (all
+// kv heads, contiguous in the source) go to one row of one page, where the
+// NHD layout keeps them contiguous too, so a token is two straight copies of
+// n_kv * hd floats. Work-group per token, 16-byte accesses; an HBM copy.
+//
+// Merge ([VT] MergeAttnStates): two softmax attention results over disjoint
+// key sets, each with its log-sum-exp, combine as
+//   m = max(lse_p, lse_s), w_p = exp(lse_p - m), w_s = exp(lse_s - m),
+//   out = (w_p out_p + w_s out_s) / (w_p + w_s), lse = m + ln(w_p + w_s),
+// in fp32, with +inf LSEs read as -inf and, when both sides are -inf (no key
+// on either side), the prefix output kept with LSE -inf. Tokens from
+// prefill_tokens_with_context on (when >= 0) take the suffix state as is.
+// One thread per 4 output dims; an HBM-bound elementwise pass.
+#include "fa_device.hpp"
+#include "fa_internal.hpp"
+
+namespace fa {
+namespace {
+
+__global__ __launch_bounds__(256) void paged_append_kernel(PagedAppendArgs a) {
+    const long long slot = a.slot_mapping[blockIdx.x];
+    if (slot < 0 || slot >= (long long)a.num_blocks * a.block_size) return;
+    const long long page = slot / a.block_size;
+    const int row = (int)(slot - page * a.block_size);
+    const int n4 = a.n_kv * a.head_dim / 4;
+    const size_t src = (size_t)blockIdx.x * n4;
+    const size_t dst = ((size_t)page * a.blk_stride + (size_t)row * a.n_kv * a.head_dim) / 4;
+    const f32x4 *ks = (const f32x4 *)a.k_new + src;
+    const f32x4 *vs = (const f32x4 *)a.v_new + src;
+    f32x4 *kd = (f32x4 *)a.k + dst;
+    f32x4 *vd = (f32x4 *)a.v + dst;
+    for (int i = threadIdx.x; i < n4; i += 256) {
+        const f32x4 kv = ks[i], vv = vs[i];
+        kd[i] = kv;
+        vd[i] = vv;
+    }
+}
+
+__global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
+    const int tpr = a.D / 4;                           // threads per (token, head) row
+    const long long total = (long long)a.T * a.H * tpr;
+    for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < total;
+         i += (long long)gridDim.x * 256) {
+        const long long row = i / tpr;                 // t * H + h
+        const int c = (int)(i - row * tpr);
+        const int t = (int)(row / a.H);
+        const int h = (int)(row - (long long)t * a.H);
+        const size_t li = (size_t)h * a.T + t;
+        const size_t oi = (size_t)row * tpr + c;
+        const f32x4 so = ((const f32x4 *)a.s_out)[oi];
+        f32x4 o;
+        float lse;
+        if (a.prefill_tokens_with_context >= 0 && t >= a.prefill_tokens_with_context) {
+            o = so;
+            lse = a.s_lse[li];
+        } else {
+            float pl = a.p_lse[li], sl = a.s_lse[li];
+            pl = pl == INFINITY ? -INFINITY : pl;
+            sl = sl == INFINITY ? -INFINITY : sl;
+            const f32x4 po = ((const f32x4 *)a.p_out)[oi];
+            if (pl == -INFINITY && sl == -INFINITY) {
+                o = po;
+                lse = -INFINITY;
+            } else {
+                const float m = fmaxf(pl, sl);
+                const float wp = expf(pl - m), ws = expf(sl - m);
+                const float tot = wp + ws;
+                o = po * (wp / tot) + so * (ws / tot);
+                lse = logf(tot) + m;
+            }
+        }
+        ((f32x4 *)a.out)[oi] = o;
+        if (a.out_lse && c == 0) a.out_lse[li] = lse;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_paged_append(const PagedAppendArgs &a, hipStream_t s) {
+    hipLaunchKernelGGL(paged_append_kernel, dim3((unsigned)a.n), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_merge(const MergeArgs &a, hipStream_t s) {
+    const long long total = (long long)a.T * a.H * (a.D / 4);
+    long long blocks = (total + 255) / 256;
+    if (blocks > 8192) blocks = 8192;      // grid-stride beyond 32 work-groups per CU
+    hipLaunchKernelGGL(merge_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace fa

@@ -40,6 +40,14 @@
 //     runs a few times per row instead of on most tiles; the final acc / l
 //     is unchanged up to rounding because acc and l share the reference.
 //   * Tiles inside every row's key set skip the mask.
+//   * Paged varlen batch ([VT] PagedAttention, fp32 rows): the same kernel
+//     with the segments of every request in one stream-K list. Requests are
+//     described on the device (query_start_loc, seq_lens, block table), so
+//     the launch needs no device-to-host read: each work-group rebuilds the
+//     request table in LDS, a segment is a (request, kv head, query block),
+//     and each K/V row is DMA'd through its own descriptor at its page.
+//   * Optional LSE output (ln of the softmax denominator) per row, from the
+//     final {m, l}: the state [VT] MergeAttnStates merges.
 #include <type_traits>
 
 #include "fa_device.hpp"
@@ -160,7 +168,7 @@ __device__ __forceinline__ int block_excl_scan(int x, int tid, int *scratch, int
     return before + incl - x;
 }
 
-template <int HD, int G, int FMT>
+template <int HD, int G, int FMT, bool PG>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void prefill_kernel(PrefillArgs a) {
     using Sh = PrefillShape<HD, G, FMT>;
@@ -176,18 +184,71 @@ void prefill_kernel(PrefillArgs a) {
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index: uniform
     const int hlf = lane >> 5;        // which half of the contraction / key sub-block
     const int r32 = lane & 31;        // this lane's query row within the wave
-    const int NWG = gridDim.x;
-    // Work-groups are dealt to the 8 XCDs round-robin (block b on XCD b % 8);
-    // give each XCD a contiguous stretch of runs so that its L2 holds the K/V
-    // rows of few kv heads.
-    const int wg = NWG % kXcds == 0 ? (blockIdx.x % kXcds) * (NWG / kXcds) + blockIdx.x / kXcds
-                                    : blockIdx.x;
-    const int nsegs = a.n_kv * a.n_qblocks;
 
-    auto seg_of = [&](int s, int *q0, int *q1) {
-        const int qb = seg_qblock(s, a.n_qblocks);
-        *q0 = a.pos0 + qb * Sh::BQ;
-        *q1 = min(*q0 + Sh::BQ - 1, a.pos0 + a.n - 1);
+    // ---- paged batch: the requests' geometry, in LDS behind the K/V
+    // buffers. Segments are numbered request by request, then kv head, then
+    // query block. Device metadata is clamped so that no access leaves the
+    // query, output, block-table or cache buffers: query tokens to [0, n),
+    // a request's context to its block-table row.
+    int *rq_seg0 = (int *)(lds + 2 * Sh::BUF);   // [n_req + 1] first segment of each request
+    int *rq_ctx = rq_seg0 + a.n_req + 1;          // position of its first query token
+    int *rq_tok = rq_ctx + a.n_req;               // its first query token
+    int *rq_len = rq_tok + a.n_req;               // its query tokens
+    int nsegs = a.n_kv * a.n_qblocks;
+    if constexpr (PG) {
+        const int cap = a.bt_stride * a.block_size;
+        int carry = 0;
+        for (int base = 0; base < a.n_req; base += 256) {
+            const int r = base + tid;
+            int cnt = 0;
+            if (r < a.n_req) {
+                const int t0 = min(max(a.qsl[r], 0), a.n);
+                const int len = min(min(max(a.qsl[r + 1], t0), a.n) - t0, cap);
+                const int seq = min(max(a.seq_lens[r], len), cap);
+                rq_ctx[r] = seq - len;
+                rq_tok[r] = t0;
+                rq_len[r] = len;
+                cnt = a.n_kv * ((len + Sh::BQ - 1) / Sh::BQ);
+            }
+            int chunk;
+            const int before = block_excl_scan(cnt, tid, scan_scratch, &chunk);
+            if (r < a.n_req) rq_seg0[r] = carry + before;
+            carry += chunk;
+        }
+        if (tid == 0) rq_seg0[a.n_req] = carry;
+        __syncthreads();
+        nsegs = carry;
+    }
+
+    // Segment s: query block [q0, q1] (positions) of kv head kvh; position
+    // p is query token p + tok.
+    struct Seg {
+        int q0, q1, kvh, tok, req;
+    };
+    auto seg_of = [&](int s) -> Seg {
+        Seg g;
+        if constexpr (PG) {
+            int lo = 0, hi = a.n_req - 1;      // the last request starting at or before s
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (rq_seg0[mid] <= s) lo = mid;
+                else hi = mid - 1;
+            }
+            const int len = rq_len[lo], nqb = (len + Sh::BQ - 1) / Sh::BQ;
+            const int loc = s - rq_seg0[lo];
+            g.kvh = loc / nqb;
+            g.q0 = rq_ctx[lo] + seg_qblock(loc % nqb, nqb) * Sh::BQ;
+            g.q1 = min(g.q0 + Sh::BQ - 1, rq_ctx[lo] + len - 1);
+            g.tok = rq_tok[lo] - rq_ctx[lo];
+            g.req = lo;
+        } else {
+            g.kvh = s / a.n_qblocks;
+            g.q0 = a.pos0 + seg_qblock(s, a.n_qblocks) * Sh::BQ;
+            g.q1 = min(g.q0 + Sh::BQ - 1, a.pos0 + a.n - 1);
+            g.tok = -a.pos0;
+            g.req = 0;
+        }
+        return g;
     };
 
     // ---- schedule: total units, this work-group's run, the piece table.
@@ -199,42 +260,64 @@ void prefill_kernel(PrefillArgs a) {
     // least kTileUnits units (the host keeps work-groups <= tiles), so every
     // run between a segment's first and last owner owns one of its tiles.
     auto seg_units = [&](int s, int *cnt) {
-        int q0, q1;
-        seg_of(s, &q0, &q1);
-        *cnt = seg_tiles(q0, q1, a.sink, a.win, BK).count;
+        if (s >= nsegs) {
+            *cnt = 0;
+            return 0;
+        }
+        const Seg g = seg_of(s);
+        *cnt = seg_tiles(g.q0, g.q1, a.sink, a.win, BK).count;
         return *cnt > 0 ? *cnt * kTileUnits + kSegUnits : 0;
     };
     int total = 0;
     for (int base = 0; base < nsegs; base += 256) {
         const int s = base + tid;
         int cnt = 0;
-        const int u = s < nsegs ? seg_units(s, &cnt) : 0;
+        const int u = seg_units(s, &cnt);
         int chunk;
         block_excl_scan(u, tid, scan_scratch, &chunk);
         total += chunk;
     }
-    const long long lo = (long long)wg * total / NWG;
-    const long long hi = (long long)(wg + 1) * total / NWG;
+    // The host sizes the grid from the tile count; a paged launch cannot see
+    // it, so its grid is the maximum and it keeps total / kTileUnits runs at
+    // most (every run must span a whole tile), the other work-groups idle.
+    int NWG = gridDim.x;
+    if constexpr (PG) NWG = min(NWG, max(1, total / kTileUnits));
+    // Work-groups are dealt to the 8 XCDs round-robin (block b on XCD b % 8);
+    // give each XCD a contiguous stretch of runs so that its L2 holds the K/V
+    // rows of few kv heads.
+    const int b = blockIdx.x;
+    const int wg = b >= NWG ? -1
+                 : NWG % kXcds == 0 ? (b % kXcds) * (NWG / kXcds) + b / kXcds : b;
+    const long long lo = wg < 0 ? 0 : (long long)wg * total / NWG;
+    const long long hi = wg < 0 ? 0 : (long long)(wg + 1) * total / NWG;
     auto owner = [&](long long f) -> int { return (int)(((f + 1) * NWG - 1) / total); };
     if (tid == 0) {
         run_info[0] = -1;          // first segment of the run
         run_info[1] = -1;          // last segment of the run
     }
     {
-        int f_carry = 0, p_carry = 0;
+        int f_carry = 0, p_carry = 0, c_carry = 0;
         for (int base = 0; base < nsegs; base += 256) {
             const int s = base + tid;
             int cnt = 0;
-            const int u = s < nsegs ? seg_units(s, &cnt) : 0;
-            int chunk, chunk_p;
+            const int u = seg_units(s, &cnt);
+            int chunk, chunk_pc;
             const int F = f_carry + block_excl_scan(u, tid, scan_scratch, &chunk);
             const int T0 = F + kSegUnits;      // first tile unit
             const int np = cnt > 0 ? owner(T0 + (cnt - 1) * kTileUnits) - owner(T0) + 1 : 0;
-            const int pc = np > 1 ? np : 0;
-            const int P = p_carry + block_excl_scan(pc, tid, scan_scratch, &chunk_p);
-            if (wg == 0 && s < nsegs) {
-                a.seg_table[2 * s] = P;
-                a.seg_table[2 * s + 1] = np;
+            // pieces (< 2^16 in a launch) and cut segments, scanned together
+            const int pc = np > 1 ? np | (1 << 16) : 0;
+            const int PC = block_excl_scan(pc, tid, scan_scratch, &chunk_pc);
+            const int P = p_carry + (PC & 0xffff);
+            if (wg == 0 && np > 1) {
+                const Seg g = seg_of(s);
+                CutSeg &c = a.cuts->seg[c_carry + (PC >> 16)];
+                c.piece0 = P;
+                c.n_pieces = np;
+                c.q0 = g.q0;
+                c.q1 = g.q1;
+                c.kvh = g.kvh;
+                c.tok = g.tok;
             }
             if (u > 0 && F <= lo && lo < F + u) {
                 run_info[0] = s;
@@ -247,8 +330,10 @@ void prefill_kernel(PrefillArgs a) {
                 run_info[5] = P;
             }
             f_carry += chunk;
-            p_carry += chunk_p;
+            p_carry += chunk_pc & 0xffff;
+            c_carry += chunk_pc >> 16;
         }
+        if (wg == 0 && tid == 0) a.cuts->count = c_carry;
     }
     __syncthreads();
     const int s_first = run_info[0], s_last = run_info[1];
@@ -258,9 +343,8 @@ void prefill_kernel(PrefillArgs a) {
     // ---- fold tiles [t_lo, t_hi) of one segment; whole segments write out,
     // cut ones write piece `piece` of the partial buffer
     auto run_segment = [&](int seg, int t_lo, int t_hi, bool whole, int piece, bool first_owner) {
-    const int kvh = seg / a.n_qblocks;
-    int q0, q1;
-    seg_of(seg, &q0, &q1);
+    const Seg sg = seg_of(seg);
+    const int kvh = sg.kvh, q0 = sg.q0, q1 = sg.q1;
     const SegTiles st = seg_tiles(q0, q1, a.sink, a.win, BK);
     if (first_owner) skipped += (unsigned)(st.walked - st.count);
 
@@ -277,7 +361,7 @@ void prefill_kernel(PrefillArgs a) {
     // Q^T operand: this lane's row, contraction half hlf, pre-scaled.
     float qr[HH];
     if (row_live) {
-        const f32x4 *qp = (const f32x4 *)(a.q + ((size_t)(p_row - a.pos0) * a.n_head +
+        const f32x4 *qp = (const f32x4 *)(a.q + ((size_t)(p_row + sg.tok) * a.n_head +
                                                  kvh * G + g) * HD + hlf * HH);
 #pragma unroll
         for (int i = 0; i < HH / 4; i++) {
@@ -300,7 +384,7 @@ void prefill_kernel(PrefillArgs a) {
     // (only a Q4_0 cache has a shadow)
     const bool shadowed = FMT == 1 && (a.sh.sink > 0 || a.sh.win > 0);
     if (FMT == 1 && shadowed && first_owner && row_live) {
-        const size_t rf = (size_t)(p_row - a.pos0) * a.n_head + kvh * G + g;
+        const size_t rf = (size_t)(p_row + sg.tok) * a.n_head + kvh * G + g;
         const float *sp = a.out + rf * HD;
 #pragma unroll
         for (int r = 0; r < 16; r++) {
@@ -337,8 +421,50 @@ void prefill_kernel(PrefillArgs a) {
     // into LDS; Q4_0: raw blocks into registers). Rows past q1 (only in a
     // block's diagonal tile) repeat row q1 (fp32) or are zero (Q4_0): their
     // scores are masked, and V must stay finite so that p = 0 contributes 0.
+    // Paged: lane l (mod 32) holds the page and in-page row of tile row l
+    // (rows past q1 repeat row q1), loaded a tile ahead of the DMA that uses
+    // them so that the block-table read never stalls the wave.
+    const int *bt_row = PG ? a.block_table + (size_t)sg.req * a.bt_stride : nullptr;
+    int pf_page = 0, pf_row = 0;
+    auto prefetch_pages = [&](int j0) {
+        if constexpr (PG) {
+            const int jr = j0 + min(lane & (BK - 1), q1 - j0);
+            const int pi = jr / a.block_size;
+            pf_row = jr - pi * a.block_size;
+            pf_page = bt_row[pi];
+        }
+    };
+
     auto issue_tile = [&](int j0, int buf) {
-        if constexpr (FMT == 0) {
+        if constexpr (FMT == 0 && PG) {
+            constexpr int LPR = HD / 4;
+            constexpr int RPW = BK / Sh::W;
+            float *kd = lds + buf * Sh::BUF;
+            float *vd = kd + BK * KS;
+            // one descriptor per row (pages need not be adjacent); page ids
+            // outside the cache are clamped into it
+            const long long pg = min(max(pf_page, 0), a.num_blocks - 1);
+            const long long off =
+                (pg * a.blk_stride + ((long long)pf_row * a.n_kv + kvh) * HD) * (long long)sizeof(float);
+            const int olo = (int)(uint32_t)off, ohi = (int)(uint32_t)((unsigned long long)off >> 32);
+            // Row r's offset lives in lane r, which need not be one of the
+            // LPR copying lanes (HD = 64: 16 of them for 32 rows). The
+            // readlanes therefore stay outside the lane < LPR branch: a
+            // readlane may not be moved into a branch, so the offsets are
+            // computed with every lane active rather than only in the
+            // copying lanes.
+#pragma unroll
+            for (int i = 0; i < RPW; i++) {
+                const int row = w * RPW + i;
+                const unsigned long long o =
+                    ((unsigned long long)(uint32_t)__builtin_amdgcn_readlane(ohi, row) << 32) |
+                    (uint32_t)__builtin_amdgcn_readlane(olo, row);
+                if (lane < LPR) {
+                    dma16(raw_rsrc((const uint8_t *)a.k + o, (unsigned)RB), 16 * lane, kd + row * KS);
+                    dma16(raw_rsrc((const uint8_t *)a.v + o, (unsigned)RB), 16 * lane, vd + row * KS);
+                }
+            }
+        } else if constexpr (FMT == 0) {
             constexpr int LPR = HD / 4;           // lanes per row: 16-byte chunks
             constexpr int RPW = BK / Sh::W;       // rows per wave per tensor
             float *kd = lds + buf * Sh::BUF;
@@ -501,7 +627,9 @@ void prefill_kernel(PrefillArgs a) {
     __syncthreads();              // the previous segment no longer reads either buffer
     int buf = 0;
     int ti = t_lo;
+    prefetch_pages(st.tile(ti) * BK);
     issue_tile(st.tile(ti) * BK, 0);
+    if (PG && ti + 1 < t_hi) prefetch_pages(st.tile(ti + 1) * BK);
     store_tile(0);
     while (ti < t_hi) {
         wait_vmem();
@@ -510,7 +638,10 @@ void prefill_kernel(PrefillArgs a) {
         visited++;
         ti++;
         const bool more = ti < t_hi;
-        if (more) issue_tile(st.tile(ti) * BK, buf ^ 1);
+        if (more) {
+            issue_tile(st.tile(ti) * BK, buf ^ 1);
+            if (PG && ti + 1 < t_hi) prefetch_pages(st.tile(ti + 1) * BK);
+        }
         // Every wave computes every tile: for a wave whose rows need none of
         // its keys the tile is fully masked (p = 0, nothing changes). A branch
         // here would make the compiler carry O through VGPR copies.
@@ -525,8 +656,12 @@ void prefill_kernel(PrefillArgs a) {
     float *op;
     float scale_out;
     if (whole) {
-        op = a.out + ((size_t)(p_row - a.pos0) * a.n_head + kvh * G + g) * HD;
+        const size_t t = (size_t)(p_row + sg.tok);
+        op = a.out + (t * a.n_head + kvh * G + g) * HD;
         scale_out = 1.0f / l_tot;
+        // ln sum exp(scale q.k) = ln 2 * (m + log2 l): m is in base-2 units
+        if (a.lse && row_live && hlf == 0)
+            a.lse[(size_t)(kvh * G + g) * a.n + t] = (m_run + log2f(l_tot)) * kLn2;
     } else {
         const size_t prow = (size_t)piece * ROWS + row_wg;
         op = a.ws_acc + prow * HD;
@@ -596,20 +731,17 @@ constexpr int kCombineRows = 16;
 template <int HD, int G>
 __global__ __launch_bounds__(256) void prefill_combine_kernel(PrefillArgs a) {
     constexpr int ROWS = kPrefillWaves * kPrefillRowsPerWave;
-    constexpr int BQ = ROWS / G;
     constexpr int TPR = HD / 4;                    // threads per row
     constexpr int RPP = 256 / TPR;                 // rows per pass
-    const int seg = blockIdx.x;
-    const int np = a.seg_table[2 * seg + 1];
-    if (np <= 1) return;
-    const int P = a.seg_table[2 * seg];
-    const int qb = seg_qblock(seg, a.n_qblocks), kvh = seg / a.n_qblocks;
+    if ((int)blockIdx.x >= a.cuts->count) return;
+    const CutSeg c = a.cuts->seg[blockIdx.x];
+    const int np = c.n_pieces, P = c.piece0;
     const int c4 = threadIdx.x % TPR;
 #pragma unroll 1
     for (int rr = threadIdx.x / TPR; rr < kCombineRows; rr += RPP) {
         const int row = blockIdx.y * kCombineRows + rr;
-        const int p = a.pos0 + qb * BQ + row / G;
-        if (p > a.pos0 + a.n - 1) continue;
+        const int p = c.q0 + row / G;
+        if (p > c.q1) continue;
         float M = -INFINITY;
         for (int k = 0; k < np; k++) M = fmaxf(M, a.ws_m[(size_t)(P + k) * ROWS + row]);
         f32x4 o = {};
@@ -620,48 +752,59 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(PrefillArgs a) {
             L += a.ws_l[pr] * wgt;
             o += *(const f32x4 *)(a.ws_acc + pr * HD + 4 * c4) * wgt;
         }
-        *(f32x4 *)(a.out + ((size_t)(p - a.pos0) * a.n_head + kvh * G + row % G) * HD + 4 * c4) =
-            o * (1.0f / L);
+        const int h = c.kvh * G + row % G;
+        const size_t t = (size_t)(p + c.tok);
+        *(f32x4 *)(a.out + (t * a.n_head + h) * HD + 4 * c4) = o * (1.0f / L);
+        if (a.lse && c4 == 0) a.lse[(size_t)h * a.n + t] = (M + log2f(L)) * kLn2;
     }
 }
 
-template <int HD, int G, int FMT>
+// Dynamic LDS of a launch: the two K/V buffers, plus the request table of
+// a paged batch.
+template <int HD, int G, int FMT, bool PG>
+size_t lds_bytes(int n_req) {
+    return PrefillShape<HD, G, FMT>::LDS_BYTES + (PG ? (size_t)(4 * n_req + 1) * sizeof(int) : 0);
+}
+
+template <int HD, int G, int FMT, bool PG>
 hipError_t launch_one(const PrefillArgs &a, hipStream_t s) {
-    using Sh = PrefillShape<HD, G, FMT>;
     static bool attr_set = false;   // per process; the attribute is per function
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void *)prefill_kernel<HD, G, FMT>,
+        hipError_t e = hipFuncSetAttribute((const void *)prefill_kernel<HD, G, FMT, PG>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           (int)Sh::LDS_BYTES);
+                                           (int)lds_bytes<HD, G, FMT, PG>(kPagedMaxReqs));
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    hipLaunchKernelGGL((prefill_kernel<HD, G, FMT>), dim3(a.n_wg), dim3(256), Sh::LDS_BYTES, s, a);
+    const size_t lds = lds_bytes<HD, G, FMT, PG>(a.n_req);
+    hipLaunchKernelGGL((prefill_kernel<HD, G, FMT, PG>), dim3(a.n_wg), dim3(256), lds, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    // fewer cut segments than work-groups
     hipLaunchKernelGGL((prefill_combine_kernel<HD, G>),
-                       dim3(a.n_qblocks * a.n_kv, kPrefillWaves * kPrefillRowsPerWave / kCombineRows),
+                       dim3(a.n_wg > 1 ? a.n_wg - 1 : 1,
+                            kPrefillWaves * kPrefillRowsPerWave / kCombineRows),
                        dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
-template <int HD, int FMT>
+template <int HD, int FMT, bool PG>
 hipError_t by_group(int group, const PrefillArgs &a, hipStream_t s) {
     switch (group) {
-    case 1: return launch_one<HD, 1, FMT>(a, s);
-    case 2: return launch_one<HD, 2, FMT>(a, s);
-    case 4: return launch_one<HD, 4, FMT>(a, s);
-    case 8: return launch_one<HD, 8, FMT>(a, s);
+    case 1: return launch_one<HD, 1, FMT, PG>(a, s);
+    case 2: return launch_one<HD, 2, FMT, PG>(a, s);
+    case 4: return launch_one<HD, 4, FMT, PG>(a, s);
+    case 8: return launch_one<HD, 8, FMT, PG>(a, s);
     }
     return hipErrorInvalidValue;
 }
 
-template <int FMT>
+template <int FMT, bool PG>
 hipError_t by_dim(int head_dim, int group, const PrefillArgs &a, hipStream_t s) {
     switch (head_dim) {
-    case 64: return by_group<64, FMT>(group, a, s);
-    case 128: return by_group<128, FMT>(group, a, s);
-    case 256: return by_group<256, FMT>(group, a, s);
+    case 64: return by_group<64, FMT, PG>(group, a, s);
+    case 128: return by_group<128, FMT, PG>(group, a, s);
+    case 256: return by_group<256, FMT, PG>(group, a, s);
     }
     return hipErrorInvalidValue;
 }
@@ -670,7 +813,12 @@ hipError_t by_dim(int head_dim, int group, const PrefillArgs &a, hipStream_t s) 
 
 hipError_t launch_prefill(int format, int head_dim, int group, const PrefillArgs &a,
                           hipStream_t s) {
-    return format == 0 ? by_dim<0>(head_dim, group, a, s) : by_dim<1>(head_dim, group, a, s);
+    return format == 0 ? by_dim<0, false>(head_dim, group, a, s)
+                       : by_dim<1, false>(head_dim, group, a, s);
+}
+
+hipError_t launch_paged_prefill(int head_dim, int group, const PrefillArgs &a, hipStream_t s) {
+    return by_dim<0, true>(head_dim, group, a, s);
 }
 
 }  // namespace fa

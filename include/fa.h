@@ -11,8 +11,9 @@
  *        attention (slots)" section.
  *   [VT] vllm-cpp-sys include/vt/ops.h: vt::Attention, AttentionWindow,
  *        MlaDecodeAttention (split determinism), PagedAttentionArgs
- *        (host-known max_seq_len hint), kernel registration contract
- *        (unsupported inputs fail loudly).
+ *        (host-known max_seq_len hint), ReshapeAndCache, PagedAttention,
+ *        MergeAttnStates, kernel registration contract (unsupported inputs
+ *        fail loudly).
  *
  * Conventions shared by every entry point:
  *   - Pointers named k, v, k_new, v_new, q, out, d_pos, ws, tile_stats are
@@ -30,6 +31,7 @@
 #define FA_H
 
 #include <stddef.h>
+#include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -223,6 +225,98 @@ int fa_decode(const fa_cache *cache, const float *q, const int *d_pos, int n_slo
               int max_ctx_hint, int n_head, int attn_sink, int attn_win, float scale,
               float *out, void *ws, size_t ws_bytes, unsigned long long *tile_stats,
               void *stream);
+
+/* ------------------------------------------------ paged KV, varlen batch */
+/* A paged fp32 KV cache in the NHD layout of [VT] ReshapeAndCache and
+ * PagedAttention: k and v each hold num_blocks pages of block_size rows, and
+ * row o of page b for kv head g is the head_dim floats starting at float
+ *     b * block_stride + (o * n_kv_head + g) * head_dim
+ * of k (or v). block_stride 0 means block_size * n_kv_head * head_dim, i.e.
+ * k and v are [num_blocks][block_size][n_kv_head][head_dim]; the two halves
+ * of one [num_blocks][2][block_size][n_kv_head][head_dim] allocation are
+ * k = base, v = base + block_size * n_kv_head * head_dim with block_stride
+ * 2 * block_size * n_kv_head * head_dim. */
+typedef struct fa_paged_cache {
+    int num_blocks;          /* >= 1 */
+    int block_size;          /* rows per page, >= 1 */
+    int n_kv_head;           /* >= 1 */
+    int head_dim;            /* 64, 128 or 256 */
+    long long block_stride;  /* floats between pages: 0, or a multiple of 4 that is
+                                at least block_size * n_kv_head * head_dim */
+    float *k, *v;            /* device, 16-byte aligned */
+} fa_paged_cache;
+
+/* Paged KV write ([VT] ReshapeAndCache). For token t < num_slots with slot
+ * s = slot_mapping[t]: k[t] and v[t] (all kv heads) are copied verbatim to row
+ * s % block_size of page s / block_size. A slot < 0 skips its token (the
+ * padding convention); so does a slot >= num_blocks * block_size. Tokens at
+ * or past num_slots are not read (graph padding).
+ *   k, v: device [>= num_slots][n_kv_head][head_dim] fp32, 16-byte aligned.
+ *   slot_mapping: device int64[num_slots]. Two tokens mapped to one slot
+ *   race (either may win). num_slots == 0 enqueues nothing. One launch. */
+int fa_paged_append(const fa_paged_cache *cache, const float *k, const float *v,
+                    const int64_t *slot_mapping, int num_slots, void *stream);
+
+/* Workspace fa_paged_attention needs (independent of the batch); 0 if
+ * head_dim is invalid. */
+size_t fa_paged_workspace_bytes(int head_dim);
+
+/* Causal GQA attention of a varlen batch over a paged cache ([VT]
+ * PagedAttention, causal path; the key rows of every query, its own
+ * included, must already be written, e.g. by fa_paged_append). Request r
+ * owns query tokens t in [query_start_loc[r], query_start_loc[r+1]); with
+ * query_len = query_start_loc[r+1] - query_start_loc[r], token t sits at
+ * absolute position p = seq_lens[r] - query_len + (t - query_start_loc[r])
+ * (bottom-right alignment: seq_lens[r] counts the context including this
+ * chunk). Query head h reads kv head h / G; its key j <= p is row j % bs of
+ * page block_table[r * max_blocks_per_seq + j / bs] (bs = block_size).
+ *     s_j = scale * (q[t][h] . k_j);  out[t][h] = sum_j softmax(s)_j v_j
+ * over j in [0, p], or over [p - window_left, p] when window_left >= 0
+ * ([VT] AttentionWindow (left, right), bottom-right aligned: window_right,
+ * which must then be >= 0, admits no key past p under the causal bound).
+ * window_left < 0 is full causal attention. One query block of one request
+ * and kv head is the unit of work, and the blocks of all requests share one
+ * stream-K launch (key tiles outside the window are skipped) that needs no
+ * device-to-host read: the batch metadata stays on the device.
+ *   q, out: device [num_tokens][n_head][head_dim] fp32, 16-byte aligned.
+ *   lse:    NULL, or device [n_head][num_tokens] fp32 receiving
+ *           ln sum_j exp(s_j) per query row (the state fa_merge_attn_states
+ *           combines).
+ *   query_start_loc: device int32[num_reqs + 1], non-decreasing, within
+ *           [0, num_tokens]. seq_lens: device int32[num_reqs], with
+ *           query_len <= seq_lens[r] <= max_blocks_per_seq * block_size.
+ *   block_table: device int32[num_reqs][max_blocks_per_seq], entries in
+ *           [0, num_blocks).
+ *   0 <= num_reqs <= 1024; num_tokens == 0 or num_reqs == 0 enqueue nothing.
+ *   ws, ws_bytes: device scratch of at least fa_paged_workspace_bytes().
+ * The device metadata is not checked against those rules on the host (it is
+ * never read there); out-of-rule values are clamped on the device so that no
+ * access leaves the buffers, and the rows they touch are unspecified.
+ * Tokens outside every request's range are not written. Head dims, group
+ * sizes and the scale rule as fa_prefill. Two launches on `stream`. */
+int fa_paged_attention(const fa_paged_cache *cache, const float *q, int num_tokens,
+                       int n_head, const int *query_start_loc, const int *seq_lens,
+                       int num_reqs, const int *block_table, int max_blocks_per_seq,
+                       int window_left, int window_right, float scale, float *out,
+                       float *lse, void *ws, size_t ws_bytes, void *stream);
+
+/* LSE merge of two attention results over disjoint key sets ([VT]
+ * MergeAttnStates), in fp32. Per (token t, head h), with L_p, L_s the two
+ * log-sum-exps (a +inf read as -inf):
+ *   m = max(L_p, L_s); w_p = exp(L_p - m); w_s = exp(L_s - m);
+ *   out = (w_p out_p + w_s out_s) / (w_p + w_s); out_lse = m + ln(w_p + w_s)
+ * and when L_p = L_s = -inf (neither side saw a key): out = out_p and
+ * out_lse = -inf. Tokens t >= prefill_tokens_with_context (when that is
+ * >= 0) take out_s and L_s unchanged.
+ *   out, prefix_out, suffix_out: device [num_tokens][n_head][head_dim] fp32,
+ *       16-byte aligned; out may be either input.
+ *   out_lse (NULL: not written), prefix_lse, suffix_lse: device
+ *       [n_head][num_tokens] fp32; out_lse may be either input LSE.
+ *   head_dim a multiple of 4 in [4, 4096]. One launch. */
+int fa_merge_attn_states(float *out, float *out_lse, const float *prefix_out,
+                         const float *prefix_lse, const float *suffix_out,
+                         const float *suffix_lse, int num_tokens, int n_head, int head_dim,
+                         int prefill_tokens_with_context, void *stream);
 
 /* Message for a return code (static storage). */
 const char *fa_strerror(int code);

@@ -133,7 +133,7 @@ def test_prefill_validation():
     assert rc_prefill(c, n=40, ws_bytes=need - 1) == fa.FA_EWORKSPACE
     assert fa.fa_prefill_workspace_bytes(40, 6, 2, 128) == 0      # group 3
     assert fa.fa_prefill_workspace_bytes(40, 4, 2, 96) == 0
-    # the table grows with the number of query blocks, the pieces do not
+    # the cut list and the pieces do not grow with n, the shadow rows do
     assert fa.fa_prefill_workspace_bytes(40000, 4, 2, 128) >= need
 
 
@@ -154,6 +154,71 @@ def test_decode_validation():
     assert rc_decode(c, n_slots=0) == fa.FA_OK
     assert rc_decode(c, ws=0) == fa.FA_ENULL
     assert rc_decode(c, pos=0) == fa.FA_ENULL
+
+
+def paged(nb=10, bs=16, n_kv=2, hd=128, stride=0, k=FAKE, v=FAKE):
+    return fa.fa_paged_cache(nb, bs, n_kv, hd, stride, k, v)
+
+
+def rc_paged_append(c, k=FAKE, v=FAKE, sm=FAKE, n=3):
+    return fa.lib.fa_paged_append(ctypes.byref(c) if c is not None else None, k, v, sm, n, None)
+
+
+def rc_paged(c, q=FAKE, T=5, H=4, qsl=FAKE, sl=FAKE, R=2, bt=FAKE, mb=4, wl=-1, wr=0,
+             scale=0.1, out=FAKE, lse=None, ws=FAKE, ws_bytes=1 << 30):
+    return fa.lib.fa_paged_attention(ctypes.byref(c) if c is not None else None, q, T, H, qsl,
+                                     sl, R, bt, mb, wl, wr, scale, out, lse, ws, ws_bytes, None)
+
+
+def test_paged_append_validation():
+    assert rc_paged_append(None) == fa.FA_ENULL
+    assert rc_paged_append(paged(hd=96)) == fa.FA_EUNSUPPORTED
+    assert rc_paged_append(paged(nb=0)) == fa.FA_EINVAL
+    assert rc_paged_append(paged(bs=0)) == fa.FA_EINVAL
+    assert rc_paged_append(paged(k=0)) == fa.FA_ENULL
+    assert rc_paged_append(paged(k=FAKE + 4)) == fa.FA_EINVAL          # not 16-byte aligned
+    assert rc_paged_append(paged(stride=16 * 2 * 128 - 4)) == fa.FA_EINVAL   # pages overlap
+    assert rc_paged_append(paged(stride=2 * 16 * 2 * 128 + 2)) == fa.FA_EINVAL  # page misaligned
+    assert rc_paged_append(paged(), n=-1) == fa.FA_EINVAL
+    assert rc_paged_append(paged(), n=0) == fa.FA_OK
+    assert rc_paged_append(paged(), sm=0) == fa.FA_ENULL
+    assert rc_paged_append(paged(), v=0) == fa.FA_ENULL
+    assert rc_paged_append(paged(), k=FAKE + 8) == fa.FA_EINVAL
+
+
+def test_paged_attention_validation():
+    c = paged()
+    assert rc_paged(None) == fa.FA_ENULL
+    assert rc_paged(c, H=3) == fa.FA_EINVAL
+    assert rc_paged(c, H=32) == fa.FA_EUNSUPPORTED
+    assert rc_paged(c, scale=0.0) == fa.FA_EINVAL
+    assert rc_paged(c, R=1025) == fa.FA_EINVAL               # request table capacity
+    assert rc_paged(c, R=-1) == fa.FA_EINVAL
+    assert rc_paged(c, mb=0) == fa.FA_EINVAL
+    assert rc_paged(c, mb=1 << 28) == fa.FA_EINVAL           # positions past int32
+    assert rc_paged(c, wl=3, wr=-1) == fa.FA_EINVAL
+    assert rc_paged(c, T=0) == fa.FA_OK
+    assert rc_paged(c, R=0) == fa.FA_OK
+    for name in ("q", "qsl", "sl", "bt", "out", "ws"):
+        assert rc_paged(c, **{name: 0}) == fa.FA_ENULL, name
+    assert rc_paged(c, q=FAKE + 4) == fa.FA_EINVAL
+    need = fa.fa_paged_workspace_bytes(128)
+    assert need > 0 and fa.fa_paged_workspace_bytes(96) == 0
+    assert fa.fa_paged_workspace_bytes(256) > need
+    assert rc_paged(c, ws_bytes=need - 1) == fa.FA_EWORKSPACE
+
+
+def test_merge_validation():
+    def rc(T=4, H=2, D=128, out=FAKE, po=FAKE, pl=FAKE, so=FAKE, sl=FAKE):
+        return fa.lib.fa_merge_attn_states(out, None, po, pl, so, sl, T, H, D, -1, None)
+    assert rc(D=6) == fa.FA_EINVAL
+    assert rc(D=0) == fa.FA_EINVAL
+    assert rc(H=0) == fa.FA_EINVAL
+    assert rc(T=-1) == fa.FA_EINVAL
+    assert rc(T=0) == fa.FA_OK
+    for name in ("out", "po", "pl", "so", "sl"):
+        assert rc(**{name: 0}) == fa.FA_ENULL, name
+    assert rc(so=FAKE + 4) == fa.FA_EINVAL
 
 
 def test_plan_matches_oracle_with_library_constants():
