@@ -9,9 +9,11 @@ causal): fa_kv_append of the 2048 K/V rows followed by fa_prefill, inputs
 resident in HBM. `value` is key-set-counted prefill FLOPs (4*head_dim per
 attended (query, head, key)) per second of step time. The same line carries
 the other workloads as `legs` (Q4_0 8k prefill, 32k sliding-window prefill,
-64-slot Q4_0 decode), a `roofline` object for the dominant kernel (timed with
-HIP events on the launch stream) and the CPU oracle timed on the host cores
-as `cpu_baseline`.
+64-slot Q4_0 decode, both Q4_0 ones again with the fp16 sink/window shadow, a
+varlen batch over a paged fp32 cache, and the LSE merge of two attention
+states), a `roofline` object for the dominant kernel (timed with HIP events
+on the launch stream) and the CPU oracle timed on the host cores as
+`cpu_baseline`.
 """
 from __future__ import annotations
 
@@ -37,8 +39,10 @@ CSRC = os.path.join(ROOT, "causal_gqa_flash_fa_amd", "csrc")
 # Sources that define each measured launch: a change to any of them makes the
 # committed HBM counter figures stale.
 KERNEL_SOURCES = {
-    "prefill": ["fa_prefill.hip", "fa_device.hpp", "fa_internal.hpp", "fa_api.hip"],
-    "decode": ["fa_decode.hip", "fa_device.hpp", "fa_internal.hpp", "fa_api.hip"],
+    "prefill": ["fa_prefill.hip", "fa_device.hpp", "fa_internal.hpp", "fa_api.hip",
+                "fa_shadow.hpp", "fa_shadow.hip"],
+    "decode": ["fa_decode.hip", "fa_device.hpp", "fa_internal.hpp", "fa_api.hip",
+               "fa_shadow.hpp"],
 }
 
 
@@ -135,6 +139,106 @@ def prefill_leg(fa, torch, w, steps: int, warmup: int) -> dict:
         "tflops_kernel": flops / kern_ms / 1e9,
         "frac_fp32_mfma_peak": flops / kern_ms / 1e9 / PEAK_FP32_MFMA_TFLOPS,
     }
+
+
+def paged_flops(w) -> float:
+    """4 * head_dim FLOPs per attended (query, head, key), bottom-right
+    aligned positions, full causal."""
+    pairs = sum(keyset_pairs(n, c, 0, 0) for c, n in workloads.paged_requests(w))
+    return 4.0 * w.head_dim * w.n_head * pairs
+
+
+def paged_leg(fa, torch, w, steps: int, warmup: int) -> dict:
+    """One varlen step over the paged cache: fa_paged_append of the batch's
+    new K/V rows (the last query_len rows of every request), then
+    fa_paged_attention with the LSE output. The earlier context rows are
+    written once before timing."""
+    dev = torch.device("cuda:0")
+    reqs = workloads.paged_requests(w)
+    table, num_blocks, seq, qsl = workloads.paged_layout(w)
+    bs = w.block_size
+    cache, kt, vt = fa.make_paged_cache(num_blocks, bs, w.n_kv_head, w.head_dim, dev)
+    new_k, new_v, new_slots = [], [], []
+    for r, (c, n) in enumerate(reqs):
+        k, v = workloads.paged_kv(w, r, c + n)
+        rows = np.arange(c + n)
+        sm = workloads.paged_slots(table, r, rows, bs)
+        fa.fa_paged_append(cache, torch.from_numpy(k).to(dev), torch.from_numpy(v).to(dev),
+                           torch.from_numpy(sm).to(dev), c + n)
+        new_k.append(k[c:])
+        new_v.append(v[c:])
+        new_slots.append(sm[c:])
+    kn = torch.from_numpy(np.concatenate(new_k)).to(dev)
+    vn = torch.from_numpy(np.concatenate(new_v)).to(dev)
+    sn = torch.from_numpy(np.concatenate(new_slots)).to(dev)
+    T = int(qsl[-1])
+    q = torch.from_numpy(workloads.paged_q(w)).to(dev)
+    d_qsl, d_seq, d_bt = (torch.from_numpy(x).to(dev) for x in (qsl, seq, table))
+    out = torch.empty_like(q)
+    lse = torch.empty((w.n_head, T), dtype=torch.float32, device=dev)
+    ws_bytes = fa.fa_paged_workspace_bytes(w.head_dim)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ev = _events(torch, steps)
+
+    def step(i=None):
+        fa.fa_paged_append(cache, kn, vn, sn, T)
+        if i is not None:
+            ev[i][0].record()
+        fa.fa_paged_attention(cache, q, T, w.n_head, d_qsl, d_seq, len(reqs), d_bt,
+                              table.shape[1], -1, 0, w.scale, out, lse, ws, ws_bytes)
+        if i is not None:
+            ev[i][1].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kms = [a.elapsed_time(b) for a, b in ev]
+    flops = paged_flops(w)
+    step_ms = (t1 - t0) * 1e3 / steps
+    kern_ms = float(np.mean(kms))
+    return {
+        "workload": w.name, "kind": "paged", "kv": "f32", "tokens": T, "requests": len(reqs),
+        "decode_requests": sum(1 for _, n in reqs if n == 1), "block_size": bs,
+        "n_head": w.n_head, "n_kv_head": w.n_kv_head, "head_dim": w.head_dim,
+        "flops": flops, "ms_per_step": step_ms, "tflops_step": flops / step_ms / 1e9,
+        "attention_kernel_ms": kern_ms, "attention_kernel_ms_min": float(np.min(kms)),
+        "tflops_kernel": flops / kern_ms / 1e9,
+        "frac_fp32_mfma_peak": flops / kern_ms / 1e9 / PEAK_FP32_MFMA_TFLOPS,
+    }
+
+
+def merge_leg(fa, torch, steps: int, warmup: int, T: int = 8192, H: int = 16,
+              D: int = 256) -> dict:
+    """fa_merge_attn_states on [T][H][D] states: an HBM-bound pass reading
+    two outputs and two LSEs and writing one of each."""
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(workloads.SEED_BASE + 900)
+    po = torch.randn((T, H, D), device=dev, generator=g)
+    so = torch.randn((T, H, D), device=dev, generator=g)
+    pl = torch.randn((H, T), device=dev, generator=g)
+    sl = torch.randn((H, T), device=dev, generator=g)
+    out = torch.empty_like(po)
+    out_lse = torch.empty_like(pl)
+    ev = _events(torch, steps)
+    for i in range(-warmup, steps):
+        if i >= 0:
+            ev[i][0].record()
+        fa.fa_merge_attn_states(out, out_lse, po, pl, so, sl, T, H, D)
+        if i >= 0:
+            ev[i][1].record()
+    torch.cuda.synchronize()
+    kms = [a.elapsed_time(b) for a, b in ev]
+    nbytes = 3 * T * H * D * 4 + 3 * T * H * 4
+    ms = float(np.mean(kms))
+    return {"workload": f"merge-attn-states-{T}x{H}x{D}", "kind": "merge", "bytes": nbytes,
+            "kernel_ms": ms, "kernel_ms_min": float(np.min(kms)),
+            "gbs": nbytes / ms / 1e6, "frac_hbm_peak": nbytes / ms / 1e6 / PEAK_HBM_GBS}
 
 
 def decode_leg(fa, torch, w, steps: int, warmup: int) -> dict:
@@ -253,7 +357,9 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--legs", default="prefill-q4kv-8k,window-prefill-32k,decode-64slots-q4kv",
+    ap.add_argument("--legs", default="prefill-q4kv-8k,window-prefill-32k,decode-64slots-q4kv,"
+                                      "prefill-q4kv-8k-shadow,decode-64slots-q4kv-shadow,"
+                                      "paged-varlen-8k,merge-attn-states",
                     help="comma-separated extra workloads ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -272,10 +378,15 @@ def main() -> int:
     torch.cuda.set_device(0)
     fa.fa_init()
 
+    def run_leg(name):
+        if name == "merge-attn-states":
+            return merge_leg(fa, torch, args.steps, args.warmup)
+        w = workloads.BY_NAME[name]
+        fn = {"prefill": prefill_leg, "decode": decode_leg, "paged": paged_leg}[w.kind]
+        return fn(fa, torch, w, args.steps, args.warmup)
+
     if args.only:
-        w = workloads.BY_NAME[args.only]
-        leg = (prefill_leg if w.kind == "prefill" else decode_leg)(fa, torch, w, args.steps,
-                                                                   args.warmup)
+        leg = run_leg(args.only)
         if args.copy_calibration:
             leg["copy_calibration"] = copy_calibration(torch)
         print(json.dumps(leg), flush=True)
@@ -287,12 +398,8 @@ def main() -> int:
     main_leg = prefill_leg(fa, torch, head, args.steps, args.warmup)
     legs = []
     for name in [s for s in args.legs.split(",") if s]:
-        w = workloads.BY_NAME[name]
         print(f"[bench] leg {name}", file=sys.stderr, flush=True)
-        if w.kind == "prefill":
-            legs.append(prefill_leg(fa, torch, w, args.steps, args.warmup))
-        else:
-            legs.append(decode_leg(fa, torch, w, args.steps, args.warmup))
+        legs.append(run_leg(name))
         torch.cuda.empty_cache()
     extra = {}
     if args.copy_calibration:

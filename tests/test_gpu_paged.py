@@ -336,3 +336,50 @@ def test_paged_step_replays_in_a_graph_with_device_metadata():
         ref, ref_lse = oracle_batch(view, reqs, -1, scale)
         U.compare_rows(got, ref, U.TOL_F32, f"graph batch {name}")
         assert float(np.abs(got_lse - ref_lse).max()) <= TOL_LSE
+
+
+def test_paged_workload_sampled_rows_at_full_size():
+    # the varlen batch the bench times (50 requests, 8192 query tokens,
+    # 16-row pages over a 13836-page cache), in the same launch; the oracle
+    # checks the first, the last and one random token of every request
+    import workloads as WL
+    w = WL.BY_NAME["paged-varlen-8k"]
+    reqs = WL.paged_requests(w)
+    table, num_blocks, seq, qsl = WL.paged_layout(w)
+    dev = U.device()
+    U.log(f"paged workload {w.name}: {len(reqs)} requests, {int(qsl[-1])} tokens, "
+          f"{num_blocks} pages")
+    cache, kt, vt = fa.make_paged_cache(num_blocks, w.block_size, w.n_kv_head, w.head_dim, dev)
+    rng = rng_of(1700)
+    picks = []
+    for r, (c, n) in enumerate(reqs):
+        k, v = WL.paged_kv(w, r, c + n)
+        sm = WL.paged_slots(table, r, np.arange(c + n), w.block_size)
+        fa.fa_paged_append(cache, U.to_dev(k), U.to_dev(v), U.to_dev(sm), c + n)
+        local = sorted({0, n - 1, int(rng.integers(0, n))})
+        picks.append((r, local, k, v))
+    q = WL.paged_q(w)
+    T = int(qsl[-1])
+    out = torch.empty((T, w.n_head, w.head_dim), dtype=torch.float32, device=dev)
+    lse = torch.empty((w.n_head, T), dtype=torch.float32, device=dev)
+    ws_bytes = fa.fa_paged_workspace_bytes(w.head_dim)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    fa.fa_paged_attention(cache, U.to_dev(q), T, w.n_head, U.to_dev(qsl), U.to_dev(seq),
+                          len(reqs), U.to_dev(table), table.shape[1], -1, 0, w.scale, out, lse,
+                          ws, ws_bytes)
+    torch.cuda.synchronize()
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    got, ref, got_l, ref_l = [], [], [], []
+    for r, local, k, v in picks:
+        c, n = reqs[r]
+        toks = qsl[r] + np.array(local)
+        pos = (c + np.array(local)).astype(np.int32)
+        kr = np.ascontiguousarray(k.transpose(1, 0, 2))
+        vr = np.ascontiguousarray(v.transpose(1, 0, 2))
+        ref.append(oracle.gqa_rows(q[toks], pos, kr, vr, 0, 0, w.scale,
+                                   threads=U.ORACLE_THREADS).reshape(len(toks), w.n_head, -1))
+        ref_l.append(oracle.gqa_lse(q[toks], pos, kr, 0, 0, w.scale).reshape(len(toks), -1))
+        got.append(out[toks])
+        got_l.append(lse[:, toks].T)
+    U.compare_rows(np.concatenate(got), np.concatenate(ref), U.TOL_F32, "paged workload")
+    assert float(np.abs(np.concatenate(got_l) - np.concatenate(ref_l)).max()) <= TOL_LSE

@@ -6,8 +6,9 @@ library (``causal_gqa_flash_fa_amd``) can be fed from it without sharing code.
 
 Recipe: numpy ``Generator(PCG64(seed))`` standard normal, float32, with
 seed = 20261202 + 100 * config_index + tensor_id, where tensor_id is
-0 for q, 1 for k, 2 for v and 3 for decode context lengths; decode K/V of
-slot s add 1000 * s so slots can be generated one at a time.
+0 for q, 1 for k, 2 for v, 3 for decode context lengths (paged: the request
+draw) and 4 for the paged page order; decode K/V of slot s (paged: request s)
+add 1000 * s so slots can be generated one at a time.
 
 The shapes follow the workloads the Foundry attention.cu page describes
 (file header: 8k-token batched prefill of a G=8, head_dim=256 model; the
@@ -46,6 +47,7 @@ class Workload:
     ctx_hi: int = 0
     shadow_sink: int = 0  # Q4_0: fp16 shadow of the first positions ...
     shadow_win: int = 0   # ... and of the recent window (0, 0: no shadow)
+    block_size: int = 0   # paged: rows per page (n = query-token budget of the batch)
 
     @property
     def group(self) -> int:
@@ -74,7 +76,16 @@ SHADOW_WORKLOADS = [
     dataclasses.replace(WORKLOADS[4], name="decode-64slots-q4kv-shadow", shadow_sink=4,
                         shadow_win=256),
 ]
-BY_NAME = {w.name: w for w in WORKLOADS + SHADOW_WORKLOADS}
+# A varlen batch over a paged fp32 cache (the vLLM-style PagedAttention of the
+# vllm-cpp-sys ops page): requests are drawn until 8192 query tokens are
+# used, each either a decode step (one token, probability 1/2) or a prefill
+# chunk of 64..1024 tokens, after a context of 0..8192 rows; pages of 16 rows
+# are scattered over the cache in a seeded order.
+PAGED_WORKLOADS = [
+    Workload(5, "paged-varlen-8k", "paged", 16, 2, 256, KV_F32, n=8192, ctx_hi=8192,
+             block_size=16),
+]
+BY_NAME = {w.name: w for w in WORKLOADS + SHADOW_WORKLOADS + PAGED_WORKLOADS}
 
 
 def _rng(seed: int) -> np.random.Generator:
@@ -131,3 +142,53 @@ def custom_prefill(seed: int, n: int, pos0: int, n_head: int, n_kv_head: int,
     k = normal(seed + 1, (pos0 + n, n_kv_head, head_dim))
     v = normal(seed + 2, (pos0 + n, n_kv_head, head_dim))
     return q, k, v
+
+
+def paged_requests(w: Workload) -> list[tuple[int, int]]:
+    """(context rows before the chunk, query tokens) per request."""
+    rng = _rng(seed_of(w, 3))
+    reqs, budget = [], w.n
+    while budget > 0:
+        qlen = 1 if rng.random() < 0.5 else int(rng.integers(64, 1024, endpoint=True))
+        qlen = min(qlen, budget)
+        ctx = int(rng.integers(0, w.ctx_hi, endpoint=True))
+        reqs.append((ctx, qlen))
+        budget -= qlen
+    return reqs
+
+
+def paged_layout(w: Workload):
+    """Block table and cache size of the batch: request r's pages, in a seeded
+    random order over the cache. Returns (table int32 [R][max_blocks],
+    num_blocks, seq_lens int32 [R], query_start_loc int32 [R+1])."""
+    reqs = paged_requests(w)
+    bs = w.block_size
+    seq = np.array([c + n for c, n in reqs], np.int32)
+    pages = (seq + bs - 1) // bs
+    num_blocks = int(pages.sum())
+    perm = _rng(seed_of(w, 4)).permutation(num_blocks).astype(np.int32)
+    table = np.zeros((len(reqs), int(pages.max())), np.int32)
+    at = 0
+    for r, n in enumerate(pages):
+        table[r, :n] = perm[at:at + n]
+        at += n
+    qsl = np.zeros(len(reqs) + 1, np.int32)
+    qsl[1:] = np.cumsum([n for _, n in reqs])
+    return table, num_blocks, seq, qsl
+
+
+def paged_slots(table: np.ndarray, r: int, rows: np.ndarray, block_size: int) -> np.ndarray:
+    """Cache slot (page * block_size + row in page) of key rows `rows` of request r."""
+    return (table[r, rows // block_size].astype(np.int64) * block_size + rows % block_size)
+
+
+def paged_q(w: Workload) -> np.ndarray:
+    """q [tokens][n_head][head_dim] of the whole batch."""
+    return normal(seed_of(w, 0), (w.n, w.n_head, w.head_dim))
+
+
+def paged_kv(w: Workload, r: int, seq: int):
+    """k, v [seq][n_kv_head][head_dim] rows of request r (positions 0..seq-1)."""
+    k = normal(seed_of(w, 1, r), (seq, w.n_kv_head, w.head_dim))
+    v = normal(seed_of(w, 2, r), (seq, w.n_kv_head, w.head_dim))
+    return k, v
