@@ -43,6 +43,7 @@ KERNEL_SOURCES = {
                 "fa_shadow.hpp", "fa_shadow.hip"],
     "decode": ["fa_decode.hip", "fa_device.hpp", "fa_internal.hpp", "fa_api.hip",
                "fa_shadow.hpp"],
+    "merge": ["fa_paged.hip", "fa_device.hpp", "fa_internal.hpp", "fa_api.hip"],
 }
 
 
@@ -236,9 +237,11 @@ def merge_leg(fa, torch, steps: int, warmup: int, T: int = 8192, H: int = 16,
     kms = [a.elapsed_time(b) for a, b in ev]
     nbytes = 3 * T * H * D * 4 + 3 * T * H * 4
     ms = float(np.mean(kms))
+    rec = measured_traffic("merge", "merge-attn-states")
     return {"workload": f"merge-attn-states-{T}x{H}x{D}", "kind": "merge", "bytes": nbytes,
             "kernel_ms": ms, "kernel_ms_min": float(np.min(kms)),
-            "gbs": nbytes / ms / 1e6, "frac_hbm_peak": nbytes / ms / 1e6 / PEAK_HBM_GBS}
+            "gbs": nbytes / ms / 1e6, "frac_hbm_peak": nbytes / ms / 1e6 / PEAK_HBM_GBS,
+            "traffic_bytes": round(rec["traffic_bytes"]) if rec else None}
 
 
 def decode_leg(fa, torch, w, steps: int, warmup: int) -> dict:

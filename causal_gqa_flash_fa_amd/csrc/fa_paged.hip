@@ -12,7 +12,7 @@
 // in fp32, with +inf LSEs read as -inf and, when both sides are -inf (no key
 // on either side), the prefix output kept with LSE -inf. Tokens from
 // prefill_tokens_with_context on (when >= 0) take the suffix state as is.
-// One thread per 4 output dims; an HBM-bound elementwise pass.
+// An HBM-bound elementwise pass.
 #include "fa_device.hpp"
 #include "fa_internal.hpp"
 
@@ -38,42 +38,49 @@ __global__ __launch_bounds__(256) void paged_append_kernel(PagedAppendArgs a) {
     }
 }
 
-__global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
-    const int tpr = a.D / 4;                           // threads per (token, head) row
-    const long long total = (long long)a.T * a.H * tpr;
-    for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < total;
-         i += (long long)gridDim.x * 256) {
-        const long long row = i / tpr;                 // t * H + h
-        const int c = (int)(i - row * tpr);
-        const int t = (int)(row / a.H);
-        const int h = (int)(row - (long long)t * a.H);
-        const size_t li = (size_t)h * a.T + t;
-        const size_t oi = (size_t)row * tpr + c;
-        const f32x4 so = ((const f32x4 *)a.s_out)[oi];
-        f32x4 o;
-        float lse;
-        if (a.prefill_tokens_with_context >= 0 && t >= a.prefill_tokens_with_context) {
-            o = so;
-            lse = a.s_lse[li];
+// One thread per 4 dims of one (token, head) row: no loop, so each thread's
+// loads are independent of every other's; index arithmetic in 32 bits when
+// the element count allows it (64-bit division is a long software sequence).
+template <typename I>
+__device__ __forceinline__ void merge_one(const MergeArgs &a, I i) {
+    const I tpr = (I)(a.D / 4);                        // threads per (token, head) row
+    const I row = i / tpr;                             // t * H + h
+    const int c = (int)(i - row * tpr);
+    const I t = row / (I)a.H;
+    const int h = (int)(row - t * (I)a.H);
+    const size_t li = (size_t)h * a.T + (size_t)t;
+    const size_t oi = (size_t)i;
+    const f32x4 so = ((const f32x4 *)a.s_out)[oi];
+    f32x4 o;
+    float lse;
+    if (a.prefill_tokens_with_context >= 0 && t >= (I)a.prefill_tokens_with_context) {
+        o = so;
+        lse = a.s_lse[li];
+    } else {
+        float pl = a.p_lse[li], sl = a.s_lse[li];
+        pl = pl == INFINITY ? -INFINITY : pl;
+        sl = sl == INFINITY ? -INFINITY : sl;
+        const f32x4 po = ((const f32x4 *)a.p_out)[oi];
+        if (pl == -INFINITY && sl == -INFINITY) {
+            o = po;
+            lse = -INFINITY;
         } else {
-            float pl = a.p_lse[li], sl = a.s_lse[li];
-            pl = pl == INFINITY ? -INFINITY : pl;
-            sl = sl == INFINITY ? -INFINITY : sl;
-            const f32x4 po = ((const f32x4 *)a.p_out)[oi];
-            if (pl == -INFINITY && sl == -INFINITY) {
-                o = po;
-                lse = -INFINITY;
-            } else {
-                const float m = fmaxf(pl, sl);
-                const float wp = expf(pl - m), ws = expf(sl - m);
-                const float tot = wp + ws;
-                o = po * (wp / tot) + so * (ws / tot);
-                lse = logf(tot) + m;
-            }
+            const float m = fmaxf(pl, sl);
+            const float wp = expf(pl - m), ws = expf(sl - m);
+            const float tot = wp + ws;
+            o = po * (wp / tot) + so * (ws / tot);
+            lse = logf(tot) + m;
         }
-        ((f32x4 *)a.out)[oi] = o;
-        if (a.out_lse && c == 0) a.out_lse[li] = lse;
     }
+    ((f32x4 *)a.out)[oi] = o;
+    if (a.out_lse && c == 0) a.out_lse[li] = lse;
+}
+
+__global__ __launch_bounds__(256) void merge_kernel(MergeArgs a, unsigned long long total) {
+    const unsigned long long i = (unsigned long long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= total) return;
+    if (total <= 0xffffffffull) merge_one<unsigned>(a, (unsigned)i);
+    else merge_one<unsigned long long>(a, i);
 }
 
 }  // namespace
@@ -84,10 +91,10 @@ hipError_t launch_paged_append(const PagedAppendArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_merge(const MergeArgs &a, hipStream_t s) {
-    const long long total = (long long)a.T * a.H * (a.D / 4);
-    long long blocks = (total + 255) / 256;
-    if (blocks > 8192) blocks = 8192;      // grid-stride beyond 32 work-groups per CU
-    hipLaunchKernelGGL(merge_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
+    const unsigned long long total = (unsigned long long)a.T * a.H * (a.D / 4);
+    const unsigned long long blocks = (total + 255) / 256;
+    if (blocks > 0x7fffffffull) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(merge_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a, total);
     return hipGetLastError();
 }
 
