@@ -9,8 +9,8 @@ causal): fa_kv_append of the 2048 K/V rows followed by fa_prefill, inputs
 resident in HBM. `value` is key-set-counted prefill FLOPs (4*head_dim per
 attended (query, head, key)) per second of step time. The same line carries
 the other workloads as `legs` (Q4_0 8k prefill, 32k sliding-window prefill,
-64-slot Q4_0 decode, both Q4_0 ones again with the fp16 sink/window shadow, a
-varlen batch over a paged fp32 cache, and the LSE merge of two attention
+64-slot Q4_0 decode, both Q4_0 ones again with the fp16 sink/window shadow,
+the 64-slot decode over an fp32 cache, a varlen batch over a paged fp32 cache, and the LSE merge of two attention
 states), a `roofline` object for the dominant kernel (timed with HIP events
 on the launch stream) and the CPU oracle timed on the host cores as
 `cpu_baseline`.
@@ -94,7 +94,11 @@ def _events(torch, n):
             for _ in range(n)]
 
 
-def prefill_leg(fa, torch, w, steps: int, warmup: int) -> dict:
+def prefill_leg(fa, torch, w, steps: int, warmup: int, graph: bool = False) -> dict:
+    """Append + prefill of one workload. Kernel time: HIP events around each
+    eager fa_prefill. Step time: the same two calls launched eagerly, or, with
+    `graph`, captured once in a HIP graph and replayed (same kernels, same
+    work, no per-launch host overhead)."""
     dev = torch.device("cuda:0")
     q = torch.from_numpy(workloads.prefill_q(w)).to(dev)
     k_np, v_np = workloads.prefill_kv(w)
@@ -128,13 +132,28 @@ def prefill_leg(fa, torch, w, steps: int, warmup: int) -> dict:
     t1 = time.perf_counter()
     kms = [a.elapsed_time(b) for a, b in ev]
     flops = prefill_flops(w)
-    step_ms = (t1 - t0) * 1e3 / steps
+    eager_ms = (t1 - t0) * 1e3 / steps
+    step_ms = eager_ms
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            g.replay()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        step_ms = (t1 - t0) * 1e3 / steps
     kern_ms = float(np.mean(kms))
     return {
         "workload": w.name, "kind": "prefill", "kv": "q4_0" if w.kv_format else "f32",
         "n": w.n, "n_head": w.n_head, "n_kv_head": w.n_kv_head, "head_dim": w.head_dim,
         "attn_sink": w.attn_sink, "attn_win": w.attn_win,
         "shadow_sink": w.shadow_sink, "shadow_win": w.shadow_win,
+        "launch": "hip_graph" if graph else "eager", "ms_per_step_eager": eager_ms,
         "flops": flops, "ms_per_step": step_ms, "tflops_step": flops / step_ms / 1e9,
         "prefill_kernel_ms": kern_ms, "prefill_kernel_ms_min": float(np.min(kms)),
         "tflops_kernel": flops / kern_ms / 1e9,
@@ -362,9 +381,12 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--legs", default="prefill-q4kv-8k,window-prefill-32k,decode-64slots-q4kv,"
                                       "prefill-q4kv-8k-shadow,decode-64slots-q4kv-shadow,"
+                                      "decode-64slots-f32kv,"
                                       "paged-varlen-8k,merge-attn-states",
                     help="comma-separated extra workloads ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch the headline step eagerly instead of replaying a HIP graph")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (for counter scaling)")
     ap.add_argument("--only", default="",
@@ -398,7 +420,7 @@ def main() -> int:
     head = workloads.BY_NAME["prefill-f32kv-2k"]
     print(f"[bench] {head.name}: warmup {args.warmup}, steps {args.steps}", file=sys.stderr,
           flush=True)
-    main_leg = prefill_leg(fa, torch, head, args.steps, args.warmup)
+    main_leg = prefill_leg(fa, torch, head, args.steps, args.warmup, graph=not args.eager)
     legs = []
     for name in [s for s in args.legs.split(",") if s]:
         print(f"[bench] leg {name}", file=sys.stderr, flush=True)
@@ -433,7 +455,9 @@ def main() -> int:
         "config": {"workload": head.name, "n": head.n, "pos0": head.pos0,
                    "n_head": head.n_head, "n_kv_head": head.n_kv_head,
                    "head_dim": head.head_dim, "kv": "f32", "attn_sink": head.attn_sink,
-                   "attn_win": head.attn_win, "step": "fa_kv_append + fa_prefill"},
+                   "attn_win": head.attn_win, "step": "fa_kv_append + fa_prefill",
+                   "launch": main_leg["launch"],
+                   "ms_per_step_eager": round(main_leg["ms_per_step_eager"], 4)},
         "roofline": {"bound": "mfma",
                      "kernel": "fa_prefill: prefill_kernel<256,8,f32> + prefill_combine_kernel<256,8>",
                      "achieved": round(kern_tflops, 3), "peak": PEAK_FP32_MFMA_TFLOPS,

@@ -59,7 +59,10 @@ struct DShape {
     static constexpr int BKD = kDecodeKeyTile;      // keys per tile, one per lane in QK
     static constexpr int NHG = (G + 3) / 4;         // groups of 4 q heads
     static constexpr int HP = NHG * 4;              // padded head count
-    static constexpr int QS = HD + 4;               // padded LDS rows: broadcast reads hit distinct banks
+    // padded LDS q rows: the Q4_0 broadcast reads (HD + 4) and the fp32
+    // per-quarter reads (HD + 16: row r starts 64 r bytes into a bank period)
+    // hit distinct banks
+    static constexpr int QS = FMT == 0 ? HD + 16 : HD + 4;
     static constexpr int PS = BKD + 4;
     static constexpr int NB = HD / kQ4Block;
     static constexpr int RB = FMT == 0 ? HD * 4 : NB * kQ4BlockBytes;
@@ -246,53 +249,157 @@ void decode_partial_kernel(DecodeArgs a) {
         const float *qlane = Qs + (lane & 3) * QS;
 
         if constexpr (FMT == 0) {
-            // ---------------- fp32 tiles: direct row reads
-            for (int j = next_visited(k_lo); j < k_hi; j = next_visited(j + BKD)) {
+            // ---------------- fp32 tiles: direct row reads, software-pipelined
+            // At 4 FLOP per byte the fp32 tile is bound by memory, so:
+            //  * K rows are read 64 contiguous bytes at a time. The 16 blocks
+            //    of each QK MFMA split the contraction in four instead of
+            //    covering 64 keys: block 4 kg + u takes keys 4 kg + j
+            //    (j = lane & 3) of a 16-key set and the dims of quarter u of
+            //    every 16-dim chunk, so the 4 lanes of one key (u = 0..3)
+            //    load its 64 bytes of a chunk together (a lane per key
+            //    loading 16 bytes touched 64 rows per instruction, ~20%
+            //    slower). Key set s of the tile accumulates in acc[s]; at the
+            //    end the four quarter sums are added across lanes (xor 4, 8)
+            //    and lane l keeps key set u(l): lane l holds key
+            //    K(l) = 16 u + 4 kg + j, a fixed permutation of the tile.
+            //  * Both operands stream through register rings: K KD loads
+            //    ahead of the MFMAs (the next tile's first KD during this
+            //    tile's PV), V (lanes = dims) VD rows ahead (the tile's first
+            //    VD before QK). Rows past k_hi repeat row k_hi - 1 (their
+            //    keys are masked, so V only has to be finite). Scheduling
+            //    fences keep every load where it is written (the scheduler
+            //    would otherwise sink the ring loads next to their uses to
+            //    save registers), and LDS operands are read one step ahead.
+            constexpr int NCH = HD / 16;                // 16-dim chunks per row
+            constexpr int NKL = 4 * NCH;                // K loads per tile (chunk, key set)
+            // K loads in flight (fewer with 8 heads, whose accumulators take
+            // the registers)
+            constexpr int KD = NKL < 16 ? NKL : (NHG > 1 ? 8 : 16);
+            constexpr int VD = 8;                       // V rows in flight
+            constexpr int VPR = HD / 64;                // V floats per lane per row (= OD)
+            const int qu = (lane >> 2) & 3;             // contraction quarter of this lane
+            const int kl = 4 * (lane >> 4) + (lane & 3);   // key of this lane in a 16-key set
+            const int kperm = 16 * qu + kl;             // the tile key this lane ends up with
+            f32x4 kring[KD];
+            float vring[VD][VPR];
+            // load c = 4 * chunk + key set
+            auto kload = [&](int j, int c) -> f32x4 {
+                const int row = min(j + 16 * (c & 3) + kl, k_hi - 1);
+                return *(const f32x4 *)(kb + (size_t)row * RB + 64 * (c >> 2) + 16 * qu);
+            };
+            auto vload = [&](int j, int r, float (&dst)[VPR]) {
+                const float *vr = (const float *)(vb + (size_t)min(j + r, k_hi - 1) * RB);
+#pragma unroll
+                for (int c = 0; c < VPR; c++) dst[c] = vr[lane + 64 * c];
+            };
+            int j = next_visited(k_lo);
+            if (j < k_hi) {
+#pragma unroll
+                for (int c = 0; c < KD; c++) kring[c] = kload(j, c);
+            }
+            while (j < k_hi) {
                 vis++;
-                const int key = j + lane;
+                const int jn = next_visited(j + BKD);
+                const int key = j + kperm;
                 const bool kval = key < k_hi && in_key_set(key, pos, a.sink, a.win);
-                const f32x4 *kr = (const f32x4 *)(kb + (size_t)min(key, k_hi - 1) * RB);
-                f32x4 sacc2[NHG][2];
 #pragma unroll
-                for (int hg = 0; hg < NHG; hg++) sacc2[hg][0] = sacc2[hg][1] = f32x4{};
-#pragma unroll 8
-                for (int c4 = 0; c4 < HD / 4; c4++) {
-                    const f32x4 kv = kr[c4];
+                for (int r = 0; r < VD; r++) vload(j, r, vring[r]);
+                f32x4 acc[4][NHG];
 #pragma unroll
-                    for (int hg = 0; hg < NHG; hg++) {
-                        const f32x4 qv = *(const f32x4 *)(qlane + hg * 4 * QS + 4 * c4);
+                for (int ks = 0; ks < 4; ks++)
 #pragma unroll
-                        for (int t = 0; t < 4; t++)
-                            sacc2[hg][t & 1] = mfma4(qv[t], kv[t], sacc2[hg][t & 1]);
-                    }
-                }
-                f32x4 sacc[NHG];
-#pragma unroll
-                for (int hg = 0; hg < NHG; hg++) sacc[hg] = sacc2[hg][0] + sacc2[hg][1];
-                softmax_tile(sacc, kval, lane);
-                wave_lds_sync();
-                const float *plane = Pw + (lane & 3) * PS;
-#pragma unroll 2
-                for (int k4 = 0; k4 < BKD / 4; k4++) {
-                    f32x4 pa[NHG];
+                    for (int hg = 0; hg < NHG; hg++) acc[ks][hg] = f32x4{};
+                // q operand of chunk b: heads 4 hg + (lane & 3), dims of quarter qu
+                auto qread = [&](int b, f32x4 (&qv)[NHG]) {
 #pragma unroll
                     for (int hg = 0; hg < NHG; hg++)
-                        pa[hg] = *(const f32x4 *)(plane + hg * 4 * PS + 4 * k4);
+                        qv[hg] = *(const f32x4 *)(qlane + hg * 4 * QS + 16 * b + 4 * qu);
+                };
+                f32x4 qc[NHG];
+                qread(0, qc);
 #pragma unroll
-                    for (int t = 0; t < 4; t++) {
-                        const float *vr =
-                            (const float *)(vb + (size_t)min(j + 4 * k4 + t, k_hi - 1) * RB);
-                        float vv[OD];
+                for (int b = 0; b < NCH; b++) {
+                    f32x4 kv[4];
 #pragma unroll
-                        for (int c = 0; c < OD; c++) vv[c] = vr[lane + 64 * c];
+                    for (int ks = 0; ks < 4; ks++) {
+                        const int c = 4 * b + ks;
+                        kv[ks] = kring[c % KD];
+                        if (c + KD < NKL) kring[c % KD] = kload(j, c + KD);
+                    }
+                    f32x4 qn[NHG];
+                    if (b + 1 < NCH) qread(b + 1, qn);
+                    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                        for (int c = 0; c < OD; c++)
+                    for (int t = 0; t < 4; t++)
+#pragma unroll
+                        for (int ks = 0; ks < 4; ks++)
 #pragma unroll
                             for (int hg = 0; hg < NHG; hg++)
-                                O[c][hg] = mfma4(pa[hg][t], vv[c], O[c][hg]);
+                                acc[ks][hg] = mfma4(qc[hg][t], kv[ks][t], acc[ks][hg]);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (b + 1 < NCH) {
+#pragma unroll
+                        for (int hg = 0; hg < NHG; hg++) qc[hg] = qn[hg];
+                    }
+                }
+                // quarter sums across the lanes of one key, then key set qu
+                f32x4 sacc[NHG];
+#pragma unroll
+                for (int hg = 0; hg < NHG; hg++) {
+#pragma unroll
+                    for (int ks = 0; ks < 4; ks++) {
+#pragma unroll
+                        for (int i = 0; i < 4; i++) {
+                            float x = acc[ks][hg][i];
+                            x += __shfl_xor(x, 4);
+                            x += __shfl_xor(x, 8);
+                            acc[ks][hg][i] = x;
+                        }
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; i++)
+                        sacc[hg][i] = qu == 0 ? acc[0][hg][i]
+                                    : qu == 1 ? acc[1][hg][i]
+                                    : qu == 2 ? acc[2][hg][i] : acc[3][hg][i];
+                }
+                softmax_tile(sacc, kval, kperm);
+                wave_lds_sync();
+                const float *plane = Pw + (lane & 3) * PS;
+                auto pread = [&](int t4, f32x4 (&pa)[NHG]) {
+#pragma unroll
+                    for (int hg = 0; hg < NHG; hg++)
+                        pa[hg] = *(const f32x4 *)(plane + hg * 4 * PS + 4 * t4);
+                };
+                f32x4 pa[NHG];
+                pread(0, pa);
+#pragma unroll
+                for (int r = 0; r < BKD; r++) {
+                    const int t = r & 3;
+                    float vv[VPR];
+#pragma unroll
+                    for (int c = 0; c < VPR; c++) vv[c] = vring[r % VD][c];
+                    if (r + VD < BKD) vload(j, r + VD, vring[r % VD]);
+                    // the next tile's first K chunks fly during the rest of PV
+                    if (r == BKD - KD && jn < k_hi) {
+#pragma unroll
+                        for (int c = 0; c < KD; c++) kring[c] = kload(jn, c);
+                    }
+                    f32x4 pn[NHG];
+                    if (t == 3 && r + 1 < BKD) pread((r + 1) / 4, pn);
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int c = 0; c < VPR; c++)
+#pragma unroll
+                        for (int hg = 0; hg < NHG; hg++)
+                            O[c][hg] = mfma4(pa[hg][t], vv[c], O[c][hg]);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (t == 3 && r + 1 < BKD) {
+#pragma unroll
+                        for (int hg = 0; hg < NHG; hg++) pa[hg] = pn[hg];
                     }
                 }
                 wave_lds_sync();
+                j = jn;
             }
         } else {
             // ---------------- Q4_0 tiles
@@ -347,10 +454,12 @@ void decode_partial_kernel(DecodeArgs a) {
                     }
                 }
 
-                // QK: 2 accumulator chains per head group; step st covers
-                // code word q = st % 4 of block blk = st / 4. The q operands of
-                // the next step are read before this step's MFMAs (fenced so
-                // the scheduler keeps them there).
+                // QK: 2 accumulator chains per head group, issued so that an
+                // MFMA's accumulator was last written 2 * NHG instructions
+                // earlier, not by the one just before; step st covers code
+                // word q = st % 4 of block blk = st / 4. The q
+                // operands of the next step are read before this step's MFMAs
+                // (fenced so the scheduler keeps them there).
                 const int key = tj + lane;
                 // fp16-shadow keys are folded by the shadow pass, not here
                 const bool kval = key < k_hi && in_key_set(key, pos, a.sink, a.win) &&
@@ -386,13 +495,15 @@ void decode_partial_kernel(DecodeArgs a) {
                     if (st + 1 < NST) qread(st + 1, na, nh);
                     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                    for (int hg = 0; hg < NHG; hg++) {
+                    for (int t = 0; t < 4; t++)
 #pragma unroll
-                        for (int t = 0; t < 4; t++) {
+                        for (int hg = 0; hg < NHG; hg++)
                             sacc2[hg][t & 1] = mfma4(qa[hg][t], kv[t], sacc2[hg][t & 1]);
+#pragma unroll
+                    for (int t = 0; t < 4; t++)
+#pragma unroll
+                        for (int hg = 0; hg < NHG; hg++)
                             sacc2[hg][t & 1] = mfma4(qh[hg][t], kv[4 + t], sacc2[hg][t & 1]);
-                        }
-                    }
                     __builtin_amdgcn_sched_barrier(0);
                     if (st + 1 < NST) {
 #pragma unroll
@@ -406,7 +517,8 @@ void decode_partial_kernel(DecodeArgs a) {
                 const bool more = j < k_hi;
                 f32x4 sacc[NHG];
 #pragma unroll
-                for (int hg = 0; hg < NHG; hg++) sacc[hg] = sacc2[hg][0] + sacc2[hg][1];
+                for (int hg = 0; hg < NHG; hg++)
+                    sacc[hg] = sacc2[hg][0] + sacc2[hg][1];
                 softmax_tile(sacc, kval, (lane & 1) * 32 + (lane >> 1));   // even keys, then odd
 
                 wait_vmem_le<0>();                    // this tile's V bytes (nothing else in flight)

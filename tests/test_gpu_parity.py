@@ -321,11 +321,13 @@ def test_decode_out_of_range_position_gives_nan_rows():
     U.compare_rows(out[:1], ref.reshape(1, 4, 64), U.TOL_F32, "decode good slot")
 
 
-def test_decode_workload():
-    w = workloads.BY_NAME["decode-64slots-q4kv"]
+@pytest.mark.parametrize("name", ["decode-64slots-q4kv", "decode-64slots-f32kv"])
+def test_decode_workload(name):
+    w = workloads.BY_NAME[name]
     ctx = workloads.decode_ctx(w)
     q = workloads.decode_q(w)
-    U.log(f"workload {w.name}: {w.n_slots} slots, ctx {ctx.min()}..{ctx.max()}, Q4_0")
+    U.log(f"workload {w.name}: {w.n_slots} slots, ctx {ctx.min()}..{ctx.max()}, "
+          f"{'Q4_0' if w.kv_format else 'fp32'}")
     cache, kt, vt = fa.make_cache(w.kv_format, w.n_slots, w.n_kv_head, w.head_dim, w.max_seq,
                                   U.device())
     rng = np.random.Generator(np.random.PCG64(w.index))
@@ -351,8 +353,9 @@ def test_decode_workload():
     gpu = out.cpu().numpy()
     ks = {s: kept[s][0] for s in check}
     vs = {s: kept[s][1] for s in check}
-    ref = decode_reference(1, q, ks, vs, ctx, 0, 0, w.scale, check)
-    U.compare_rows(gpu[check], ref.reshape(len(check), w.n_head, w.head_dim), U.TOL_Q4, w.name)
+    ref = decode_reference(w.kv_format, q, ks, vs, ctx, 0, 0, w.scale, check)
+    U.compare_rows(gpu[check], ref.reshape(len(check), w.n_head, w.head_dim),
+                   U.TOL_Q4 if w.kv_format else U.TOL_F32, w.name)
     # every slot: finite output, and a second launch is bitwise identical
     assert np.all(np.isfinite(gpu))
     out2 = torch.full_like(qd, float("nan"))

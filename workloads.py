@@ -76,6 +76,12 @@ SHADOW_WORKLOADS = [
     dataclasses.replace(WORKLOADS[4], name="decode-64slots-q4kv-shadow", shadow_sink=4,
                         shadow_win=256),
 ]
+# The 64-slot decode again over an fp32 cache (same seeded inputs): at
+# 4 FLOP/B it is bound by HBM, not by fp32 MFMA, so it measures the decode
+# kernel's memory path against the bandwidth roofline.
+F32_DECODE_WORKLOADS = [
+    dataclasses.replace(WORKLOADS[4], name="decode-64slots-f32kv", kv_format=KV_F32),
+]
 # A varlen batch over a paged fp32 cache (the vLLM-style PagedAttention of the
 # vllm-cpp-sys ops page): requests are drawn until 8192 query tokens are
 # used, each either a decode step (one token, probability 1/2) or a prefill
@@ -85,7 +91,8 @@ PAGED_WORKLOADS = [
     Workload(5, "paged-varlen-8k", "paged", 16, 2, 256, KV_F32, n=8192, ctx_hi=8192,
              block_size=16),
 ]
-BY_NAME = {w.name: w for w in WORKLOADS + SHADOW_WORKLOADS + PAGED_WORKLOADS}
+BY_NAME = {w.name: w for w in
+           WORKLOADS + SHADOW_WORKLOADS + F32_DECODE_WORKLOADS + PAGED_WORKLOADS}
 
 
 def _rng(seed: int) -> np.random.Generator:
