@@ -82,7 +82,7 @@ template <> struct Chunk<4> { typedef uint32_t T; };
 template <int HD, int FMT>
 __device__ __forceinline__ int o_dim(int lane, int c) {
     if constexpr (FMT == 0) {
-        return lane + 64 * c;
+        return (HD / 64) * lane + c;      // consecutive dims per lane: one vector load per V row
     } else {
         using Sh = DShape<HD, 1, 1>;
         const int ll = lane & 31;
@@ -266,7 +266,9 @@ void decode_partial_kernel(DecodeArgs a) {
             //    ahead of the MFMAs (the next tile's first KD during this
             //    tile's PV), V (lanes = dims) VD rows ahead (the tile's first
             //    VD before QK). Rows past k_hi repeat row k_hi - 1 (their
-            //    keys are masked, so V only has to be finite). Scheduling
+            //    keys are masked, so V only has to be finite). A lane owns
+            //    VPR consecutive output dims, so a V row is one vector load
+            //    per lane. Scheduling
             //    fences keep every load where it is written (the scheduler
             //    would otherwise sink the ring loads next to their uses to
             //    save registers), and LDS operands are read one step ahead.
@@ -287,10 +289,19 @@ void decode_partial_kernel(DecodeArgs a) {
                 const int row = min(j + 16 * (c & 3) + kl, k_hi - 1);
                 return *(const f32x4 *)(kb + (size_t)row * RB + 64 * (c >> 2) + 16 * qu);
             };
+            // lane holds dims VPR * lane .. VPR * lane + VPR - 1: a row is one
+            // vector load per lane
             auto vload = [&](int j, int r, float (&dst)[VPR]) {
-                const float *vr = (const float *)(vb + (size_t)min(j + r, k_hi - 1) * RB);
-#pragma unroll
-                for (int c = 0; c < VPR; c++) dst[c] = vr[lane + 64 * c];
+                const float *vr = (const float *)(vb + (size_t)min(j + r, k_hi - 1) * RB) + VPR * lane;
+                if constexpr (VPR == 4) {
+                    const f32x4 x = *(const f32x4 *)vr;
+                    dst[0] = x[0]; dst[1] = x[1]; dst[2] = x[2]; dst[3] = x[3];
+                } else if constexpr (VPR == 2) {
+                    const f32x2 x = *(const f32x2 *)vr;
+                    dst[0] = x[0]; dst[1] = x[1];
+                } else {
+                    dst[0] = vr[0];
+                }
             };
             int j = next_visited(k_lo);
             if (j < k_hi) {
