@@ -10,7 +10,8 @@ resident in HBM. `value` is key-set-counted prefill FLOPs (4*head_dim per
 attended (query, head, key)) per second of step time. The same line carries
 the other workloads as `legs` (Q4_0 8k prefill, 32k sliding-window prefill,
 64-slot Q4_0 decode, both Q4_0 ones again with the fp16 sink/window shadow,
-the 64-slot decode over an fp32 cache, a varlen batch over a paged fp32 cache, and the LSE merge of two attention
+the 64-slot decode over an fp32 cache, a varlen batch over a paged fp32 cache,
+the 64-slot decode as 64 one-token requests over a paged fp32 cache, and the LSE merge of two attention
 states), a `roofline` object for the dominant kernel (timed with HIP events
 on the launch stream) and the CPU oracle timed on the host cores as
 `cpu_baseline`.
@@ -232,6 +233,58 @@ def paged_leg(fa, torch, w, steps: int, warmup: int) -> dict:
     }
 
 
+def paged_decode_leg(fa, torch, w, steps: int, warmup: int) -> dict:
+    """fa_paged_decode over the decode workload's rows in a paged fp32 cache
+    (one query token per request), timed like the decode leg: HIP events,
+    the last-level cache flushed between reps."""
+    dev = torch.device("cuda:0")
+    ctx = workloads.decode_ctx(w)
+    table, num_blocks = workloads.decode_page_table(w, ctx)
+    bs = w.block_size
+    cache, kt, vt = fa.make_paged_cache(num_blocks, bs, w.n_kv_head, w.head_dim, dev)
+    for s in range(w.n_slots):
+        k, v = workloads.decode_kv(w, s, int(ctx[s]))
+        sm = workloads.paged_slots(table, s, np.arange(int(ctx[s])), bs)
+        fa.fa_paged_append(cache, torch.from_numpy(k).to(dev), torch.from_numpy(v).to(dev),
+                           torch.from_numpy(sm).to(dev), int(ctx[s]))
+    q = torch.from_numpy(workloads.decode_q(w)).to(dev)
+    seq = torch.from_numpy(ctx.astype(np.int32)).to(dev)
+    bt = torch.from_numpy(table).to(dev)
+    out = torch.empty_like(q)
+    lse = torch.empty((w.n_head, w.n_slots), dtype=torch.float32, device=dev)
+    hint = int(ctx.max())
+    ws_bytes = fa.fa_paged_decode_workspace_bytes(w.n_slots, w.n_head, w.n_kv_head, w.head_dim,
+                                                  hint)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    ev = _events(torch, steps)
+
+    def step(i=None):
+        if i is not None:
+            ev[i][0].record()
+        fa.fa_paged_decode(cache, q, w.n_slots, w.n_head, seq, bt, table.shape[1], hint, -1, 0,
+                           w.scale, out, lse, ws, ws_bytes)
+        if i is not None:
+            ev[i][1].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    for i in range(steps):
+        flush.zero_()
+        step(i)
+    torch.cuda.synchronize()
+    kms = [a.elapsed_time(b) for a, b in ev]
+    ms = float(np.mean(kms))
+    kv_bytes = int(ctx.sum()) * w.n_kv_head * 2 * w.head_dim * 4
+    nbytes = kv_bytes + 2 * w.n_slots * w.n_head * w.head_dim * 4
+    gbs = nbytes / ms / 1e6
+    return {"workload": w.name, "kind": "paged_decode", "kv": "f32", "requests": w.n_slots,
+            "block_size": bs, "num_blocks": num_blocks, "ctx_sum": int(ctx.sum()),
+            "bytes": nbytes, "decode_ms": ms, "decode_ms_min": float(np.min(kms)), "gbs": gbs,
+            "frac_hbm_peak": gbs / PEAK_HBM_GBS}
+
+
 def merge_leg(fa, torch, steps: int, warmup: int, T: int = 8192, H: int = 16,
               D: int = 256) -> dict:
     """fa_merge_attn_states on [T][H][D] states: an HBM-bound pass reading
@@ -382,7 +435,7 @@ def main() -> int:
     ap.add_argument("--legs", default="prefill-q4kv-8k,window-prefill-32k,decode-64slots-q4kv,"
                                       "prefill-q4kv-8k-shadow,decode-64slots-q4kv-shadow,"
                                       "decode-64slots-f32kv,"
-                                      "paged-varlen-8k,merge-attn-states",
+                                      "paged-varlen-8k,paged-decode-64req-f32kv,merge-attn-states",
                     help="comma-separated extra workloads ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true",
@@ -407,7 +460,8 @@ def main() -> int:
         if name == "merge-attn-states":
             return merge_leg(fa, torch, args.steps, args.warmup)
         w = workloads.BY_NAME[name]
-        fn = {"prefill": prefill_leg, "decode": decode_leg, "paged": paged_leg}[w.kind]
+        fn = {"prefill": prefill_leg, "decode": decode_leg, "paged": paged_leg,
+              "paged_decode": paged_decode_leg}[w.kind]
         return fn(fa, torch, w, args.steps, args.warmup)
 
     if args.only:

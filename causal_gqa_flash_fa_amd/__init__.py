@@ -33,6 +33,7 @@ EXPORTS = [
     "fa_prefill_tile_shape", "fa_prefill_workspace_bytes", "fa_decode_plan", "fa_decode_plan_params",
     "fa_decode_workspace_bytes", "fa_decode", "fa_strerror", "fa_last_hip_error",
     "fa_paged_append", "fa_paged_workspace_bytes", "fa_paged_attention", "fa_merge_attn_states",
+    "fa_paged_decode", "fa_paged_decode_workspace_bytes",
 ]
 
 
@@ -114,6 +115,10 @@ def _load() -> ctypes.CDLL:
     L.fa_paged_workspace_bytes.restype = Z
     L.fa_paged_attention.argtypes = [PC, P, I, I, P, P, I, P, I, I, I, F, P, P, P, Z, P]
     L.fa_paged_attention.restype = I
+    L.fa_paged_decode_workspace_bytes.argtypes = [I, I, I, I, I]
+    L.fa_paged_decode_workspace_bytes.restype = Z
+    L.fa_paged_decode.argtypes = [PC, P, I, I, P, P, I, I, I, I, F, P, P, P, Z, P]
+    L.fa_paged_decode.restype = I
     L.fa_merge_attn_states.argtypes = [P, P, P, P, P, P, I, I, I, I, P]
     L.fa_merge_attn_states.restype = I
     L.fa_strerror.argtypes = [I]
@@ -279,6 +284,22 @@ def fa_paged_attention(cache: fa_paged_cache, q, num_tokens: int, n_head: int,
                                   _ptr(block_table), max_blocks_per_seq, window_left,
                                   window_right, scale, _ptr(out), _ptr(lse), _ptr(ws), ws_bytes,
                                   _stream(stream)), "fa_paged_attention")
+
+
+def fa_paged_decode_workspace_bytes(num_reqs: int, n_head: int, n_kv_head: int, head_dim: int,
+                                    max_seq_len_hint: int) -> int:
+    return lib.fa_paged_decode_workspace_bytes(num_reqs, n_head, n_kv_head, head_dim,
+                                               max_seq_len_hint)
+
+
+def fa_paged_decode(cache: fa_paged_cache, q, num_reqs: int, n_head: int, seq_lens, block_table,
+                    max_blocks_per_seq: int, max_seq_len_hint: int, window_left: int,
+                    window_right: int, scale: float, out, lse, ws, ws_bytes: int,
+                    stream=None) -> None:
+    _check(lib.fa_paged_decode(ctypes.byref(cache), _ptr(q), num_reqs, n_head, _ptr(seq_lens),
+                               _ptr(block_table), max_blocks_per_seq, max_seq_len_hint,
+                               window_left, window_right, scale, _ptr(out), _ptr(lse), _ptr(ws),
+                               ws_bytes, _stream(stream)), "fa_paged_decode")
 
 
 def fa_merge_attn_states(out, out_lse, prefix_out, prefix_lse, suffix_out, suffix_lse,

@@ -338,10 +338,11 @@ int shadow_groups(const fa_cache *c) {
     return (c->shadow_sink + c->shadow_win + 63) / 64;
 }
 
-DecodeLayout decode_layout(const fa_cache *c, int n_slots, int n_head, int max_ctx) {
+DecodeLayout decode_layout_of(int n_kv_head, int head_dim, int sh_groups, int n_slots, int n_head,
+                              int max_ctx) {
     DecodeLayout d;
-    const size_t nsegs = (size_t)n_slots * c->n_kv_head;
-    const int group = n_head / c->n_kv_head;
+    const size_t nsegs = (size_t)n_slots * n_kv_head;
+    const int group = n_head / n_kv_head;
     const size_t items = nsegs * (size_t)fa_decode_plan(max_ctx, nullptr, nullptr);
     d.waves = (int)(items < (size_t)fa::kDecodeMaxWaves ? (items ? items : 1)
                                                         : (size_t)fa::kDecodeMaxWaves);
@@ -350,14 +351,18 @@ DecodeLayout decode_layout(const fa_cache *c, int n_slots, int n_head, int max_c
     d.m_off = d.table_bytes;
     d.l_off = d.m_off + align256(d.max_partials * group * sizeof(float));
     d.acc_off = d.l_off + align256(d.max_partials * group * sizeof(float));
-    size_t end = d.acc_off + d.max_partials * group * (size_t)c->head_dim * sizeof(float);
-    d.sh_groups = shadow_groups(c);
+    size_t end = d.acc_off + d.max_partials * group * (size_t)head_dim * sizeof(float);
+    d.sh_groups = sh_groups;
     const size_t sh_rows = nsegs * (size_t)d.sh_groups * group;
     d.sh_m_off = align256(end);
     d.sh_l_off = d.sh_m_off + align256(sh_rows * sizeof(float));
     d.sh_acc_off = d.sh_l_off + align256(sh_rows * sizeof(float));
-    d.total = d.sh_groups ? d.sh_acc_off + sh_rows * (size_t)c->head_dim * sizeof(float) : end;
+    d.total = d.sh_groups ? d.sh_acc_off + sh_rows * (size_t)head_dim * sizeof(float) : end;
     return d;
+}
+
+DecodeLayout decode_layout(const fa_cache *c, int n_slots, int n_head, int max_ctx) {
+    return decode_layout_of(c->n_kv_head, c->head_dim, shadow_groups(c), n_slots, n_head, max_ctx);
 }
 }  // namespace
 
@@ -384,7 +389,7 @@ int fa_decode(const fa_cache *cache, const float *q, const int *d_pos, int n_slo
     if (ws_bytes < lay.total) return FA_EWORKSPACE;
     if ((rc = fa_init())) return rc;
     uint8_t *wsb = (uint8_t *)ws;
-    fa::DecodeArgs a;
+    fa::DecodeArgs a{};
     a.q = q;
     a.pos = d_pos;
     a.k = cache->k;
@@ -559,6 +564,71 @@ int fa_paged_attention(const fa_paged_cache *cache, const float *q, int num_toke
     a.blk_stride = paged_block_stride(cache);
     return hip_rc(fa::launch_paged_prefill(cache->head_dim, n_head / cache->n_kv_head, a,
                                            (hipStream_t)stream));
+}
+
+size_t fa_paged_decode_workspace_bytes(int num_reqs, int n_head, int n_kv_head, int head_dim,
+                                       int max_seq_len_hint) {
+    if (num_reqs < 0 || n_kv_head < 1 || n_head < 1 || n_head % n_kv_head ||
+        !group_ok(n_head / n_kv_head) || !dim_ok(head_dim) || max_seq_len_hint < 1)
+        return 0;
+    return decode_layout_of(n_kv_head, head_dim, 0, num_reqs, n_head, max_seq_len_hint).total;
+}
+
+int fa_paged_decode(const fa_paged_cache *cache, const float *q, int num_reqs, int n_head,
+                    const int *seq_lens, const int *block_table, int max_blocks_per_seq,
+                    int max_seq_len_hint, int window_left, int window_right, float scale,
+                    float *out, float *lse, void *ws, size_t ws_bytes, void *stream) {
+    int rc = check_paged_cache(cache);
+    if (rc) return rc;
+    if (cache->block_size % 16 != 0) return FA_EUNSUPPORTED;
+    if (n_head < 1 || n_head % cache->n_kv_head != 0) return FA_EINVAL;
+    if (!group_ok(n_head / cache->n_kv_head)) return FA_EUNSUPPORTED;
+    if ((rc = check_scale(scale))) return rc;
+    if (num_reqs < 0 || max_blocks_per_seq < 1 ||
+        (long long)max_blocks_per_seq * cache->block_size > 0x7fffffffLL)
+        return FA_EINVAL;
+    const long long cap = (long long)max_blocks_per_seq * cache->block_size;
+    if (max_seq_len_hint < 1 || max_seq_len_hint > cap) return FA_EINVAL;
+    if (window_left >= 0 && window_right < 0) return FA_EINVAL;
+    if (num_reqs == 0) return FA_OK;
+    if (!q || !out || !seq_lens || !block_table || !ws) return FA_ENULL;
+    if (((uintptr_t)q | (uintptr_t)out) % 16 != 0) return FA_EINVAL;
+    const int group = n_head / cache->n_kv_head;
+    const DecodeLayout lay =
+        decode_layout_of(cache->n_kv_head, cache->head_dim, 0, num_reqs, n_head, max_seq_len_hint);
+    if (ws_bytes < lay.total) return FA_EWORKSPACE;
+    if ((rc = fa_init())) return rc;
+    uint8_t *wsb = (uint8_t *)ws;
+    fa::DecodeArgs a{};
+    a.q = q;
+    a.pos = nullptr;
+    a.k = cache->k;
+    a.v = cache->v;
+    a.seg_table = (int *)wsb;
+    a.ws_m = (float *)(wsb + lay.m_off);
+    a.ws_l = (float *)(wsb + lay.l_off);
+    a.ws_acc = (float *)(wsb + lay.acc_off);
+    a.out = out;
+    a.stats = nullptr;
+    a.n_slots = num_reqs;
+    a.n_head = n_head;
+    a.n_kv = cache->n_kv_head;
+    a.max_seq = (int)cap;              // positions past a request's table row are invalid
+    a.sink = 0;
+    a.win = window_left < 0 || window_left >= cap ? 0 : window_left + 1;
+    a.qscale = scale * fa::kLog2e;
+    a.kps = fa::kDecodeKps;
+    a.cap = fa::kDecodeSplitCap;
+    a.sh_groups = 0;
+    a.sh_waves = 0;
+    a.seq_lens = seq_lens;
+    a.block_table = block_table;
+    a.bt_stride = max_blocks_per_seq;
+    a.block_size = cache->block_size;
+    a.num_blocks = cache->num_blocks;
+    a.blk_stride = paged_block_stride(cache);
+    a.lse = lse;
+    return hip_rc(fa::launch_paged_decode(cache->head_dim, group, a, lay.waves, (hipStream_t)stream));
 }
 
 int fa_merge_attn_states(float *out, float *out_lse, const float *prefix_out,

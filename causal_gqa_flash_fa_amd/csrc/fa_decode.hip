@@ -120,9 +120,10 @@ __device__ __forceinline__ int slot_items(int pos, const DecodeArgs &a, int *spl
     return decode_plan(pos + 1, a.kps, a.cap, kDecodeKeyTile, &n, split_len);
 }
 
-template <int HD, int G, int FMT>
+template <int HD, int G, int FMT, bool PG>
 __global__ __attribute__((amdgpu_flat_work_group_size(64, 64), amdgpu_waves_per_eu(2)))
 void decode_partial_kernel(DecodeArgs a) {
+    static_assert(!PG || FMT == 0, "paged caches hold fp32 rows");
     using Sh = DShape<HD, G, FMT>;
     constexpr int BKD = Sh::BKD, NHG = Sh::NHG, HP = Sh::HP, QS = Sh::QS, PS = Sh::PS;
     constexpr int NB = Sh::NB, RB = Sh::RB, CB = Sh::CB, BPL = Sh::BPL, OD = Sh::OD;
@@ -145,13 +146,19 @@ void decode_partial_kernel(DecodeArgs a) {
     const int w = blockIdx.x - (FMT == 1 ? a.sh_waves : 0);
     const int NW = gridDim.x - (FMT == 1 ? a.sh_waves : 0);
     const int nsegs = a.n_slots * a.n_kv;
+    // query position of a slot (paged: the request's last position, its
+    // length clamped to its block-table row)
+    auto pos_of = [&](int slot) -> int {
+        if constexpr (PG) return min(max(a.seq_lens[slot], 0), a.max_seq) - 1;
+        else return a.pos[slot];
+    };
 
     // ---- pass 1: total number of items
     int total = 0;
     for (int base = 0; base < nsegs; base += 64) {
         const int s = base + lane;
         int sl;
-        const int it = s < nsegs ? slot_items(a.pos[s / a.n_kv], a, &sl) : 0;
+        const int it = s < nsegs ? slot_items(pos_of(s / a.n_kv), a, &sl) : 0;
         total += __builtin_amdgcn_readfirstlane(wave_sum_i(it));
     }
     const long long lo = (long long)w * total / NW;
@@ -164,7 +171,7 @@ void decode_partial_kernel(DecodeArgs a) {
     // ---- per-segment fold of items [it_lo, it_hi) into one partial
     auto run_segment = [&](int seg, int it_lo, int it_hi, int pidx) {
         const int slot = seg / a.n_kv, kvh = seg % a.n_kv;
-        const int pos = __builtin_amdgcn_readfirstlane(a.pos[slot]);
+        const int pos = __builtin_amdgcn_readfirstlane(pos_of(slot));
         const bool shadowed = a.sh.sink > 0 || a.sh.win > 0;
         const int *wpos = a.sh.win_pos + (size_t)slot * kShadowWinMax;
         int split_len;
@@ -284,15 +291,49 @@ void decode_partial_kernel(DecodeArgs a) {
             const int kperm = 16 * qu + kl;             // the tile key this lane ends up with
             f32x4 kring[KD];
             float vring[VD][VPR];
-            // load c = 4 * chunk + key set
-            auto kload = [&](int j, int c) -> f32x4 {
-                const int row = min(j + 16 * (c & 3) + kl, k_hi - 1);
-                return *(const f32x4 *)(kb + (size_t)row * RB + 64 * (c >> 2) + 16 * qu);
+            // Paged: byte offset (from the cache base) of kv head kvh's row
+            // `row`; wave-uniform. A 16-key set starts at a multiple of 16
+            // and block_size is one too, so the set's rows are consecutive
+            // rows of one page: the set needs one lookup. Table indices and
+            // page ids are clamped into range; rows past k_hi are masked
+            // keys (K) or replaced by row k_hi - 1 (V).
+            const int *btr = PG ? a.block_table + (size_t)slot * a.bt_stride : nullptr;
+            const size_t rowb = (size_t)a.n_kv * HD * sizeof(float);   // bytes between page rows
+            // The table is read through the constant address space: the
+            // entry is a scalar load, counted apart from the vector loads in
+            // flight, so reading it never drains the K and V rings.
+            auto row_off = [&](int row) -> size_t {
+                const int ru = __builtin_amdgcn_readfirstlane(row);
+                const int pi = ru / a.block_size;
+                const __attribute__((address_space(4))) int *bt4 =
+                    (const __attribute__((address_space(4))) int *)(btr + min(pi, a.bt_stride - 1));
+                const int pg = min(max(*bt4, 0), a.num_blocks - 1);
+                return (size_t)pg * (size_t)a.blk_stride * sizeof(float) +
+                       (size_t)(ru - pi * a.block_size) * rowb + (size_t)kvh * HD * sizeof(float);
             };
+            size_t set_off[4] = {0, 0, 0, 0}, next_off[4] = {0, 0, 0, 0};
+            const size_t last_off = PG ? row_off(k_hi - 1) : 0;
+            // load c = 4 * chunk + key set
+            auto kload_at = [&](int j, int c, const size_t (&off)[4]) -> f32x4 {
+                if constexpr (PG) {
+                    return *(const f32x4 *)((const uint8_t *)a.k + off[c & 3] + kl * rowb +
+                                            64 * (c >> 2) + 16 * qu);
+                } else {
+                    const int row = min(j + 16 * (c & 3) + kl, k_hi - 1);
+                    return *(const f32x4 *)(kb + (size_t)row * RB + 64 * (c >> 2) + 16 * qu);
+                }
+            };
+            auto kload = [&](int j, int c) -> f32x4 { return kload_at(j, c, set_off); };
             // lane holds dims VPR * lane .. VPR * lane + VPR - 1: a row is one
             // vector load per lane
             auto vload = [&](int j, int r, float (&dst)[VPR]) {
-                const float *vr = (const float *)(vb + (size_t)min(j + r, k_hi - 1) * RB) + VPR * lane;
+                const float *vr;
+                if constexpr (PG) {
+                    const size_t o = j + r < k_hi ? set_off[r >> 4] + (size_t)(r & 15) * rowb : last_off;
+                    vr = (const float *)((const uint8_t *)a.v + o) + VPR * lane;
+                } else {
+                    vr = (const float *)(vb + (size_t)min(j + r, k_hi - 1) * RB) + VPR * lane;
+                }
                 if constexpr (VPR == 4) {
                     const f32x4 x = *(const f32x4 *)vr;
                     dst[0] = x[0]; dst[1] = x[1]; dst[2] = x[2]; dst[3] = x[3];
@@ -305,12 +346,23 @@ void decode_partial_kernel(DecodeArgs a) {
             };
             int j = next_visited(k_lo);
             if (j < k_hi) {
+                if constexpr (PG) {
+#pragma unroll
+                    for (int ks = 0; ks < 4; ks++) set_off[ks] = row_off(j + 16 * ks);
+                }
 #pragma unroll
                 for (int c = 0; c < KD; c++) kring[c] = kload(j, c);
             }
             while (j < k_hi) {
                 vis++;
                 const int jn = next_visited(j + BKD);
+                if constexpr (PG) {
+                    // the next tile's pages, read a tile ahead of its first K loads
+                    if (jn < k_hi) {
+#pragma unroll
+                        for (int ks = 0; ks < 4; ks++) next_off[ks] = row_off(jn + 16 * ks);
+                    }
+                }
                 const int key = j + kperm;
                 const bool kval = key < k_hi && in_key_set(key, pos, a.sink, a.win);
 #pragma unroll
@@ -393,7 +445,7 @@ void decode_partial_kernel(DecodeArgs a) {
                     // the next tile's first K chunks fly during the rest of PV
                     if (r == BKD - KD && jn < k_hi) {
 #pragma unroll
-                        for (int c = 0; c < KD; c++) kring[c] = kload(jn, c);
+                        for (int c = 0; c < KD; c++) kring[c] = kload_at(jn, c, next_off);
                     }
                     f32x4 pn[NHG];
                     if (t == 3 && r + 1 < BKD) pread((r + 1) / 4, pn);
@@ -411,6 +463,10 @@ void decode_partial_kernel(DecodeArgs a) {
                 }
                 wave_lds_sync();
                 j = jn;
+                if constexpr (PG) {
+#pragma unroll
+                    for (int ks = 0; ks < 4; ks++) set_off[ks] = next_off[ks];
+                }
             }
         } else {
             // ---------------- Q4_0 tiles
@@ -649,7 +705,7 @@ void decode_partial_kernel(DecodeArgs a) {
     for (int base = 0; base < nsegs; base += 64) {
         const int s = base + lane;
         int sl;
-        const int it = s < nsegs ? slot_items(a.pos[s / a.n_kv], a, &sl) : 0;
+        const int it = s < nsegs ? slot_items(pos_of(s / a.n_kv), a, &sl) : 0;
         const int incl = wave_incl_scan(it, lane);
         const int F = f_carry + incl - it;
         const int nw = it > 0 ? owner(F + it - 1) - owner(F) + 1 : 0;
@@ -712,12 +768,14 @@ __global__ __launch_bounds__(HD) void decode_combine_kernel(DecodeArgs a) {
         o += a.sh_acc[pi * HD + dd] * wgt;
     }
     a.out[(size_t)gh * HD + dd] = o / L;   // no partial (bad position): 0/0 = NaN
+    // ln sum exp(scale q.k) = ln 2 * (M + log2 L): partial m are in base-2 units
+    if (a.lse && dd == 0) a.lse[(size_t)h * a.n_slots + slot] = (M + log2f(L)) * kLn2;
 }
 
-template <int HD, int G, int FMT>
+template <int HD, int G, int FMT, bool PG>
 hipError_t launch_one(const DecodeArgs &a, int waves, hipStream_t s) {
-    hipLaunchKernelGGL((decode_partial_kernel<HD, G, FMT>), dim3(waves + a.sh_waves), dim3(64), 0,
-                       s, a);
+    hipLaunchKernelGGL((decode_partial_kernel<HD, G, FMT, PG>), dim3(waves + a.sh_waves), dim3(64),
+                       0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((decode_combine_kernel<HD, G>), dim3(a.n_slots * a.n_head), dim3(HD), 0, s,
@@ -725,23 +783,23 @@ hipError_t launch_one(const DecodeArgs &a, int waves, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <int HD, int FMT>
+template <int HD, int FMT, bool PG>
 hipError_t by_group(int group, const DecodeArgs &a, int waves, hipStream_t s) {
     switch (group) {
-    case 1: return launch_one<HD, 1, FMT>(a, waves, s);
-    case 2: return launch_one<HD, 2, FMT>(a, waves, s);
-    case 4: return launch_one<HD, 4, FMT>(a, waves, s);
-    case 8: return launch_one<HD, 8, FMT>(a, waves, s);
+    case 1: return launch_one<HD, 1, FMT, PG>(a, waves, s);
+    case 2: return launch_one<HD, 2, FMT, PG>(a, waves, s);
+    case 4: return launch_one<HD, 4, FMT, PG>(a, waves, s);
+    case 8: return launch_one<HD, 8, FMT, PG>(a, waves, s);
     }
     return hipErrorInvalidValue;
 }
 
-template <int FMT>
+template <int FMT, bool PG>
 hipError_t by_dim(int head_dim, int group, const DecodeArgs &a, int waves, hipStream_t s) {
     switch (head_dim) {
-    case 64: return by_group<64, FMT>(group, a, waves, s);
-    case 128: return by_group<128, FMT>(group, a, waves, s);
-    case 256: return by_group<256, FMT>(group, a, waves, s);
+    case 64: return by_group<64, FMT, PG>(group, a, waves, s);
+    case 128: return by_group<128, FMT, PG>(group, a, waves, s);
+    case 256: return by_group<256, FMT, PG>(group, a, waves, s);
     }
     return hipErrorInvalidValue;
 }
@@ -750,8 +808,13 @@ hipError_t by_dim(int head_dim, int group, const DecodeArgs &a, int waves, hipSt
 
 hipError_t launch_decode(int format, int head_dim, int group, const DecodeArgs &a, int waves,
                          hipStream_t s) {
-    return format == 0 ? by_dim<0>(head_dim, group, a, waves, s)
-                       : by_dim<1>(head_dim, group, a, waves, s);
+    return format == 0 ? by_dim<0, false>(head_dim, group, a, waves, s)
+                       : by_dim<1, false>(head_dim, group, a, waves, s);
+}
+
+hipError_t launch_paged_decode(int head_dim, int group, const DecodeArgs &a, int waves,
+                               hipStream_t s) {
+    return by_dim<0, true>(head_dim, group, a, waves, s);
 }
 
 }  // namespace fa

@@ -141,6 +141,15 @@ struct DecodeArgs {
     // the partial launch (shp.m_out/l_out/acc_out = sh_m/sh_l/sh_acc).
     ShadowPassArgs shp;
     int sh_waves;
+    // Paged batch (paged fp32 instances): slot s is request s, whose query
+    // sits at position seq_lens[s] - 1 (pos is unused) and whose key row j
+    // is row j % block_size of page block_table[s * bt_stride + j /
+    // block_size], at float page * blk_stride + (row * n_kv + kv head) * hd.
+    // block_size is a multiple of 16, so 16 aligned rows share a page.
+    const int *seq_lens, *block_table;
+    int bt_stride, block_size, num_blocks;
+    long long blk_stride;
+    float *lse;                   // NULL or [n_head][n_slots]: ln sum_j exp(scale q.k_j)
 };
 
 inline int prefill_q_positions(int group) {
@@ -175,6 +184,8 @@ struct MergeArgs {
 hipError_t launch_merge(const MergeArgs &a, hipStream_t s);
 hipError_t launch_decode(int format, int head_dim, int group, const DecodeArgs &a, int waves,
                          hipStream_t s);
+hipError_t launch_paged_decode(int head_dim, int group, const DecodeArgs &a, int waves,
+                               hipStream_t s);
 
 // Host copy of the device plan ([FA] fc_attn_dec_plan).
 __host__ __device__ inline int decode_plan(int seq_len, int kps, int cap, int tile, int *n_splits,

@@ -300,6 +300,43 @@ int fa_paged_attention(const fa_paged_cache *cache, const float *q, int num_toke
                        int window_left, int window_right, float scale, float *out,
                        float *lse, void *ws, size_t ws_bytes, void *stream);
 
+/* Workspace fa_paged_decode needs: the split-KV partials of fa_decode's
+ * scheme, sized by the request count, head counts and max_seq_len_hint; 0 if
+ * an argument is invalid. */
+size_t fa_paged_decode_workspace_bytes(int num_reqs, int n_head, int n_kv_head, int head_dim,
+                                       int max_seq_len_hint);
+
+/* Decode step over a paged cache: request r has exactly one query token, row
+ * r of q, at position p = seq_lens[r] - 1, and attends keys [0, p] (or
+ * [p - window_left, p] when window_left >= 0, with window_right >= 0 and
+ * otherwise unused, as in fa_paged_attention), read through the block table
+ * as in fa_paged_attention ([VT] PagedAttention on a batch of decode tokens).
+ * The same computation as fa_paged_attention on such a batch, with
+ * fa_decode's split-KV schedule ([FA] "Decode-mode flash attention"): every
+ * request's keys are cut into splits by fa_decode_plan, all requests' splits
+ * share one work list, and a combine pass merges the partials in ascending
+ * order, so a fixed launch is bit-reproducible.
+ *   cache->block_size must be a multiple of 16 (FA_EUNSUPPORTED otherwise):
+ *       16 aligned rows then share a page, so a 16-key group needs one
+ *       block-table lookup.
+ *   q, out: device [num_reqs][n_head][head_dim] fp32, 16-byte aligned.
+ *   lse: NULL, or device [n_head][num_reqs] fp32 (ln sum_j exp(s_j)).
+ *   seq_lens: device int32[num_reqs]; values are clamped on the device to
+ *       max_blocks_per_seq * block_size, and a request with seq_lens < 1
+ *       gets NaN rows (no key).
+ *   block_table: device int32[num_reqs][max_blocks_per_seq] (entries
+ *       clamped on the device into [0, num_blocks)).
+ *   max_seq_len_hint: host upper bound on seq_lens, 1..max_blocks_per_seq *
+ *       block_size ([VT] PagedAttentionArgs max_seq_len); sizes the launch.
+ *       Longer requests are still computed exactly.
+ *   ws, ws_bytes: at least fa_paged_decode_workspace_bytes(...).
+ * No device metadata is read on the host. num_reqs == 0 enqueues nothing.
+ * Two launches on `stream`. */
+int fa_paged_decode(const fa_paged_cache *cache, const float *q, int num_reqs, int n_head,
+                    const int *seq_lens, const int *block_table, int max_blocks_per_seq,
+                    int max_seq_len_hint, int window_left, int window_right, float scale,
+                    float *out, float *lse, void *ws, size_t ws_bytes, void *stream);
+
 /* LSE merge of two attention results over disjoint key sets ([VT]
  * MergeAttnStates), in fp32. Per (token t, head h), with L_p, L_s the two
  * log-sum-exps (a +inf read as -inf):

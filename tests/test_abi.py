@@ -208,6 +208,34 @@ def test_paged_attention_validation():
     assert rc_paged(c, ws_bytes=need - 1) == fa.FA_EWORKSPACE
 
 
+def test_paged_decode_validation():
+    def rc(c=None, q=FAKE, R=3, H=4, sl=FAKE, bt=FAKE, mb=4, hint=50, wl=-1, wr=0, scale=0.1,
+           out=FAKE, ws=FAKE, ws_bytes=1 << 30):
+        c = paged() if c is None else c
+        return fa.lib.fa_paged_decode(ctypes.byref(c), q, R, H, sl, bt, mb, hint, wl, wr, scale,
+                                      out, None, ws, ws_bytes, None)
+    assert fa.lib.fa_paged_decode(None, FAKE, 1, 4, FAKE, FAKE, 4, 10, -1, 0, 0.1, FAKE, None,
+                                  FAKE, 1 << 30, None) == fa.FA_ENULL
+    assert rc(c=paged(bs=24)) == fa.FA_EUNSUPPORTED        # block size not a multiple of 16
+    assert rc(c=paged(hd=96)) == fa.FA_EUNSUPPORTED
+    assert rc(H=3) == fa.FA_EINVAL
+    assert rc(H=32) == fa.FA_EUNSUPPORTED
+    assert rc(scale=-1.0) == fa.FA_EINVAL
+    assert rc(R=-1) == fa.FA_EINVAL
+    assert rc(mb=0) == fa.FA_EINVAL
+    assert rc(hint=0) == fa.FA_EINVAL
+    assert rc(hint=65) == fa.FA_EINVAL                      # past max_blocks * block_size
+    assert rc(wl=5, wr=-1) == fa.FA_EINVAL
+    assert rc(R=0) == fa.FA_OK
+    for name in ("q", "sl", "bt", "out", "ws"):
+        assert rc(**{name: 0}) == fa.FA_ENULL, name
+    need = fa.fa_paged_decode_workspace_bytes(3, 4, 2, 128, 50)
+    assert need > 0 and rc(ws_bytes=need - 1) == fa.FA_EWORKSPACE
+    assert fa.fa_paged_decode_workspace_bytes(3, 4, 2, 128, 0) == 0
+    assert fa.fa_paged_decode_workspace_bytes(3, 6, 2, 128, 50) == 0
+    assert fa.fa_paged_decode_workspace_bytes(3, 4, 2, 128, 5000) >= need
+
+
 def test_merge_validation():
     def rc(T=4, H=2, D=128, out=FAKE, po=FAKE, pl=FAKE, so=FAKE, sl=FAKE):
         return fa.lib.fa_merge_attn_states(out, None, po, pl, so, sl, T, H, D, -1, None)

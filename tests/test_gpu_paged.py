@@ -166,7 +166,7 @@ def test_paged_attention_interleaved_cache_layout():
     b = build_batch(rng_of(1100), reqs, n_kv, hd, H, bs)
     scale = 0.09
     U.log(f"paged attention interleaved [blocks][2][bs][kv][hd] T={b['T']}")
-    cache, _, _ = fill_cache(b, bs, n_kv, hd, interleaved=True)
+    cache, kt, vt = fill_cache(b, bs, n_kv, hd, interleaved=True)
     out, lse = run_paged(cache, b, H, hd, -1, scale)
     ref, ref_lse = oracle_batch(b, reqs, -1, scale)
     U.compare_rows(out, ref, U.TOL_F32, "paged interleaved")
@@ -181,7 +181,7 @@ def test_paged_single_sequence_agrees_with_the_contiguous_prefill():
     b = build_batch(rng, [(0, n)], n_kv, hd, H, bs)
     scale = float(1.0 / np.sqrt(hd))
     U.log(f"paged vs contiguous prefill n={n}")
-    pc, _, _ = fill_cache(b, bs, n_kv, hd)
+    pc, pkt, pvt = fill_cache(b, bs, n_kv, hd)
     out_p, _ = run_paged(pc, b, H, hd, -1, scale, want_lse=False)
     cache, kt, vt = fa.make_cache(fa.FA_KV_F32, 1, n_kv, hd, n, U.device())
     fa.fa_kv_append(cache, 0, 0, n, U.to_dev(b["k_rows"][0]), U.to_dev(b["v_rows"][0]))
@@ -207,7 +207,7 @@ def test_lse_merge_of_two_key_ranges_gives_the_full_attention():
     b = build_batch(rng, [(c, 1) for c in ctx], n_kv, hd, H, bs)
     scale = float(1.0 / np.sqrt(hd))
     U.log(f"LSE merge composition over {len(ctx)} decode rows, split {left} keys back")
-    cache, _, _ = fill_cache(b, bs, n_kv, hd)
+    cache, kt, vt = fill_cache(b, bs, n_kv, hd)
     full, full_lse = run_paged(cache, b, H, hd, -1, scale)
     suf, suf_lse = run_paged(cache, b, H, hd, left, scale)
     pre_b = dict(b)
@@ -283,7 +283,7 @@ def test_paged_step_replays_in_a_graph_with_device_metadata():
     ba = build_batch(rng, reqs_a, n_kv, hd, H, bs, extra_pages=200)
     T = max(ba["T"], sum(n for _, n in reqs_b))
     dev = U.device()
-    cache, _, _ = fill_cache(ba, bs, n_kv, hd)
+    cache, kt, vt = fill_cache(ba, bs, n_kv, hd)
     scale = float(1.0 / np.sqrt(hd))
     d_q = torch.zeros((T, H, hd), dtype=torch.float32, device=dev)
     d_qsl = torch.zeros(4, dtype=torch.int32, device=dev)
@@ -383,3 +383,115 @@ def test_paged_workload_sampled_rows_at_full_size():
         got_l.append(lse[:, toks].T)
     U.compare_rows(np.concatenate(got), np.concatenate(ref), U.TOL_F32, "paged workload")
     assert float(np.abs(np.concatenate(got_l) - np.concatenate(ref_l)).max()) <= TOL_LSE
+
+
+def run_paged_decode(cache, b, H, hd, window_left, scale, hint=None):
+    dev = U.device()
+    R = len(b["seq"])
+    hint = int(max(1, b["seq"].max())) if hint is None else hint
+    out = torch.full((R, H, hd), float("nan"), dtype=torch.float32, device=dev)
+    lse = torch.full((H, R), float("nan"), dtype=torch.float32, device=dev)
+    ws_bytes = fa.fa_paged_decode_workspace_bytes(R, H, cache.n_kv_head, hd, hint)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    fa.fa_paged_decode(cache, U.to_dev(b["q"]), R, H, U.to_dev(b["seq"]), U.to_dev(b["table"]),
+                       b["max_blocks"], hint, window_left, 0, scale, out, lse, ws, ws_bytes)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), lse.cpu().numpy()
+
+
+DECODE_CTX = [0, 1, 15, 16, 63, 64, 65, 127, 128, 129, 255, 300, 1000, 2047, 2048, 4099]
+
+
+@pytest.mark.parametrize("bs,window_left,hd,H,n_kv", [
+    (16, -1, 256, 16, 2),
+    (48, -1, 128, 8, 2),         # block size a multiple of 16 but not a power of two
+    (256, 100, 128, 32, 8),
+    (16, 0, 64, 8, 1),
+    (32, 700, 64, 4, 4),
+])
+def test_paged_decode_matches_oracle(bs, window_left, hd, H, n_kv):
+    reqs = [(c, 1) for c in DECODE_CTX]
+    rng = rng_of(1900 + bs + hd + H + max(window_left, 0))
+    b = build_batch(rng, reqs, n_kv, hd, H, bs)
+    scale = float(1.0 / np.sqrt(hd))
+    U.log(f"paged decode bs={bs} win_left={window_left} hd={hd} H={H}/{n_kv} "
+          f"requests={len(reqs)} pages={b['num_blocks']}")
+    cache, kt, vt = fill_cache(b, bs, n_kv, hd)
+    out, lse = run_paged_decode(cache, b, H, hd, window_left, scale)
+    ref, ref_lse = oracle_batch(b, reqs, window_left, scale)
+    U.compare_rows(out, ref, U.TOL_F32, f"paged decode bs={bs}")
+    assert float(np.abs(lse - ref_lse).max()) <= TOL_LSE
+    # the varlen path on the same batch: same attention, another schedule
+    out_v, lse_v = run_paged(cache, b, H, hd, window_left, scale)
+    assert float(np.abs(out - out_v).max()) <= 1e-5
+    assert float(np.abs(lse - lse_v).max()) <= 1e-5
+
+
+def test_paged_decode_hint_and_empty_request():
+    # a request longer than the host hint is still exact; a request with no
+    # key (seq_lens = 0) gets NaN rows and leaves the others untouched
+    H, n_kv, hd, bs = 8, 2, 128, 16
+    reqs = [(700, 1), (30, 1), (2000, 1)]
+    b = build_batch(rng_of(2000), reqs, n_kv, hd, H, bs)
+    scale = float(1.0 / np.sqrt(hd))
+    cache, kt, vt = fill_cache(b, bs, n_kv, hd)
+    U.log("paged decode with a small hint")
+    out, lse = run_paged_decode(cache, b, H, hd, -1, scale, hint=64)
+    ref, ref_lse = oracle_batch(b, reqs, -1, scale)
+    U.compare_rows(out, ref, U.TOL_F32, "paged decode small hint")
+    b0 = dict(b)
+    b0["seq"] = b["seq"].copy()
+    b0["seq"][1] = 0
+    U.log("paged decode with an empty request")
+    out0, _ = run_paged_decode(cache, b0, H, hd, -1, scale)
+    assert np.all(np.isnan(out0[1]))
+    # the other requests are unaffected (another launch size and work list,
+    # so the same values up to where the splits fall)
+    U.compare_rows(out0[[0, 2]], ref[[0, 2]], U.TOL_F32, "paged decode beside an empty request")
+
+
+def test_paged_decode_workload_at_full_size():
+    # the 64-request decode the bench times (16-row pages, 74k pages), in its
+    # launch; the oracle checks the shortest, the longest and 4 random requests
+    import workloads as WL
+    w = WL.BY_NAME["paged-decode-64req-f32kv"]
+    ctx = WL.decode_ctx(w)
+    table, num_blocks = WL.decode_page_table(w, ctx)
+    dev = U.device()
+    U.log(f"paged decode workload {w.name}: {w.n_slots} requests, ctx {ctx.min()}..{ctx.max()}, "
+          f"{num_blocks} pages")
+    cache, kt, vt = fa.make_paged_cache(num_blocks, w.block_size, w.n_kv_head, w.head_dim, dev)
+    rng = rng_of(2100)
+    check = sorted({int(np.argmin(ctx)), int(np.argmax(ctx))} |
+                   set(rng.choice(w.n_slots, 4, replace=False).tolist()))
+    kept = {}
+    for s in range(w.n_slots):
+        k, v = WL.decode_kv(w, s, int(ctx[s]))
+        sm = WL.paged_slots(table, s, np.arange(int(ctx[s])), w.block_size)
+        fa.fa_paged_append(cache, U.to_dev(k), U.to_dev(v), U.to_dev(sm), int(ctx[s]))
+        if s in check:
+            kept[s] = (k, v)
+    q = WL.decode_q(w)
+    hint = int(ctx.max())
+    out = torch.empty((w.n_slots, w.n_head, w.head_dim), dtype=torch.float32, device=dev)
+    lse = torch.empty((w.n_head, w.n_slots), dtype=torch.float32, device=dev)
+    ws_bytes = fa.fa_paged_decode_workspace_bytes(w.n_slots, w.n_head, w.n_kv_head, w.head_dim,
+                                                  hint)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    fa.fa_paged_decode(cache, U.to_dev(q), w.n_slots, w.n_head, U.to_dev(ctx.astype(np.int32)),
+                       U.to_dev(table), table.shape[1], hint, -1, 0, w.scale, out, lse, ws,
+                       ws_bytes)
+    torch.cuda.synchronize()
+    got, got_l = out.cpu().numpy(), lse.cpu().numpy()
+    assert np.all(np.isfinite(got)) and np.all(np.isfinite(got_l))
+    refs, ref_l = [], []
+    for s in check:
+        k, v = kept[s]
+        kr = np.ascontiguousarray(k.transpose(1, 0, 2))
+        vr = np.ascontiguousarray(v.transpose(1, 0, 2))
+        p = np.array([ctx[s] - 1], np.int32)
+        refs.append(oracle.gqa_rows(q[s:s + 1], p, kr, vr, 0, 0, w.scale,
+                                    threads=U.ORACLE_THREADS).reshape(w.n_head, -1))
+        ref_l.append(oracle.gqa_lse(q[s:s + 1], p, kr, 0, 0, w.scale))
+    U.compare_rows(got[check], np.stack(refs), U.TOL_F32, w.name)
+    assert float(np.abs(got_l[:, check].T - np.stack(ref_l)).max()) <= TOL_LSE

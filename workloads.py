@@ -91,6 +91,11 @@ PAGED_WORKLOADS = [
     Workload(5, "paged-varlen-8k", "paged", 16, 2, 256, KV_F32, n=8192, ctx_hi=8192,
              block_size=16),
 ]
+# The 64-slot decode again (same seeded inputs) over a paged fp32 cache of
+# 16-row pages in a seeded random order: one decode token per request.
+PAGED_WORKLOADS.append(
+    dataclasses.replace(WORKLOADS[4], name="paged-decode-64req-f32kv", kind="paged_decode",
+                        kv_format=KV_F32, block_size=16))
 BY_NAME = {w.name: w for w in
            WORKLOADS + SHADOW_WORKLOADS + F32_DECODE_WORKLOADS + PAGED_WORKLOADS}
 
@@ -199,3 +204,19 @@ def paged_kv(w: Workload, r: int, seq: int):
     k = normal(seed_of(w, 1, r), (seq, w.n_kv_head, w.head_dim))
     v = normal(seed_of(w, 2, r), (seq, w.n_kv_head, w.head_dim))
     return k, v
+
+
+def decode_page_table(w: Workload, ctx: np.ndarray):
+    """Pages of a decode batch whose request s holds ctx[s] rows: request by
+    request, consecutive page slots of a seeded permutation of the cache.
+    Returns (table int32 [R][max_blocks], num_blocks)."""
+    bs = w.block_size
+    pages = (ctx.astype(np.int64) + bs - 1) // bs
+    num_blocks = int(pages.sum())
+    perm = _rng(seed_of(w, 4)).permutation(num_blocks).astype(np.int32)
+    table = np.zeros((len(ctx), int(pages.max())), np.int32)
+    at = 0
+    for r, n in enumerate(pages):
+        table[r, :n] = perm[at:at + n]
+        at += int(n)
+    return table, num_blocks
