@@ -40,8 +40,7 @@ CSRC = os.path.join(ROOT, "causal_gqa_flash_fa_amd", "csrc")
 # Sources that define each measured launch: a change to any of them makes the
 # committed HBM counter figures stale.
 KERNEL_SOURCES = {
-    "prefill": ["fa_prefill.hip", "fa_device.hpp", "fa_internal.hpp", "fa_api.hip",
-                "fa_shadow.hpp", "fa_shadow.hip"],
+    "prefill": ["fa_prefill.hip", "fa_device.hpp", "fa_internal.hpp", "fa_api.hip"],
     "decode": ["fa_decode.hip", "fa_device.hpp", "fa_internal.hpp", "fa_api.hip",
                "fa_shadow.hpp"],
     "merge": ["fa_paged.hip", "fa_device.hpp", "fa_internal.hpp", "fa_api.hip"],

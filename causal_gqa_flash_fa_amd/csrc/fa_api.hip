@@ -280,26 +280,27 @@ int fa_prefill(const fa_cache *cache, int slot, const float *q, int pos0, int n,
     a.sh_m = (const float *)(wsb + lay.sh_m_off);
     a.sh_l = (const float *)(wsb + lay.sh_l_off);
     if (a.sh.sink > 0 || a.sh.win > 0) {
-        // each row's shadow-key partial: m, l to the workspace, acc to out
-        fa::ShadowPassArgs sp;
-        sp.q = q;
-        sp.d_pos = nullptr;
-        sp.pos0 = pos0;
-        sp.n_q = n;
-        sp.n_head = n_head;
-        sp.n_kv = cache->n_kv_head;
-        sp.max_seq = cache->max_seq;
-        sp.sink = a.sink;
-        sp.win = a.win;
-        sp.qscale = a.qscale;
-        sp.sh = a.sh;
-        sp.chunk_groups = 1;
-        sp.chunks_per_group = (fa::kShadowSinkMax + fa::kShadowWinMax + 63) / 64;
-        sp.m_out = (float *)a.sh_m;
-        sp.l_out = (float *)a.sh_l;
-        sp.acc_out = out;
-        if ((rc = hip_rc(fa::launch_shadow_pass(cache->head_dim, group, sp,
-                                                n * cache->n_kv_head, (hipStream_t)stream))))
+        // each row's shadow-key partial (m, l to the workspace, acc to out),
+        // from the same kernel in its shadow mode: per query block, the
+        // union of its rows' shadow keys in 32-key tiles
+        fa::PrefillArgs sa = a;
+        sa.stats = nullptr;
+        sa.lse = nullptr;
+        long long sh_tiles = 0;
+        for (int q0 = pos0; q0 < pos0 + n; q0 += bq) {
+            const int q1 = q0 + bq - 1 < pos0 + n - 1 ? q0 + bq - 1 : pos0 + n - 1;
+            const int n_sk = a.sh.sink < q1 + 1 ? a.sh.sink : q1 + 1;
+            const int wlo = a.sh.sink > q0 - a.sh.win + 1 ? a.sh.sink : q0 - a.sh.win + 1;
+            const int nk = n_sk + (a.sh.win > 0 && q1 >= wlo ? q1 - wlo + 1 : 0);
+            sh_tiles += (nk + fa::kPrefillKeyTile - 1) / fa::kPrefillKeyTile;
+        }
+        sh_tiles *= cache->n_kv_head;
+        long long sh_wg = g_device_cus[dev] < fa::kPrefillMaxWorkGroups ? g_device_cus[dev]
+                                                                        : fa::kPrefillMaxWorkGroups;
+        if (sh_tiles < sh_wg) sh_wg = sh_tiles;
+        sa.n_wg = sh_wg < 1 ? 1 : (int)sh_wg;
+        if ((rc = hip_rc(fa::launch_shadow_prefill(cache->head_dim, group, sa,
+                                                   (hipStream_t)stream))))
             return rc;
     }
     return hip_rc(fa::launch_prefill(cache->format, cache->head_dim, group, a,

@@ -30,11 +30,12 @@ __device__ __forceinline__ bool shadow_key(const ShadowArgs &sh, const int *win_
     return sh.win > 0 && s > p - sh.win && win_pos[s % kShadowWinMax] == s;
 }
 
-// Shadow pass (fa_shadow.hip): the softmax partial of each query row over its
-// fp16 shadow keys. Work item = (query i, kv head) x chunk group; query i sits
-// at d_pos[i] (decode: one per slot, shadow buffers of slot i) or pos0 + i
-// (prefill: shadow buffers of one slot). Partial of head g of item it, chunk
-// group cg: row (it * chunk_groups + cg) * G + g of m_out, l_out, acc_out.
+// Decode shadow work items (fa_shadow.hpp): the softmax partial of each
+// query row over its fp16 shadow keys. Work item = (query i, kv head) x chunk
+// group; query i sits at d_pos[i] (one per slot, shadow buffers of slot i;
+// d_pos NULL: at pos0 + i, shadow buffers of one slot). Partial of head g of
+// item it, chunk group cg: row (it * chunk_groups + cg) * G + g of m_out,
+// l_out, acc_out.
 struct ShadowPassArgs {
     const float *q;               // [n_q][n_head][hd]
     const int *d_pos;             // decode positions, or NULL
@@ -113,8 +114,9 @@ struct PrefillArgs {
     int n_req, bt_stride, block_size, num_blocks;
     long long blk_stride;
     // fp16 shadow (Q4_0): buffers of this slot. Its keys are skipped here;
-    // the shadow pass left each row's partial in sh_m, sh_l ([n][n_head]) and
-    // out (acc), and the first piece of every segment starts from it.
+    // the shadow-mode launch left each row's partial in sh_m, sh_l
+    // ([n][n_head]) and out (acc), and the first piece of every segment
+    // starts from it. The shadow mode itself writes them.
     ShadowArgs sh;
     const float *sh_m, *sh_l;
 };
@@ -157,11 +159,12 @@ inline int prefill_q_positions(int group) {
 }
 
 hipError_t launch_append(int format, const AppendArgs &a, hipStream_t s);
-hipError_t launch_shadow_pass(int head_dim, int group, const ShadowPassArgs &a, int items,
-                              hipStream_t s);
 hipError_t launch_prefill(int format, int head_dim, int group, const PrefillArgs &a,
                           hipStream_t s);
 hipError_t launch_paged_prefill(int head_dim, int group, const PrefillArgs &a, hipStream_t s);
+// fp16-shadow keys of a Q4_0 slot cache on the prefill MFMA path: leaves each
+// row's partial in sh_m, sh_l (m, l) and out (acc, unnormalised).
+hipError_t launch_shadow_prefill(int head_dim, int group, const PrefillArgs &a, hipStream_t s);
 
 // Paged KV append ([VT] ReshapeAndCache): token t < n goes to slot
 // slot_mapping[t] (page slot / block_size, row slot % block_size); slots < 0

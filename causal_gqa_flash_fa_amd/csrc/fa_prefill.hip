@@ -48,6 +48,13 @@
 //     and each K/V row is DMA'd through its own descriptor at its page.
 //   * Optional LSE output (ln of the softmax denominator) per row, from the
 //     final {m, l}: the state [VT] MergeAttnStates merges.
+//   * fp16-shadow keys of a Q4_0 cache ([FA] "fp16 sink + recent-window
+//     exemption"): the same kernel in a third mode folds, per query block,
+//     the union of its rows' shadow keys (sink rows, then the window ring
+//     rows the block can reach: about 9 tiles of 32) on the MFMA path, fp16
+//     rows converted into the fp32 LDS tiles, each key masked per row by the
+//     shadow predicate. It leaves every row's unnormalised partial
+//     {m, l, acc}, from which the main Q4_0 pass starts.
 #include <type_traits>
 
 #include "fa_device.hpp"
@@ -168,9 +175,17 @@ __device__ __forceinline__ int block_excl_scan(int x, int tid, int *scratch, int
     return before + incl - x;
 }
 
-template <int HD, int G, int FMT, bool PG>
+// Kernel modes: plain (one sequence of a slot cache), paged (varlen batch
+// over a paged fp32 cache), shadow (the fp16-shadow keys of a Q4_0 slot
+// cache, fp32 tiles; writes partials).
+constexpr int kModePlain = 0, kModePaged = 1, kModeShadow = 2;
+
+template <int HD, int G, int FMT, int MODE>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void prefill_kernel(PrefillArgs a) {
+    constexpr bool PG = MODE == kModePaged;
+    constexpr bool SH = MODE == kModeShadow;
+    static_assert(!(PG || SH) || FMT == 0, "paged and shadow modes stage fp32 tiles");
     using Sh = PrefillShape<HD, G, FMT>;
     constexpr int BK = Sh::BK, KS = Sh::KS, NT = Sh::NT, GS = Sh::GS, HH = Sh::HH;
     constexpr int NB = Sh::NB, RB = Sh::RB;
@@ -259,13 +274,29 @@ void prefill_kernel(PrefillArgs a) {
     // start at T0 belongs to owner(T0 + t * kTileUnits). Every run spans at
     // least kTileUnits units (the host keeps work-groups <= tiles), so every
     // run between a segment's first and last owner owns one of its tiles.
+    // Shadow mode: the keys of query block [q0, q1] that may come from the
+    // fp16 shadow for some row, in list order: sink positions [0, n_sk),
+    // then window positions [wlo, q1] (every position some row's ring window
+    // reaches). List entry i is position i (i < n_sk) or wlo + i - n_sk.
+    struct ShList {
+        int n_sk, wlo, nk;
+        __device__ int pos(int i) const { return i < n_sk ? i : wlo + i - n_sk; }
+    };
+    auto sh_list = [&](int q0, int q1) -> ShList {
+        ShList l;
+        l.n_sk = min(a.sh.sink, q1 + 1);
+        l.wlo = max(a.sh.sink, q0 - a.sh.win + 1);
+        l.nk = l.n_sk + (a.sh.win > 0 ? max(0, q1 - l.wlo + 1) : 0);
+        return l;
+    };
     auto seg_units = [&](int s, int *cnt) {
         if (s >= nsegs) {
             *cnt = 0;
             return 0;
         }
         const Seg g = seg_of(s);
-        *cnt = seg_tiles(g.q0, g.q1, a.sink, a.win, BK).count;
+        if constexpr (SH) *cnt = (sh_list(g.q0, g.q1).nk + BK - 1) / BK;
+        else *cnt = seg_tiles(g.q0, g.q1, a.sink, a.win, BK).count;
         return *cnt > 0 ? *cnt * kTileUnits + kSegUnits : 0;
     };
     int total = 0;
@@ -346,7 +377,10 @@ void prefill_kernel(PrefillArgs a) {
     const Seg sg = seg_of(seg);
     const int kvh = sg.kvh, q0 = sg.q0, q1 = sg.q1;
     const SegTiles st = seg_tiles(q0, q1, a.sink, a.win, BK);
-    if (first_owner) skipped += (unsigned)(st.walked - st.count);
+    if (!SH && first_owner) skipped += (unsigned)(st.walked - st.count);
+    const ShList shl = sh_list(q0, q1);
+    // first key (plain, paged) or list entry (shadow) of visited tile t
+    auto tile_at = [&](int t) { return SH ? t * BK : st.tile(t) * BK; };
 
     const int row_wg = w * Sh::R + r32;
     const int p_row = q0 + row_wg / G;
@@ -382,7 +416,7 @@ void prefill_kernel(PrefillArgs a) {
     // shadow-key partial, its acc read through the d permutation of the
     // output stores below
     // (only a Q4_0 cache has a shadow)
-    const bool shadowed = FMT == 1 && (a.sh.sink > 0 || a.sh.win > 0);
+    const bool shadowed = FMT == 1 && !SH && (a.sh.sink > 0 || a.sh.win > 0);
     if (FMT == 1 && shadowed && first_owner && row_live) {
         const size_t rf = (size_t)(p_row + sg.tok) * a.n_head + kvh * G + g;
         const float *sp = a.out + rf * HD;
@@ -405,6 +439,11 @@ void prefill_kernel(PrefillArgs a) {
     // when it is 4-byte aligned (even blocks), else from 2 bytes before it.
     // Both stay inside the row, which holds an even number of blocks.
     uint32_t raw[FMT == 0 ? 1 : Sh::IPT][5];
+    // shadow mode: fp16 rows staged as 16-byte chunks (8 values), item idx
+    // -> chunk idx % CPR of row (idx / CPR) % BK of K (or V past BK rows)
+    constexpr int CPR = HD / 8;
+    constexpr int SIPT = SH ? 2 * BK * CPR / 256 : 1;
+    u32x4 sraw[SIPT];
     // Q4_0 item idx -> (row, block) of the K tile (idx < BK*NB) or V tile:
     // 8 consecutive items take 8 consecutive rows of one block, then the
     // next block. A wave thus reads 8 whole rows (contiguous in memory),
@@ -436,7 +475,28 @@ void prefill_kernel(PrefillArgs a) {
     };
 
     auto issue_tile = [&](int j0, int buf) {
-        if constexpr (FMT == 0 && PG) {
+        if constexpr (SH) {
+            // entries past the list are zero rows (their keys are masked)
+#pragma unroll
+            for (int i = 0; i < SIPT; i++) {
+                const int idx = tid + 256 * i;
+                const int c = idx % CPR, kk = (idx / CPR) % BK;
+                const bool isv = idx >= BK * CPR;
+                const int li = j0 + kk;
+                if (li < shl.nk) {
+                    const int ps = shl.pos(li);
+                    const uint16_t *src =
+                        ps < a.sh.sink
+                            ? (isv ? a.sh.v_sink : a.sh.k_sink) +
+                                  ((size_t)kvh * kShadowSinkMax + ps) * HD
+                            : (isv ? a.sh.v_win : a.sh.k_win) +
+                                  ((size_t)kvh * kShadowWinMax + ps % kShadowWinMax) * HD;
+                    sraw[i] = *(const u32x4 *)(src + 8 * c);
+                } else {
+                    sraw[i] = u32x4{0u, 0u, 0u, 0u};
+                }
+            }
+        } else if constexpr (FMT == 0 && PG) {
             constexpr int LPR = HD / 4;
             constexpr int RPW = BK / Sh::W;
             float *kd = lds + buf * Sh::BUF;
@@ -503,9 +563,22 @@ void prefill_kernel(PrefillArgs a) {
         }
     };
 
-    // Q4_0 only: decode the staged blocks into LDS buffer `buf`.
+    // Q4_0: decode the staged blocks into LDS buffer `buf`; shadow mode:
+    // widen the staged fp16 rows.
     auto store_tile = [&](int buf) {
-        if constexpr (FMT == 1) {
+        if constexpr (SH) {
+            float *kd = lds + buf * Sh::BUF;
+            float *vd = kd + BK * KS;
+#pragma unroll
+            for (int i = 0; i < SIPT; i++) {
+                const int idx = tid + 256 * i;
+                const int c = idx % CPR, kk = (idx / CPR) % BK;
+                float *dst = (idx >= BK * CPR ? vd : kd) + kk * KS + 8 * c;
+                const u32x4 r = sraw[i];
+                *(f32x4 *)dst = f32x4{lo_h(r[0]), hi_h(r[0]), lo_h(r[1]), hi_h(r[1])};
+                *(f32x4 *)(dst + 4) = f32x4{lo_h(r[2]), hi_h(r[2]), lo_h(r[3]), hi_h(r[3])};
+            }
+        } else if constexpr (FMT == 1) {
             float *kd = lds + buf * Sh::BUF;
             float *vd = kd + BK * KS;
             const NibConsts nk = nib_consts();
@@ -557,9 +630,30 @@ void prefill_kernel(PrefillArgs a) {
         // no key of the tile is an fp16-shadow key for any row of the wave
         const bool shadow_free =
             !shadowed || (jc >= a.sh.sink && (a.sh.win <= 0 || jc + BK - 1 <= pw0 - a.sh.win));
-        const bool full = jc + BK - 1 <= pw0 && shadow_free &&
+        const bool full = !SH && jc + BK - 1 <= pw0 && shadow_free &&
                           (a.win <= 0 || jc + BK - 1 < a.sink || jc >= pw1 - a.win + 1);
-        if (!full) {
+        if (SH) {
+            // list entry li (position ps) is live for this row iff it is in
+            // the row's key set and read from the shadow for it: a sink
+            // position, or a ring row inside the row's shadow window that
+            // still holds ps (tag bit from one lane per entry)
+            const int lane_li = jc + (lane & 31);
+            const int lane_ps = shl.pos(lane_li);
+            const bool tag_ok = lane_li < shl.nk && lane_ps >= a.sh.sink &&
+                                a.sh.win_pos[lane_ps % kShadowWinMax] == lane_ps;
+            const unsigned tags = (unsigned)__ballot(tag_ok);
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const int kl = 8 * (r >> 2) + 4 * hlf + (r & 3);
+                const int li = jc + kl;
+                const int ps = shl.pos(li);
+                const bool from_shadow =
+                    ps < a.sh.sink || (ps > p_row - a.sh.win && ((tags >> kl) & 1u) != 0);
+                const bool ok = row_live && li < shl.nk && from_shadow &&
+                                in_key_set(ps, p_row, a.sink, a.win);
+                s[r] = ok ? s[r] : -INFINITY;
+            }
+        } else if (!full) {
             // key j is live for this row iff lo_win <= j <= p_row or j < sink_end
             const int hi_key = row_live ? p_row : -1;
             const int lo_win = a.win > 0 ? p_row - a.win + 1 : 0;
@@ -627,20 +721,20 @@ void prefill_kernel(PrefillArgs a) {
     __syncthreads();              // the previous segment no longer reads either buffer
     int buf = 0;
     int ti = t_lo;
-    prefetch_pages(st.tile(ti) * BK);
-    issue_tile(st.tile(ti) * BK, 0);
-    if (PG && ti + 1 < t_hi) prefetch_pages(st.tile(ti + 1) * BK);
+    prefetch_pages(tile_at(ti));
+    issue_tile(tile_at(ti), 0);
+    if (PG && ti + 1 < t_hi) prefetch_pages(tile_at(ti + 1));
     store_tile(0);
     while (ti < t_hi) {
         wait_vmem();
         __syncthreads();
-        const int jc = st.tile(ti) * BK;
+        const int jc = tile_at(ti);
         visited++;
         ti++;
         const bool more = ti < t_hi;
         if (more) {
-            issue_tile(st.tile(ti) * BK, buf ^ 1);
-            if (PG && ti + 1 < t_hi) prefetch_pages(st.tile(ti + 1) * BK);
+            issue_tile(tile_at(ti), buf ^ 1);
+            if (PG && ti + 1 < t_hi) prefetch_pages(tile_at(ti + 1));
         }
         // Every wave computes every tile: for a wave whose rows need none of
         // its keys the tile is fully masked (p = 0, nothing changes). A branch
@@ -655,7 +749,16 @@ void prefill_kernel(PrefillArgs a) {
     const float l_tot = l_run + __shfl_xor(l_run, 32);
     float *op;
     float scale_out;
-    if (whole) {
+    if (whole && SH) {
+        // the row's shadow partial: m, l to the workspace, acc (unnormalised) to out
+        const size_t rf = (size_t)(p_row + sg.tok) * a.n_head + kvh * G + g;
+        op = a.out + rf * HD;
+        scale_out = 1.0f;
+        if (row_live && hlf == 0) {
+            const_cast<float *>(a.sh_m)[rf] = m_run;
+            const_cast<float *>(a.sh_l)[rf] = l_tot;
+        }
+    } else if (whole) {
         const size_t t = (size_t)(p_row + sg.tok);
         op = a.out + (t * a.n_head + kvh * G + g) * HD;
         scale_out = 1.0f / l_tot;
@@ -716,7 +819,7 @@ void prefill_kernel(PrefillArgs a) {
             F += u;
         }
     }
-    if (a.stats && tid == 0) {
+    if (!SH && a.stats && tid == 0) {
         atomicAdd(&a.stats[0], (unsigned long long)visited);
         atomicAdd(&a.stats[1], (unsigned long long)skipped);
     }
@@ -728,7 +831,7 @@ void prefill_kernel(PrefillArgs a) {
 // return at once. Each thread owns 4 consecutive output dims of one row.
 constexpr int kCombineRows = 16;
 
-template <int HD, int G>
+template <int HD, int G, bool SH>
 __global__ __launch_bounds__(256) void prefill_combine_kernel(PrefillArgs a) {
     constexpr int ROWS = kPrefillWaves * kPrefillRowsPerWave;
     constexpr int TPR = HD / 4;                    // threads per row
@@ -748,63 +851,76 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(PrefillArgs a) {
         float L = 0.0f;
         for (int k = 0; k < np; k++) {
             const size_t pr = (size_t)(P + k) * ROWS + row;
-            const float wgt = fast_exp2(a.ws_m[pr] - M);
+            // a piece that saw no key (m = -inf; only shadow-mode rows, whose
+            // shadow keys may all be masked) weighs nothing, also when every
+            // piece is empty
+            const float wgt = a.ws_m[pr] == -INFINITY ? 0.0f : fast_exp2(a.ws_m[pr] - M);
             L += a.ws_l[pr] * wgt;
             o += *(const f32x4 *)(a.ws_acc + pr * HD + 4 * c4) * wgt;
         }
         const int h = c.kvh * G + row % G;
         const size_t t = (size_t)(p + c.tok);
-        *(f32x4 *)(a.out + (t * a.n_head + h) * HD + 4 * c4) = o * (1.0f / L);
-        if (a.lse && c4 == 0) a.lse[(size_t)h * a.n + t] = (M + log2f(L)) * kLn2;
+        if constexpr (SH) {
+            // merged shadow partial, still unnormalised
+            *(f32x4 *)(a.out + (t * a.n_head + h) * HD + 4 * c4) = o;
+            if (c4 == 0) {
+                const_cast<float *>(a.sh_m)[t * a.n_head + h] = M;
+                const_cast<float *>(a.sh_l)[t * a.n_head + h] = L;
+            }
+        } else {
+            *(f32x4 *)(a.out + (t * a.n_head + h) * HD + 4 * c4) = o * (1.0f / L);
+            if (a.lse && c4 == 0) a.lse[(size_t)h * a.n + t] = (M + log2f(L)) * kLn2;
+        }
     }
 }
 
 // Dynamic LDS of a launch: the two K/V buffers, plus the request table of
 // a paged batch.
-template <int HD, int G, int FMT, bool PG>
+template <int HD, int G, int FMT, int MODE>
 size_t lds_bytes(int n_req) {
-    return PrefillShape<HD, G, FMT>::LDS_BYTES + (PG ? (size_t)(4 * n_req + 1) * sizeof(int) : 0);
+    return PrefillShape<HD, G, FMT>::LDS_BYTES +
+           (MODE == kModePaged ? (size_t)(4 * n_req + 1) * sizeof(int) : 0);
 }
 
-template <int HD, int G, int FMT, bool PG>
+template <int HD, int G, int FMT, int MODE>
 hipError_t launch_one(const PrefillArgs &a, hipStream_t s) {
     static bool attr_set = false;   // per process; the attribute is per function
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void *)prefill_kernel<HD, G, FMT, PG>,
+        hipError_t e = hipFuncSetAttribute((const void *)prefill_kernel<HD, G, FMT, MODE>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           (int)lds_bytes<HD, G, FMT, PG>(kPagedMaxReqs));
+                                           (int)lds_bytes<HD, G, FMT, MODE>(kPagedMaxReqs));
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    const size_t lds = lds_bytes<HD, G, FMT, PG>(a.n_req);
-    hipLaunchKernelGGL((prefill_kernel<HD, G, FMT, PG>), dim3(a.n_wg), dim3(256), lds, s, a);
+    const size_t lds = lds_bytes<HD, G, FMT, MODE>(a.n_req);
+    hipLaunchKernelGGL((prefill_kernel<HD, G, FMT, MODE>), dim3(a.n_wg), dim3(256), lds, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     // fewer cut segments than work-groups
-    hipLaunchKernelGGL((prefill_combine_kernel<HD, G>),
+    hipLaunchKernelGGL((prefill_combine_kernel<HD, G, MODE == kModeShadow>),
                        dim3(a.n_wg > 1 ? a.n_wg - 1 : 1,
                             kPrefillWaves * kPrefillRowsPerWave / kCombineRows),
                        dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
-template <int HD, int FMT, bool PG>
+template <int HD, int FMT, int MODE>
 hipError_t by_group(int group, const PrefillArgs &a, hipStream_t s) {
     switch (group) {
-    case 1: return launch_one<HD, 1, FMT, PG>(a, s);
-    case 2: return launch_one<HD, 2, FMT, PG>(a, s);
-    case 4: return launch_one<HD, 4, FMT, PG>(a, s);
-    case 8: return launch_one<HD, 8, FMT, PG>(a, s);
+    case 1: return launch_one<HD, 1, FMT, MODE>(a, s);
+    case 2: return launch_one<HD, 2, FMT, MODE>(a, s);
+    case 4: return launch_one<HD, 4, FMT, MODE>(a, s);
+    case 8: return launch_one<HD, 8, FMT, MODE>(a, s);
     }
     return hipErrorInvalidValue;
 }
 
-template <int FMT, bool PG>
+template <int FMT, int MODE>
 hipError_t by_dim(int head_dim, int group, const PrefillArgs &a, hipStream_t s) {
     switch (head_dim) {
-    case 64: return by_group<64, FMT, PG>(group, a, s);
-    case 128: return by_group<128, FMT, PG>(group, a, s);
-    case 256: return by_group<256, FMT, PG>(group, a, s);
+    case 64: return by_group<64, FMT, MODE>(group, a, s);
+    case 128: return by_group<128, FMT, MODE>(group, a, s);
+    case 256: return by_group<256, FMT, MODE>(group, a, s);
     }
     return hipErrorInvalidValue;
 }
@@ -813,12 +929,16 @@ hipError_t by_dim(int head_dim, int group, const PrefillArgs &a, hipStream_t s) 
 
 hipError_t launch_prefill(int format, int head_dim, int group, const PrefillArgs &a,
                           hipStream_t s) {
-    return format == 0 ? by_dim<0, false>(head_dim, group, a, s)
-                       : by_dim<1, false>(head_dim, group, a, s);
+    return format == 0 ? by_dim<0, kModePlain>(head_dim, group, a, s)
+                       : by_dim<1, kModePlain>(head_dim, group, a, s);
 }
 
 hipError_t launch_paged_prefill(int head_dim, int group, const PrefillArgs &a, hipStream_t s) {
-    return by_dim<0, true>(head_dim, group, a, s);
+    return by_dim<0, kModePaged>(head_dim, group, a, s);
+}
+
+hipError_t launch_shadow_prefill(int head_dim, int group, const PrefillArgs &a, hipStream_t s) {
+    return by_dim<0, kModeShadow>(head_dim, group, a, s);
 }
 
 }  // namespace fa

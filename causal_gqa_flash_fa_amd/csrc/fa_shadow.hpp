@@ -1,6 +1,19 @@
-// Shadow-key partials (see fa_shadow.hip): the work of one single-wave
-// work-group, shared by the standalone shadow pass (prefill) and by the decode
-// partial kernel, which runs these work items in front of its own.
+// Attention over the fp16 shadow keys of a Q4_0 cache, for decode.
+//
+// [FA] "fp16 sink + recent-window exemption" (fc_kvq4_is_fp16 and the fp16
+// read paths of the Q4 decode): for a query at position p, key s is read from
+// the fp16 shadow instead of the Q4_0 body iff s is a sink position or lies
+// in the recent window of p and the window ring still holds it. That key set
+// is small (at most FA_SHADOW_SINK_MAX + FA_SHADOW_WIN_MAX keys) and the same
+// for all heads of a GQA group. A work item folds one query row's shadow keys
+// (intersected with its key set) into a softmax partial {m, l, acc} in the
+// decode kernel's conventions (scores in base-2 units, acc unnormalised); the
+// decode partial kernel runs these items as its first work-groups and its
+// combine merges them. One single-wave work-group per (query, kv head, chunk
+// group): QK with one candidate key per lane (its fp16 row against the G q
+// rows in LDS), online softmax across 64-key chunks, PV with output dims on
+// lanes. (Prefill folds the shadow keys on its MFMA path instead, in the
+// prefill kernel's shadow mode.)
 #pragma once
 
 #include "fa_device.hpp"
