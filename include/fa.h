@@ -158,7 +158,12 @@ int fa_kv_append_slots(const fa_cache *cache, const int *d_pos, int n_slots,
  *   tile_stats: NULL, or device uint64[2] to which the call ADDS the number
  *   of key tiles it visited ([0]) and window-skipped ([1]); tile geometry
  *   from fa_prefill_tile_shape(). Tiles past the causal bound are neither.
- * Rows of q and out must not overlap. Two launches on `stream`. */
+ * With an fp16 shadow, the shadow keys of every query block are folded
+ * first, by a launch of the same kernel over the shadow buffers, and each
+ * row's pass over the Q4_0 body starts from that partial.
+ * Rows of q and out must not overlap. Two launches on `stream` (four with a
+ * shadow); nothing in them depends on host reads of device data, so a
+ * captured HIP graph replays the call. */
 int fa_prefill(const fa_cache *cache, int slot, const float *q, int pos0, int n,
                int n_head, int attn_sink, int attn_win, float scale, float *out,
                void *ws, size_t ws_bytes, unsigned long long *tile_stats, void *stream);
@@ -166,9 +171,10 @@ int fa_prefill(const fa_cache *cache, int slot, const float *q, int pos0, int n,
 /* Workspace fa_prefill needs for n query rows: when a query block's key
  * tiles are spread over several work-groups (the schedule balances the
  * causal triangle across CUs), each part leaves a partial {m, l, acc} per
- * row ([FA] decode partial form) that a second launch merges; plus a table
- * per (kv head, query block). Independent of pos0 and of the data. 0 if an
- * argument is invalid. */
+ * row ([FA] decode partial form) that a second launch merges; plus the list
+ * of such cut blocks (fewer than the work-groups), and, for a cache with an
+ * fp16 shadow, each row's shadow-key m and l. Independent of pos0 and of the
+ * data. 0 if an argument is invalid. */
 size_t fa_prefill_workspace_bytes(int n, int n_head, int n_kv_head, int head_dim);
 
 /* Tile geometry fa_prefill uses for a shape: each work-group owns
