@@ -495,3 +495,24 @@ def test_paged_decode_workload_at_full_size():
         ref_l.append(oracle.gqa_lse(q[s:s + 1], p, kr, 0, 0, w.scale))
     U.compare_rows(got[check], np.stack(refs), U.TOL_F32, w.name)
     assert float(np.abs(got_l[:, check].T - np.stack(ref_l)).max()) <= TOL_LSE
+
+
+def test_paged_attention_at_the_request_cap():
+    # 1024 requests (the cap), hd 256: the request table (16 KB of LDS) sits
+    # beside the largest K/V tile buffers; mostly tiny requests, a few empty,
+    # a few longer, so segments of many requests share work-groups
+    rng = rng_of(2200)
+    R, H, n_kv, hd, bs = 1024, 16, 2, 256, 16
+    lens = rng.integers(0, 4, R)
+    lens[rng.choice(R, 8, replace=False)] = rng.integers(20, 60, 8)
+    ctxs = rng.integers(0, 40, R)
+    reqs = [(int(c), int(n)) for c, n in zip(ctxs, lens)]
+    b = build_batch(rng, reqs, n_kv, hd, H, bs)
+    scale = float(1.0 / np.sqrt(hd))
+    U.log(f"paged attention at the request cap: {R} requests, {b['T']} tokens, "
+          f"{b['num_blocks']} pages")
+    cache, kt, vt = fill_cache(b, bs, n_kv, hd)
+    out, lse = run_paged(cache, b, H, hd, -1, scale)
+    ref, ref_lse = oracle_batch(b, reqs, -1, scale)
+    U.compare_rows(out, ref, U.TOL_F32, "paged at the request cap")
+    assert float(np.abs(lse - ref_lse).max()) <= TOL_LSE
