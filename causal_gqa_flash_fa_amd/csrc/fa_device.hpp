@@ -133,6 +133,17 @@ __device__ __forceinline__ float wave_max(float x) {
     return x;
 }
 
+// max(x[l], x[l ^ 32]) for every lane l. v_permlane32_swap exchanges the
+// two 32-lane halves of a register: each lane receives its own value and its
+// partner's, in an order that depends on the half (lanes below 32 get their
+// own first), which a symmetric max does not see. One VALU instruction, where
+// a shuffle through ds_bpermute is an LDS round trip.
+__device__ __forceinline__ float half_swap_max(float x) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1)

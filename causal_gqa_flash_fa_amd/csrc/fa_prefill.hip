@@ -392,21 +392,24 @@ void prefill_kernel(PrefillArgs a) {
     const uint8_t *kbase = (const uint8_t *)a.k + (size_t)kvh * a.max_seq * RB;
     const uint8_t *vbase = (const uint8_t *)a.v + (size_t)kvh * a.max_seq * RB;
 
-    // Q^T operand: this lane's row, contraction half hlf, pre-scaled.
+    // Q^T operand: this lane's row, contraction half hlf, pre-scaled. Loaded
+    // after the first tile's request, so that the two latencies overlap.
     float qr[HH];
-    if (row_live) {
-        const f32x4 *qp = (const f32x4 *)(a.q + ((size_t)(p_row + sg.tok) * a.n_head +
-                                                 kvh * G + g) * HD + hlf * HH);
+    auto load_q = [&]() {
+        if (row_live) {
+            const f32x4 *qp = (const f32x4 *)(a.q + ((size_t)(p_row + sg.tok) * a.n_head +
+                                                     kvh * G + g) * HD + hlf * HH);
 #pragma unroll
-        for (int i = 0; i < HH / 4; i++) {
-            const f32x4 v = qp[i];
+            for (int i = 0; i < HH / 4; i++) {
+                const f32x4 v = qp[i];
 #pragma unroll
-            for (int t = 0; t < 4; t++) qr[4 * i + t] = v[t] * a.qscale;
+                for (int t = 0; t < 4; t++) qr[4 * i + t] = v[t] * a.qscale;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < HH; i++) qr[i] = 0.0f;
         }
-    } else {
-#pragma unroll
-        for (int i = 0; i < HH; i++) qr[i] = 0.0f;
-    }
+    };
 
     f32x16 O[NT];
 #pragma unroll
@@ -474,6 +477,36 @@ void prefill_kernel(PrefillArgs a) {
         }
     };
 
+    // fp32 tiles of a plain launch: a tile's DMA split by row, so that the
+    // rows of the next tile can be requested between the MFMAs of this
+    // tile's QK (scalar and memory instructions issue while an MFMA runs),
+    // rather than in a burst with no MFMA to hide it. Descriptors cover the
+    // rows of the tile that exist (j0 .. q1); lanes past HD / 4 idle.
+    constexpr bool PLAIN = FMT == 0 && !PG && !SH;
+    constexpr int RPW = BK / Sh::W;               // rows per wave per tensor
+    struct PlainDma {
+        __amdgpu_buffer_rsrc_t rk, rv;
+        float *kd, *vd;
+        int nrows;
+    };
+    auto plain_dma = [&](int j0, int buf) -> PlainDma {
+        PlainDma d;
+        d.kd = lds + buf * Sh::BUF;
+        d.vd = d.kd + BK * KS;
+        d.nrows = min(q1 + 1 - j0, BK);
+        const size_t tile0 = (size_t)j0 * RB;
+        d.rk = raw_rsrc(kbase + tile0, (unsigned)(d.nrows * RB));
+        d.rv = raw_rsrc(vbase + tile0, (unsigned)(d.nrows * RB));
+        return d;
+    };
+    auto plain_row = [&](const PlainDma &d, int i) {
+        if (lane < HD / 4) {
+            const int row = w * RPW + i;
+            const unsigned voff = (unsigned)(min(row, d.nrows - 1) * RB + 16 * lane);
+            dma16(d.rk, voff, d.kd + row * KS);
+            dma16(d.rv, voff, d.vd + row * KS);
+        }
+    };
     auto issue_tile = [&](int j0, int buf) {
         if constexpr (SH) {
             // entries past the list are zero rows (their keys are masked)
@@ -525,24 +558,9 @@ void prefill_kernel(PrefillArgs a) {
                 }
             }
         } else if constexpr (FMT == 0) {
-            constexpr int LPR = HD / 4;           // lanes per row: 16-byte chunks
-            constexpr int RPW = BK / Sh::W;       // rows per wave per tensor
-            float *kd = lds + buf * Sh::BUF;
-            float *vd = kd + BK * KS;
-            // descriptors over the rows of this tile that exist (j0 .. q1)
-            const int nrows = min(q1 + 1 - j0, BK);
-            const size_t tile0 = (size_t)j0 * RB;
-            const __amdgpu_buffer_rsrc_t rk = raw_rsrc(kbase + tile0, (unsigned)(nrows * RB));
-            const __amdgpu_buffer_rsrc_t rv = raw_rsrc(vbase + tile0, (unsigned)(nrows * RB));
-            if (lane < LPR) {
+            const PlainDma d = plain_dma(j0, buf);
 #pragma unroll
-                for (int i = 0; i < RPW; i++) {
-                    const int row = w * RPW + i;
-                    const unsigned voff = (unsigned)(min(row, nrows - 1) * RB + 16 * lane);
-                    dma16(rk, voff, kd + row * KS);
-                    dma16(rv, voff, vd + row * KS);
-                }
-            }
+            for (int i = 0; i < RPW; i++) plain_row(d, i);
         } else {
 #pragma unroll
             for (int i = 0; i < Sh::IPT; i++) {
@@ -607,19 +625,39 @@ void prefill_kernel(PrefillArgs a) {
         }
     };
 
-    auto compute_tile = [&](int jc, int buf) {
+    // Tile at key jc from LDS buffer `buf`. Plain fp32 launches: jn >= 0 is
+    // the next tile, whose rows are requested into buffer buf ^ 1 during QK.
+    auto compute_tile = [&](int jc, int buf, int jn) {
         const float *Ks = lds + buf * Sh::BUF;
         const float *Vs = Ks + BK * KS;
+        // O^T += V^T P^T operands: contraction step kk covers keys
+        // 8*(kk/4) + 4*hlf + kk%4
+        constexpr int NG = NT / GS;
+        using VVec = typename std::conditional<GS == 4, f32x4, f32x2>::type;
+        auto vread = [&](int step) {
+            const int kk = step / NG, ng = step % NG;
+            const int key = 8 * (kk >> 2) + 4 * hlf + (kk & 3);
+            return *(const VVec *)(Vs + key * KS + GS * r32 + ng * 32 * GS);
+        };
+        PlainDma nd{};
+        if constexpr (PLAIN) {
+            if (jn >= 0) nd = plain_dma(jn, buf ^ 1);
+        }
         // S^T = K Q^T: lane holds row r32, keys 8*(r/4) + 4*hlf + r%4
         // LDS reads run one step ahead of the MFMAs that consume them; the
         // scheduling fences keep the compiler from sinking them back.
         f32x16 s = f32x16{};
         const float *krow = Ks + r32 * KS + hlf * HH;
         f32x4 kc = *(const f32x4 *)krow;
+        VVec vc0{};
 #pragma unroll
         for (int i = 0; i < HH / 4; i++) {
             f32x4 kn = kc;
             if (i + 1 < HH / 4) kn = *(const f32x4 *)(krow + 4 * (i + 1));
+            else vc0 = vread(0);       // PV's first operand, read during the last MFMAs
+            if constexpr (PLAIN) {
+                if (jn >= 0 && i < RPW) plain_row(nd, i);
+            }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int t = 0; t < 4; t++) s = mfma32(kc[t], qr[4 * i + t], s);
@@ -670,7 +708,7 @@ void prefill_kernel(PrefillArgs a) {
         float tmax = s[0];
 #pragma unroll
         for (int r = 1; r < 16; r++) tmax = fmaxf(tmax, s[r]);
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        tmax = half_swap_max(tmax);
         // move the reference max only when the tile max passes it by kTau
         // (from -inf: whenever the tile has a live key)
         const bool rebase = tmax > m_run + kTau;
@@ -692,16 +730,8 @@ void prefill_kernel(PrefillArgs a) {
         }
         l_run += psum;
 
-        // O^T += V^T P^T: contraction step kk covers keys 8*(kk/4) + 4*hlf + kk%4
-        // (reads one step ahead, as above)
-        constexpr int NG = NT / GS;
-        using VVec = typename std::conditional<GS == 4, f32x4, f32x2>::type;
-        auto vread = [&](int step) {
-            const int kk = step / NG, ng = step % NG;
-            const int key = 8 * (kk >> 2) + 4 * hlf + (kk & 3);
-            return *(const VVec *)(Vs + key * KS + GS * r32 + ng * 32 * GS);
-        };
-        VVec vc = vread(0);
+        // O^T += V^T P^T (reads one step ahead, as above)
+        VVec vc = vc0;
 #pragma unroll
         for (int step = 0; step < 16 * NG; step++) {
             VVec vn = vc;
@@ -725,6 +755,7 @@ void prefill_kernel(PrefillArgs a) {
     issue_tile(tile_at(ti), 0);
     if (PG && ti + 1 < t_hi) prefetch_pages(tile_at(ti + 1));
     store_tile(0);
+    load_q();
     while (ti < t_hi) {
         wait_vmem();
         __syncthreads();
@@ -732,27 +763,24 @@ void prefill_kernel(PrefillArgs a) {
         visited++;
         ti++;
         const bool more = ti < t_hi;
-        if (more) {
+        if (more && !PLAIN) {
             issue_tile(tile_at(ti), buf ^ 1);
             if (PG && ti + 1 < t_hi) prefetch_pages(tile_at(ti + 1));
         }
         // Every wave computes every tile: for a wave whose rows need none of
         // its keys the tile is fully masked (p = 0, nothing changes). A branch
         // here would make the compiler carry O through VGPR copies.
-        compute_tile(jc, buf);
+        compute_tile(jc, buf, PLAIN && more ? tile_at(ti) : -1);
         if (more) store_tile(buf ^ 1);
         buf ^= 1;
     }
 
-    // ---- finalise: out = acc / l (whole segment) or this piece's partial,
-    // scattered back through the d permutation
+    // ---- finalise: out = acc / l (whole segment) or this piece's partial
     const float l_tot = l_run + __shfl_xor(l_run, 32);
-    float *op;
     float scale_out;
     if (whole && SH) {
         // the row's shadow partial: m, l to the workspace, acc (unnormalised) to out
         const size_t rf = (size_t)(p_row + sg.tok) * a.n_head + kvh * G + g;
-        op = a.out + rf * HD;
         scale_out = 1.0f;
         if (row_live && hlf == 0) {
             const_cast<float *>(a.sh_m)[rf] = m_run;
@@ -760,34 +788,61 @@ void prefill_kernel(PrefillArgs a) {
         }
     } else if (whole) {
         const size_t t = (size_t)(p_row + sg.tok);
-        op = a.out + (t * a.n_head + kvh * G + g) * HD;
         scale_out = 1.0f / l_tot;
         // ln sum exp(scale q.k) = ln 2 * (m + log2 l): m is in base-2 units
         if (a.lse && row_live && hlf == 0)
             a.lse[(size_t)(kvh * G + g) * a.n + t] = (m_run + log2f(l_tot)) * kLn2;
     } else {
         const size_t prow = (size_t)piece * ROWS + row_wg;
-        op = a.ws_acc + prow * HD;
         scale_out = 1.0f;
         if (hlf == 0) {
             a.ws_m[prow] = m_run;
             a.ws_l[prow] = l_tot;
         }
     }
-    if (row_live || !whole) {
+    // O leaves through LDS. A lane's registers hold 16-byte pieces of its
+    // own row (through the d permutation), so direct stores would touch 64
+    // rows per instruction; staged as rows of stride KS, each store
+    // instruction writes whole rows (HD contiguous floats). The staging area
+    // is the tile buffers (W * R rows = 4 * BK rows), free once every wave
+    // is past the last tile; the next segment's first barrier orders the
+    // read-back below before the buffers are refilled.
+    __syncthreads();
+    float *stg = lds + (size_t)w * Sh::R * KS;
 #pragma unroll
-        for (int r = 0; r < 16; r++) {
-            const int mi = 8 * (r >> 2) + 4 * hlf + (r & 3);
+    for (int r = 0; r < 16; r++) {
+        const int mi = 8 * (r >> 2) + 4 * hlf + (r & 3);
 #pragma unroll
-            for (int ng = 0; ng < NT / GS; ng++) {
-                float *dst = op + ng * 32 * GS + GS * mi;
-                if constexpr (GS == 4) {
-                    *(f32x4 *)dst = f32x4{O[ng * 4 + 0][r], O[ng * 4 + 1][r], O[ng * 4 + 2][r],
-                                          O[ng * 4 + 3][r]} * scale_out;
-                } else {
-                    *(f32x2 *)dst = f32x2{O[ng * 2 + 0][r], O[ng * 2 + 1][r]} * scale_out;
-                }
+        for (int ng = 0; ng < NT / GS; ng++) {
+            float *dst = stg + r32 * KS + ng * 32 * GS + GS * mi;
+            if constexpr (GS == 4) {
+                *(f32x4 *)dst = f32x4{O[ng * 4 + 0][r], O[ng * 4 + 1][r], O[ng * 4 + 2][r],
+                                      O[ng * 4 + 3][r]} * scale_out;
+            } else {
+                *(f32x2 *)dst = f32x2{O[ng * 2 + 0][r], O[ng * 2 + 1][r]} * scale_out;
             }
+        }
+    }
+    wave_lds_sync();
+    {
+        constexpr int LPR = HD / 4;            // lanes per row (16 bytes each)
+        constexpr int RPI = 64 / LPR;          // rows per store instruction
+        const int rsub = lane / LPR, c4 = lane % LPR;
+#pragma unroll
+        for (int i = 0; i < Sh::R / RPI; i++) {
+            const int rr = i * RPI + rsub;     // row within the wave
+            const int rw = w * Sh::R + rr;     // row within the work-group
+            const f32x4 v = *(const f32x4 *)(stg + rr * KS + 4 * c4);
+            float *dst;
+            bool live = true;
+            if (whole) {
+                const int pr = q0 + rw / G;
+                live = pr <= q1;
+                dst = a.out + (((size_t)(pr + sg.tok)) * a.n_head + kvh * G + rw % G) * HD;
+            } else {
+                dst = a.ws_acc + ((size_t)piece * ROWS + rw) * HD;
+            }
+            if (live) *(f32x4 *)(dst + 4 * c4) = v;
         }
     }
     };   // run_segment
