@@ -160,6 +160,15 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Work-group barrier that orders LDS accesses only: the wave's LDS
+// operations complete before it arrives, while global loads and stores stay
+// in flight across it (a full __syncthreads waits for those too).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Key-set membership ([FA] file header): causal, plus sink U recent window
 // when attn_win > 0.
 __device__ __forceinline__ bool in_key_set(int j, int p, int sink, int win) {

@@ -748,7 +748,7 @@ void prefill_kernel(PrefillArgs a) {
     // Double-buffered walk, one barrier per tile: the barrier makes tile ti
     // (buffer buf) visible and guarantees every wave is done with buf ^ 1,
     // which then receives tile ti + 1 while tile ti is computed.
-    __syncthreads();              // the previous segment no longer reads either buffer
+    lds_barrier();                // the previous segment no longer reads either buffer
     int buf = 0;
     int ti = t_lo;
     prefetch_pages(tile_at(ti));
@@ -806,8 +806,9 @@ void prefill_kernel(PrefillArgs a) {
     // instruction writes whole rows (HD contiguous floats). The staging area
     // is the tile buffers (W * R rows = 4 * BK rows), free once every wave
     // is past the last tile; the next segment's first barrier orders the
-    // read-back below before the buffers are refilled.
-    __syncthreads();
+    // read-back below before the buffers are refilled. Both barriers order
+    // LDS only; this segment's output stores stay in flight.
+    lds_barrier();
     float *stg = lds + (size_t)w * Sh::R * KS;
 #pragma unroll
     for (int r = 0; r < 16; r++) {
