@@ -477,34 +477,60 @@ void prefill_kernel(PrefillArgs a) {
         }
     };
 
-    // fp32 tiles of a plain launch: a tile's DMA split by row, so that the
-    // rows of the next tile can be requested between the MFMAs of this
-    // tile's QK (scalar and memory instructions issue while an MFMA runs),
-    // rather than in a burst with no MFMA to hide it. Descriptors cover the
-    // rows of the tile that exist (j0 .. q1); lanes past HD / 4 idle.
-    constexpr bool PLAIN = FMT == 0 && !PG && !SH;
+    // fp32 tiles (plain and paged launches): a tile's DMA split by row, so
+    // that the rows of the next tile can be requested between the MFMAs of
+    // this tile's QK (scalar and memory instructions issue while an MFMA
+    // runs), rather than in a burst with no MFMA to hide it. Lanes past
+    // HD / 4 idle.
+    //  * plain: descriptors over the rows of the tile that exist (j0 .. q1);
+    //  * paged: one descriptor per row (pages need not be adjacent), from the
+    //    byte offset of tile row r held by lane r (page ids outside the cache
+    //    clamped into it). Row r's lane need not be a copying lane (HD = 64:
+    //    16 of them for 32 rows), so the offsets are computed, and read out,
+    //    with every lane active: a readlane may not sit inside the copying
+    //    lanes' branch.
+    constexpr bool SPLIT = FMT == 0 && !SH;
     constexpr int RPW = BK / Sh::W;               // rows per wave per tensor
-    struct PlainDma {
-        __amdgpu_buffer_rsrc_t rk, rv;
+    struct RowDma {
+        __amdgpu_buffer_rsrc_t rk, rv;            // plain
         float *kd, *vd;
-        int nrows;
+        int nrows;                                // plain
+        int olo, ohi;                             // paged: this lane's tile row offset
     };
-    auto plain_dma = [&](int j0, int buf) -> PlainDma {
-        PlainDma d;
+    auto row_dma = [&](int j0, int buf) -> RowDma {
+        RowDma d{};
         d.kd = lds + buf * Sh::BUF;
         d.vd = d.kd + BK * KS;
-        d.nrows = min(q1 + 1 - j0, BK);
-        const size_t tile0 = (size_t)j0 * RB;
-        d.rk = raw_rsrc(kbase + tile0, (unsigned)(d.nrows * RB));
-        d.rv = raw_rsrc(vbase + tile0, (unsigned)(d.nrows * RB));
+        if constexpr (PG) {
+            const long long pg = min(max(pf_page, 0), a.num_blocks - 1);
+            const long long off =
+                (pg * a.blk_stride + ((long long)pf_row * a.n_kv + kvh) * HD) * (long long)sizeof(float);
+            d.olo = (int)(uint32_t)off;
+            d.ohi = (int)(uint32_t)((unsigned long long)off >> 32);
+        } else {
+            d.nrows = min(q1 + 1 - j0, BK);
+            const size_t tile0 = (size_t)j0 * RB;
+            d.rk = raw_rsrc(kbase + tile0, (unsigned)(d.nrows * RB));
+            d.rv = raw_rsrc(vbase + tile0, (unsigned)(d.nrows * RB));
+        }
         return d;
     };
-    auto plain_row = [&](const PlainDma &d, int i) {
-        if (lane < HD / 4) {
-            const int row = w * RPW + i;
-            const unsigned voff = (unsigned)(min(row, d.nrows - 1) * RB + 16 * lane);
-            dma16(d.rk, voff, d.kd + row * KS);
-            dma16(d.rv, voff, d.vd + row * KS);
+    auto issue_row = [&](const RowDma &d, int i) {
+        const int row = w * RPW + i;
+        if constexpr (PG) {
+            const unsigned long long o =
+                ((unsigned long long)(uint32_t)__builtin_amdgcn_readlane(d.ohi, row) << 32) |
+                (uint32_t)__builtin_amdgcn_readlane(d.olo, row);
+            if (lane < HD / 4) {
+                dma16(raw_rsrc((const uint8_t *)a.k + o, (unsigned)RB), 16 * lane, d.kd + row * KS);
+                dma16(raw_rsrc((const uint8_t *)a.v + o, (unsigned)RB), 16 * lane, d.vd + row * KS);
+            }
+        } else {
+            if (lane < HD / 4) {
+                const unsigned voff = (unsigned)(min(row, d.nrows - 1) * RB + 16 * lane);
+                dma16(d.rk, voff, d.kd + row * KS);
+                dma16(d.rv, voff, d.vd + row * KS);
+            }
         }
     };
     auto issue_tile = [&](int j0, int buf) {
@@ -529,38 +555,10 @@ void prefill_kernel(PrefillArgs a) {
                     sraw[i] = u32x4{0u, 0u, 0u, 0u};
                 }
             }
-        } else if constexpr (FMT == 0 && PG) {
-            constexpr int LPR = HD / 4;
-            constexpr int RPW = BK / Sh::W;
-            float *kd = lds + buf * Sh::BUF;
-            float *vd = kd + BK * KS;
-            // one descriptor per row (pages need not be adjacent); page ids
-            // outside the cache are clamped into it
-            const long long pg = min(max(pf_page, 0), a.num_blocks - 1);
-            const long long off =
-                (pg * a.blk_stride + ((long long)pf_row * a.n_kv + kvh) * HD) * (long long)sizeof(float);
-            const int olo = (int)(uint32_t)off, ohi = (int)(uint32_t)((unsigned long long)off >> 32);
-            // Row r's offset lives in lane r, which need not be one of the
-            // LPR copying lanes (HD = 64: 16 of them for 32 rows). The
-            // readlanes therefore stay outside the lane < LPR branch: a
-            // readlane may not be moved into a branch, so the offsets are
-            // computed with every lane active rather than only in the
-            // copying lanes.
-#pragma unroll
-            for (int i = 0; i < RPW; i++) {
-                const int row = w * RPW + i;
-                const unsigned long long o =
-                    ((unsigned long long)(uint32_t)__builtin_amdgcn_readlane(ohi, row) << 32) |
-                    (uint32_t)__builtin_amdgcn_readlane(olo, row);
-                if (lane < LPR) {
-                    dma16(raw_rsrc((const uint8_t *)a.k + o, (unsigned)RB), 16 * lane, kd + row * KS);
-                    dma16(raw_rsrc((const uint8_t *)a.v + o, (unsigned)RB), 16 * lane, vd + row * KS);
-                }
-            }
         } else if constexpr (FMT == 0) {
-            const PlainDma d = plain_dma(j0, buf);
+            const RowDma d = row_dma(j0, buf);
 #pragma unroll
-            for (int i = 0; i < RPW; i++) plain_row(d, i);
+            for (int i = 0; i < RPW; i++) issue_row(d, i);
         } else {
 #pragma unroll
             for (int i = 0; i < Sh::IPT; i++) {
@@ -625,9 +623,9 @@ void prefill_kernel(PrefillArgs a) {
         }
     };
 
-    // Tile at key jc from LDS buffer `buf`. Plain fp32 launches: jn >= 0 is
-    // the next tile, whose rows are requested into buffer buf ^ 1 during QK.
-    auto compute_tile = [&](int jc, int buf, int jn) {
+    // Tile at key jc from LDS buffer `buf`. fp32 launches with `dma`: the
+    // next tile's rows (`nd`) are requested into buffer buf ^ 1 during QK.
+    auto compute_tile = [&](int jc, int buf, bool dma, const RowDma &nd) {
         const float *Ks = lds + buf * Sh::BUF;
         const float *Vs = Ks + BK * KS;
         // O^T += V^T P^T operands: contraction step kk covers keys
@@ -639,10 +637,6 @@ void prefill_kernel(PrefillArgs a) {
             const int key = 8 * (kk >> 2) + 4 * hlf + (kk & 3);
             return *(const VVec *)(Vs + key * KS + GS * r32 + ng * 32 * GS);
         };
-        PlainDma nd{};
-        if constexpr (PLAIN) {
-            if (jn >= 0) nd = plain_dma(jn, buf ^ 1);
-        }
         // S^T = K Q^T: lane holds row r32, keys 8*(r/4) + 4*hlf + r%4
         // LDS reads run one step ahead of the MFMAs that consume them; the
         // scheduling fences keep the compiler from sinking them back.
@@ -655,8 +649,8 @@ void prefill_kernel(PrefillArgs a) {
             f32x4 kn = kc;
             if (i + 1 < HH / 4) kn = *(const f32x4 *)(krow + 4 * (i + 1));
             else vc0 = vread(0);       // PV's first operand, read during the last MFMAs
-            if constexpr (PLAIN) {
-                if (jn >= 0 && i < RPW) plain_row(nd, i);
+            if constexpr (SPLIT) {
+                if (dma && i < RPW) issue_row(nd, i);
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -763,14 +757,18 @@ void prefill_kernel(PrefillArgs a) {
         visited++;
         ti++;
         const bool more = ti < t_hi;
-        if (more && !PLAIN) {
-            issue_tile(tile_at(ti), buf ^ 1);
+        RowDma nd{};
+        if (more) {
+            // fp32: the row offsets now (paged: from the pages read a tile
+            // ahead), the requests during QK
+            if constexpr (SPLIT) nd = row_dma(tile_at(ti), buf ^ 1);
+            else issue_tile(tile_at(ti), buf ^ 1);
             if (PG && ti + 1 < t_hi) prefetch_pages(tile_at(ti + 1));
         }
         // Every wave computes every tile: for a wave whose rows need none of
         // its keys the tile is fully masked (p = 0, nothing changes). A branch
         // here would make the compiler carry O through VGPR copies.
-        compute_tile(jc, buf, PLAIN && more ? tile_at(ti) : -1);
+        compute_tile(jc, buf, SPLIT && more, nd);
         if (more) store_tile(buf ^ 1);
         buf ^= 1;
     }
