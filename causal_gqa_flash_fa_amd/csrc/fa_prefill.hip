@@ -32,8 +32,11 @@
 //   * K/V tiles are double-buffered in LDS with one barrier per tile: fp32
 //     rows go straight from global memory into the next buffer
 //     (buffer_load_dwordx4 ... lds, one row per wave instruction, so no staging
-//     registers), Q4_0 blocks are staged in registers and decoded into the
-//     next buffer after the current tile's matrix work.
+//     registers), requested row by row between the current tile's QK MFMAs;
+//     Q4_0 blocks are staged in registers and decoded into the next buffer
+//     after the current tile's matrix work.
+//   * Output rows leave through LDS (the tile buffers, free after the last
+//     tile), so that every store instruction writes whole contiguous rows.
 //   * Lazy rescale: a row's reference max only moves when a tile's max
 //     exceeds it by more than kTau (log2 units). Probabilities are then
 //     bounded by 2^kTau, and the O rescale (a pass over all accumulators)
