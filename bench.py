@@ -94,6 +94,15 @@ def _events(torch, n):
             for _ in range(n)]
 
 
+def spread(kms, key: str) -> dict:
+    """Median, 90th percentile and relative standard deviation of the per-call
+    HIP-event times `kms` (ms); the leg's headline figure stays the mean, the
+    average launch duration the roofline is defined on."""
+    a = np.asarray(kms, dtype=np.float64)
+    return {key + "_median": float(np.median(a)), key + "_p90": float(np.percentile(a, 90)),
+            key + "_rel_std": float(np.std(a) / np.mean(a))}
+
+
 def prefill_leg(fa, torch, w, steps: int, warmup: int, graph: bool = False) -> dict:
     """Append + prefill of one workload. Kernel time: HIP events around each
     eager fa_prefill. Step time: the same two calls launched eagerly, or, with
@@ -156,6 +165,7 @@ def prefill_leg(fa, torch, w, steps: int, warmup: int, graph: bool = False) -> d
         "launch": "hip_graph" if graph else "eager", "ms_per_step_eager": eager_ms,
         "flops": flops, "ms_per_step": step_ms, "tflops_step": flops / step_ms / 1e9,
         "prefill_kernel_ms": kern_ms, "prefill_kernel_ms_min": float(np.min(kms)),
+        **spread(kms, "prefill_kernel_ms"),
         "tflops_kernel": flops / kern_ms / 1e9,
         "frac_fp32_mfma_peak": flops / kern_ms / 1e9 / PEAK_FP32_MFMA_TFLOPS,
     }
@@ -227,6 +237,7 @@ def paged_leg(fa, torch, w, steps: int, warmup: int) -> dict:
         "n_head": w.n_head, "n_kv_head": w.n_kv_head, "head_dim": w.head_dim,
         "flops": flops, "ms_per_step": step_ms, "tflops_step": flops / step_ms / 1e9,
         "attention_kernel_ms": kern_ms, "attention_kernel_ms_min": float(np.min(kms)),
+        **spread(kms, "attention_kernel_ms"),
         "tflops_kernel": flops / kern_ms / 1e9,
         "frac_fp32_mfma_peak": flops / kern_ms / 1e9 / PEAK_FP32_MFMA_TFLOPS,
     }
@@ -280,8 +291,8 @@ def paged_decode_leg(fa, torch, w, steps: int, warmup: int) -> dict:
     gbs = nbytes / ms / 1e6
     return {"workload": w.name, "kind": "paged_decode", "kv": "f32", "requests": w.n_slots,
             "block_size": bs, "num_blocks": num_blocks, "ctx_sum": int(ctx.sum()),
-            "bytes": nbytes, "decode_ms": ms, "decode_ms_min": float(np.min(kms)), "gbs": gbs,
-            "frac_hbm_peak": gbs / PEAK_HBM_GBS}
+            "bytes": nbytes, "decode_ms": ms, "decode_ms_min": float(np.min(kms)),
+            **spread(kms, "decode_ms"), "gbs": gbs, "frac_hbm_peak": gbs / PEAK_HBM_GBS}
 
 
 def merge_leg(fa, torch, steps: int, warmup: int, T: int = 8192, H: int = 16,
@@ -310,7 +321,7 @@ def merge_leg(fa, torch, steps: int, warmup: int, T: int = 8192, H: int = 16,
     ms = float(np.mean(kms))
     rec = measured_traffic("merge", "merge-attn-states")
     return {"workload": f"merge-attn-states-{T}x{H}x{D}", "kind": "merge", "bytes": nbytes,
-            "kernel_ms": ms, "kernel_ms_min": float(np.min(kms)),
+            "kernel_ms": ms, "kernel_ms_min": float(np.min(kms)), **spread(kms, "kernel_ms"),
             "gbs": nbytes / ms / 1e6, "frac_hbm_peak": nbytes / ms / 1e6 / PEAK_HBM_GBS,
             "traffic_bytes": round(rec["traffic_bytes"]) if rec else None}
 
@@ -362,8 +373,8 @@ def decode_leg(fa, torch, w, steps: int, warmup: int) -> dict:
         "ctx_max": int(ctx.max()), "launch_splits": fa.fa_decode_plan(hint)[0],
         "shadow_sink": w.shadow_sink, "shadow_win": w.shadow_win,
         "kv_bytes": kv_bytes, "bytes": kv_bytes + qo_bytes, "flops": flops,
-        "decode_ms": ms, "decode_ms_min": float(np.min(kms)), "gbs": gbs,
-        "frac_hbm_peak": gbs / PEAK_HBM_GBS, "tflops": flops / ms / 1e9,
+        "decode_ms": ms, "decode_ms_min": float(np.min(kms)), **spread(kms, "decode_ms"),
+        "gbs": gbs, "frac_hbm_peak": gbs / PEAK_HBM_GBS, "tflops": flops / ms / 1e9,
         "fp32_compute_ceiling_gbs": compute_ceiling_gbs,
         "frac_of_min_ceiling": gbs / min(PEAK_HBM_GBS, compute_ceiling_gbs),
         "traffic_bytes": (round(rec["traffic_bytes"]) if (rec := measured_traffic("decode", w.name))

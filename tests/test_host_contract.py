@@ -83,3 +83,10 @@ def test_generators_are_deterministic_and_distinct():
     assert not np.array_equal(a[0], a[1])                        # K and V differ
     f32 = workloads.BY_NAME["decode-64slots-f32kv"]
     assert np.array_equal(workloads.decode_kv(f32, 3, 50)[0], a[0])   # same inputs as the Q4_0 run
+
+
+def test_spread_reports_median_p90_and_relative_std():
+    got = bench.spread([2.0, 1.0, 4.0, 3.0], "t")
+    assert got["t_median"] == 2.5
+    assert abs(got["t_p90"] - 3.7) < 1e-12                        # linear interpolation
+    assert abs(got["t_rel_std"] - np.std([1, 2, 3, 4]) / 2.5) < 1e-12
