@@ -738,32 +738,63 @@ void decode_partial_kernel(DecodeArgs a) {
 }
 
 // out = sum_r exp2(m_r - M) acc_r / sum_r exp2(m_r - M) l_r over the
-// segment's partials in ascending order.
+// segment's partials in ascending order, then its fp16-shadow partials. The
+// partials are read in chunks of CH with predicated loads, every load of a
+// chunk in flight at once (a loop over the partials would wait for each
+// load in turn). A chunk is summed against the running max M including the
+// chunk's own partials; when a later chunk (or the shadow partials) raises
+// M, the sums so far are rescaled by exp2(M_old - M_new). With at most CH
+// partials this is exactly the two-pass form: one max, then the weighted
+// sums in ascending order.
 template <int HD, int G>
 __global__ __launch_bounds__(HD) void decode_combine_kernel(DecodeArgs a) {
+    constexpr int CH = 32;
     const int gh = blockIdx.x;              // slot * n_head + head
     const int slot = gh / a.n_head, h = gh % a.n_head;
     const int seg = slot * a.n_kv + h / G, g = h % G;
     const int P = a.seg_table[2 * seg], n = a.seg_table[2 * seg + 1];
     const int dd = threadIdx.x;
-    float M = -INFINITY;
-#pragma unroll 8
-    for (int r = 0; r < n; r++) M = fmaxf(M, a.ws_m[(size_t)(P + r) * G + g]);
-    for (int c = 0; c < a.sh_groups; c++)   // fp16-shadow partials of the segment
-        M = fmaxf(M, a.sh_m[((size_t)seg * a.sh_groups + c) * G + g]);
-    // unrolled so that several partials' loads are in flight at once; the
-    // sums still run in ascending partial order
-    float o = 0.0f, L = 0.0f;
-#pragma unroll 8
-    for (int r = 0; r < n; r++) {
-        const size_t pi = (size_t)(P + r) * G + g;
-        const float wgt = fast_exp2(a.ws_m[pi] - M);
-        L += a.ws_l[pi] * wgt;
-        o += a.ws_acc[pi * HD + dd] * wgt;
+    float M = -INFINITY, o = 0.0f, L = 0.0f;
+    // move the reference max up to m_new, rescaling the sums so far
+    auto rebase = [&](float m_new) {
+        if (m_new > M) {
+            const float cs = M == -INFINITY ? 0.0f : fast_exp2(M - m_new);
+            L *= cs;
+            o *= cs;
+            M = m_new;
+        }
+    };
+    for (int r0 = 0; r0 < n; r0 += CH) {
+        float mv[CH], lv[CH], xv[CH];
+#pragma unroll
+        for (int u = 0; u < CH; u++) {
+            const size_t pi = (size_t)(P + r0 + u) * G + g;
+            const bool ok = r0 + u < n;
+            mv[u] = ok ? a.ws_m[pi] : -INFINITY;
+            lv[u] = ok ? a.ws_l[pi] : 0.0f;
+            xv[u] = ok ? a.ws_acc[pi * HD + dd] : 0.0f;
+        }
+        float cm = mv[0];
+#pragma unroll
+        for (int u = 1; u < CH; u++) cm = fmaxf(cm, mv[u]);
+        rebase(cm);
+#pragma unroll
+        for (int u = 0; u < CH; u++) {
+            if (r0 + u < n) {
+                // an empty partial (m = -inf: a split whose keys all come from
+                // the fp16 shadow) weighs 0, also while M is still -inf
+                const float wgt = mv[u] == -INFINITY ? 0.0f : fast_exp2(mv[u] - M);
+                L += lv[u] * wgt;
+                o += xv[u] * wgt;
+            }
+        }
     }
-    for (int c = 0; c < a.sh_groups; c++) {
+    for (int c = 0; c < a.sh_groups; c++) {   // fp16-shadow partials of the segment
         const size_t pi = ((size_t)seg * a.sh_groups + c) * G + g;
-        const float wgt = a.sh_m[pi] == -INFINITY ? 0.0f : fast_exp2(a.sh_m[pi] - M);
+        const float m = a.sh_m[pi];
+        if (m == -INFINITY) continue;            // no shadow key: weight 0
+        rebase(m);
+        const float wgt = fast_exp2(m - M);
         L += a.sh_l[pi] * wgt;
         o += a.sh_acc[pi * HD + dd] * wgt;
     }
