@@ -138,9 +138,10 @@ __device__ __forceinline__ SegTiles seg_tiles(int q0, int q1, int sink, int win,
 
 constexpr int kXcds = 8;   // XCDs of an MI355X; block b runs on XCD b % 8
 // Schedule units: a tile is kTileUnits units and starting a segment costs
-// kSegUnits more (measured: switching segments costs ~11 us, about 1.2 times
-// a ~9 us tile, mostly the output stores and the next Q load hitting HBM at
-// once). A tile belongs to the run that holds its first unit.
+// kSegUnits more (measured: a segment switch, output stores plus the next Q
+// load and first-tile latency, costs about one ~9 us tile; 4, 5 and 6 units
+// time the same within noise). A tile belongs to the run that holds its
+// first unit.
 constexpr int kTileUnits = 4;
 constexpr int kSegUnits = 5;
 
