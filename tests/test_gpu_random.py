@@ -1,7 +1,8 @@
 """Seeded random configurations through the prefill, decode and paged paths,
-against the oracle: head shapes, GQA groups, row counts, offsets, sinks,
-windows, cache formats, block sizes and request mixes drawn from fixed seeds,
-beyond the hand-picked sweeps. Each case logs its parameters before it runs.
+with and without the fp16 shadow of a Q4_0 cache, against the oracle: head
+shapes, GQA groups, row counts, offsets, sinks, windows, shadow sizes, cache
+formats, block sizes and request mixes drawn from fixed seeds, beyond the
+hand-picked sweeps. Each case logs its parameters before it runs.
 The oracle sees only the seeded host inputs.
 """
 import numpy as np
@@ -19,6 +20,7 @@ if torch.cuda.device_count() == 0:
 import causal_gqa_flash_fa_amd as fa  # noqa: E402
 from tests import test_gpu_paged as T  # noqa: E402
 from tests import test_gpu_parity as P  # noqa: E402
+from tests import test_gpu_shadow as S  # noqa: E402
 
 
 def _prefill_cases(seed: int, count: int):
@@ -68,9 +70,49 @@ def _paged_cases(seed: int, count: int):
     return cases
 
 
+def _shadow_sizes(rng):
+    """fp16 shadow of a Q4_0 cache: sink 0..8, window 0..256, not both 0."""
+    ssink = int(rng.integers(0, 9))
+    swin = int(rng.integers(1 if ssink == 0 else 0, 257))
+    return ssink, swin
+
+
+def _shadow_prefill_cases(seed: int, count: int):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    cases = []
+    for _ in range(count):
+        hd = int(rng.choice([64, 128, 256]))
+        Hkv = int(rng.choice([1, 2]))
+        H = Hkv * int(rng.choice([1, 2, 4, 8]))
+        n = int(rng.integers(1, 500))
+        pos0 = int(rng.integers(0, 300)) if rng.random() < 0.5 else 0
+        ssink, swin = _shadow_sizes(rng)
+        awin = int(rng.integers(1, 400)) if rng.random() < 0.3 else 0
+        asink = int(rng.integers(0, 9)) if awin else 0
+        cases.append((n, pos0, H, Hkv, hd, ssink, swin, asink, awin))
+    return cases
+
+
+def _shadow_decode_cases(seed: int, count: int):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    cases = []
+    for _ in range(count):
+        hd = int(rng.choice([64, 128, 256]))
+        Hkv = int(rng.choice([1, 2]))
+        H = Hkv * int(rng.choice([1, 2, 4, 8]))
+        ssink, swin = _shadow_sizes(rng)
+        awin = int(rng.integers(1, 2000)) if rng.random() < 0.3 else 0
+        asink = int(rng.integers(0, 9)) if awin else 0
+        ctx = tuple(int(rng.integers(1, 3000)) for _ in range(int(rng.integers(1, 5))))
+        cases.append((H, Hkv, hd, ssink, swin, asink, awin, ctx))
+    return cases
+
+
 PREFILL_CASES = _prefill_cases(20261202, 12)
 DECODE_CASES = _decode_cases(20261203, 8)
 PAGED_CASES = _paged_cases(20261204, 8)
+SHADOW_PREFILL_CASES = _shadow_prefill_cases(20261205, 6)
+SHADOW_DECODE_CASES = _shadow_decode_cases(20261206, 6)
 
 
 @pytest.mark.parametrize("case", PREFILL_CASES, ids=[str(c) for c in PREFILL_CASES])
@@ -123,3 +165,59 @@ def test_random_paged(case):
     if all(ql == 1 for _, ql in reqs) and bs % 16 == 0:
         out_d, _ = T.run_paged_decode(cache, b, H, hd, window_left, scale)
         U.compare_rows(out_d, ref, U.TOL_F32, f"random paged decode {case[:5]}")
+
+
+@pytest.mark.parametrize("case", SHADOW_PREFILL_CASES, ids=[str(c) for c in SHADOW_PREFILL_CASES])
+def test_random_prefill_with_shadow(case):
+    n, pos0, H, Hkv, hd, ssink, swin, asink, awin = case
+    seed = 80000 + SHADOW_PREFILL_CASES.index(case)
+    rng = np.random.Generator(np.random.PCG64(seed))
+    L = pos0 + n
+    q = rng.standard_normal((n, H, hd)).astype(np.float32)
+    k = rng.standard_normal((L, Hkv, hd)).astype(np.float32)
+    v = rng.standard_normal((L, Hkv, hd)).astype(np.float32)
+    scale = float(1 / np.sqrt(hd))
+    U.log(f"random prefill with shadow {case} seed={seed}")
+    cache, kt, vt = fa.make_cache(fa.FA_KV_Q4_0, 1, Hkv, hd, L + 3, U.device())
+    bufs = fa.add_shadow(cache, ssink, swin, U.device())
+    if pos0:
+        fa.fa_kv_append(cache, 0, 0, pos0, U.to_dev(k[:pos0]), U.to_dev(v[:pos0]))
+    fa.fa_kv_append(cache, 0, pos0, n, U.to_dev(k[pos0:]), U.to_dev(v[pos0:]))
+    ws_bytes = fa.fa_prefill_workspace_bytes(n, H, Hkv, hd)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=U.device())
+    out = torch.full((n, H, hd), float("nan"), device=U.device())
+    fa.fa_prefill(cache, 0, U.to_dev(q), pos0, n, H, asink, awin, scale, out, ws, ws_bytes)
+    torch.cuda.synchronize()
+    gpu = out.cpu().numpy()
+    qpos = np.arange(pos0, L, dtype=np.int32)
+    ref = S.shadow_reference(q, qpos, k, v, hd, asink, awin, scale, ssink, swin, L - 1)
+    U.compare_rows(gpu, ref.reshape(gpu.shape), U.TOL_Q4, f"random prefill shadow {case}")
+    del bufs
+
+
+@pytest.mark.parametrize("case", SHADOW_DECODE_CASES, ids=[str(c[:7]) for c in SHADOW_DECODE_CASES])
+def test_random_decode_with_shadow(case):
+    H, Hkv, hd, ssink, swin, asink, awin, ctx = case
+    seed = 90000 + SHADOW_DECODE_CASES.index(case)
+    rng = np.random.Generator(np.random.PCG64(seed))
+    n = len(ctx)
+    q = rng.standard_normal((n, H, hd)).astype(np.float32)
+    ks = [rng.standard_normal((c, Hkv, hd)).astype(np.float32) for c in ctx]
+    vs = [rng.standard_normal((c, Hkv, hd)).astype(np.float32) for c in ctx]
+    scale = float(1 / np.sqrt(hd))
+    U.log(f"random decode with shadow {case} seed={seed}")
+    cache, kt, vt = fa.make_cache(fa.FA_KV_Q4_0, n, Hkv, hd, max(ctx) + 2, U.device())
+    bufs = fa.add_shadow(cache, ssink, swin, U.device())
+    for s in range(n):
+        fa.fa_kv_append(cache, s, 0, ctx[s], U.to_dev(ks[s]), U.to_dev(vs[s]))
+    ws_bytes = fa.fa_decode_workspace_bytes(cache, n, H, max(ctx))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=U.device())
+    out = torch.full((n, H, hd), float("nan"), device=U.device())
+    pos = U.to_dev(np.array(ctx, np.int32) - 1)
+    fa.fa_decode(cache, U.to_dev(q), pos, n, max(ctx), H, asink, awin, scale, out, ws, ws_bytes)
+    torch.cuda.synchronize()
+    gpu = out.cpu().numpy()
+    ref = np.stack([S.shadow_reference(q[s:s + 1], [ctx[s] - 1], ks[s], vs[s], hd, asink, awin,
+                                       scale, ssink, swin, ctx[s] - 1) for s in range(n)])
+    U.compare_rows(gpu, ref.reshape(gpu.shape), U.TOL_Q4, f"random decode shadow {case}")
+    del bufs
