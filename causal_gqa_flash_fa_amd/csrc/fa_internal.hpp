@@ -69,8 +69,11 @@ constexpr int kPrefillMaxWorkGroups = 256;
 // Decode: single-wave work-groups folding tiles of 64 keys (one per lane).
 constexpr int kDecodeKeyTile = 64;
 // Split plan constants: about kDecodeKps keys per split, at most
-// kDecodeSplitCap splits per slot. Splits are the schedulable work items.
-constexpr int kDecodeKps = 128;
+// kDecodeSplitCap splits per slot. Splits are the schedulable work items, so
+// they set how evenly the stream-K runs cut the keys: one key tile per split
+// timed ~1.3% faster than two on the 64-slot fp32-cache decode (the same on
+// Q4_0), four tiles 2-6% slower.
+constexpr int kDecodeKps = 64;
 constexpr int kDecodeSplitCap = 512;
 // Work-groups of the decode partial pass: 8 waves per CU of a 256-CU MI355X.
 constexpr int kDecodeMaxWaves = 2048;
