@@ -339,14 +339,15 @@ int shadow_groups(const fa_cache *c) {
     return (c->shadow_sink + c->shadow_win + 63) / 64;
 }
 
-DecodeLayout decode_layout_of(int n_kv_head, int head_dim, int sh_groups, int n_slots, int n_head,
-                              int max_ctx) {
+DecodeLayout decode_layout_of(int format, int n_kv_head, int head_dim, int sh_groups, int n_slots,
+                              int n_head, int max_ctx) {
     DecodeLayout d;
     const size_t nsegs = (size_t)n_slots * n_kv_head;
     const int group = n_head / n_kv_head;
     const size_t items = nsegs * (size_t)fa_decode_plan(max_ctx, nullptr, nullptr);
-    d.waves = (int)(items < (size_t)fa::kDecodeMaxWaves ? (items ? items : 1)
-                                                        : (size_t)fa::kDecodeMaxWaves);
+    const size_t max_waves =
+        (size_t)(format == FA_KV_F32 ? fa::kDecodeMaxWavesF32 : fa::kDecodeMaxWaves);
+    d.waves = (int)(items < max_waves ? (items ? items : 1) : max_waves);
     d.max_partials = nsegs + (size_t)d.waves;   // each run boundary adds at most one partial
     d.table_bytes = align256(nsegs * 2 * sizeof(int));
     d.m_off = d.table_bytes;
@@ -363,7 +364,8 @@ DecodeLayout decode_layout_of(int n_kv_head, int head_dim, int sh_groups, int n_
 }
 
 DecodeLayout decode_layout(const fa_cache *c, int n_slots, int n_head, int max_ctx) {
-    return decode_layout_of(c->n_kv_head, c->head_dim, shadow_groups(c), n_slots, n_head, max_ctx);
+    return decode_layout_of(c->format, c->n_kv_head, c->head_dim, shadow_groups(c), n_slots, n_head,
+                            max_ctx);
 }
 }  // namespace
 
@@ -572,7 +574,8 @@ size_t fa_paged_decode_workspace_bytes(int num_reqs, int n_head, int n_kv_head, 
     if (num_reqs < 0 || n_kv_head < 1 || n_head < 1 || n_head % n_kv_head ||
         !group_ok(n_head / n_kv_head) || !dim_ok(head_dim) || max_seq_len_hint < 1)
         return 0;
-    return decode_layout_of(n_kv_head, head_dim, 0, num_reqs, n_head, max_seq_len_hint).total;
+    return decode_layout_of(FA_KV_F32, n_kv_head, head_dim, 0, num_reqs, n_head, max_seq_len_hint)
+        .total;
 }
 
 int fa_paged_decode(const fa_paged_cache *cache, const float *q, int num_reqs, int n_head,
@@ -596,7 +599,8 @@ int fa_paged_decode(const fa_paged_cache *cache, const float *q, int num_reqs, i
     if (((uintptr_t)q | (uintptr_t)out) % 16 != 0) return FA_EINVAL;
     const int group = n_head / cache->n_kv_head;
     const DecodeLayout lay =
-        decode_layout_of(cache->n_kv_head, cache->head_dim, 0, num_reqs, n_head, max_seq_len_hint);
+        decode_layout_of(FA_KV_F32, cache->n_kv_head, cache->head_dim, 0, num_reqs, n_head,
+                         max_seq_len_hint);
     if (ws_bytes < lay.total) return FA_EWORKSPACE;
     if ((rc = fa_init())) return rc;
     uint8_t *wsb = (uint8_t *)ws;

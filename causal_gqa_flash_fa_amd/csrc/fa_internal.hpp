@@ -75,8 +75,13 @@ constexpr int kDecodeKeyTile = 64;
 // Q4_0), four tiles 2-6% slower.
 constexpr int kDecodeKps = 64;
 constexpr int kDecodeSplitCap = 512;
-// Work-groups of the decode partial pass: 8 waves per CU of a 256-CU MI355X.
+// Work-groups of the decode partial pass: 8 waves per CU of a 256-CU MI355X
+// for Q4_0 tiles (bound by issue: two waves per SIMD hide each other's
+// latencies; one wave per SIMD was 46% slower). fp32 tiles are bound by HBM,
+// and one wave per SIMD (4 per CU) streams them ~0.6% faster than two, with
+// half the run boundaries and partials.
 constexpr int kDecodeMaxWaves = 2048;
+constexpr int kDecodeMaxWavesF32 = 1024;
 
 // Requests of one paged prefill launch (their table sits in LDS).
 constexpr int kPagedMaxReqs = 1024;
