@@ -121,7 +121,10 @@ __device__ __forceinline__ int slot_items(int pos, const DecodeArgs &a, int *spl
 }
 
 template <int HD, int G, int FMT, bool PG>
-__global__ __attribute__((amdgpu_flat_work_group_size(64, 64), amdgpu_waves_per_eu(2)))
+// Q4_0 tiles run two waves per SIMD (bound by issue, the waves hide each
+// other's latencies); fp32 tiles one (bound by HBM: the whole register file
+// goes to the load rings below, 16 K loads and 16 V rows in flight).
+__global__ __attribute__((amdgpu_flat_work_group_size(64, 64), amdgpu_waves_per_eu(FMT == 0 ? 1 : 2)))
 void decode_partial_kernel(DecodeArgs a) {
     static_assert(!PG || FMT == 0, "paged caches hold fp32 rows");
     using Sh = DShape<HD, G, FMT>;
@@ -281,10 +284,12 @@ void decode_partial_kernel(DecodeArgs a) {
             //    save registers), and LDS operands are read one step ahead.
             constexpr int NCH = HD / 16;                // 16-dim chunks per row
             constexpr int NKL = 4 * NCH;                // K loads per tile (chunk, key set)
-            // K loads in flight (fewer with 8 heads, whose accumulators take
-            // the registers)
-            constexpr int KD = NKL < 16 ? NKL : (NHG > 1 ? 8 : 16);
-            constexpr int VD = 8;                       // V rows in flight
+            // K loads in flight: 16 (deeper rings timed the same); with one
+            // wave per SIMD there are registers for them beside the
+            // accumulators of 8 heads (two waves per SIMD had left room for 8,
+            // and streamed ~2% slower)
+            constexpr int KD = NKL < 16 ? NKL : 16;
+            constexpr int VD = 16;                      // V rows in flight
             constexpr int VPR = HD / 64;                // V floats per lane per row (= OD)
             const int qu = (lane >> 2) & 3;             // contraction quarter of this lane
             const int kl = 4 * (lane >> 4) + (lane & 3);   // key of this lane in a 16-key set
