@@ -37,12 +37,15 @@
 // next tile's rows fly during this tile's PV); the raw V tile goes into a
 // per-wave LDS buffer by LDS DMA, in flight during QK and softmax. A code
 // nibble c becomes (c - 8) * d with one v_fma_mix_f32: the nibble is placed
-// in a binary16 whose value is 1024 + c, and (1024 + c) * d - 1032 * d is
-// exact. PV takes two keys per instruction (lanes 0-31 even keys, 32-63 odd
-// keys), each lane owning dims that share one block's code bytes, with its
-// LDS operands read one step ahead; the two halves are summed at the end.
-// fp32 tiles: each lane reads its key's K row and, in PV, 4 dims of each V
-// row straight from memory.
+// in a binary16 whose value is 1024 + c (low nibble) or 1024 + 16 c (high
+// nibble), and (1024 + c) * d - 1032 * d, (1024 + 16 c) * (d / 16) - 72 * d
+// are exact. PV takes two keys per instruction (lanes 0-31 even keys, 32-63
+// odd keys), each lane owning dims that share one block's code bytes, with
+// its LDS operands read one step ahead; the two halves are summed at the end.
+// fp32 tiles (bound by HBM, one wave per SIMD): QK splits the contraction
+// four ways so that four lanes read one key's 64 contiguous bytes at a time,
+// PV reads each V row as one vector load per lane, and both stream from
+// memory through 16-deep register rings.
 //
 // The running max is recomputed across the wave only when some score exceeds
 // it by more than 8 (base-2 units); any reference max gives the same
