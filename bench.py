@@ -375,6 +375,9 @@ def decode_leg(fa, torch, w, steps: int, warmup: int) -> dict:
         "kv_bytes": kv_bytes, "bytes": kv_bytes + qo_bytes, "flops": flops,
         "decode_ms": ms, "decode_ms_min": float(np.min(kms)), **spread(kms, "decode_ms"),
         "gbs": gbs, "frac_hbm_peak": gbs / PEAK_HBM_GBS, "tflops": flops / ms / 1e9,
+        # the same call against the fp32 MFMA peak: a Q4_0 cache puts the decode
+        # above the fp32 ridge (28.4 FLOP/B at hd 256), so this is its bound
+        "frac_fp32_mfma_peak": flops / ms / 1e9 / PEAK_FP32_MFMA_TFLOPS,
         "fp32_compute_ceiling_gbs": compute_ceiling_gbs,
         "frac_of_min_ceiling": gbs / min(PEAK_HBM_GBS, compute_ceiling_gbs),
         "traffic_bytes": (round(rec["traffic_bytes"]) if (rec := measured_traffic("decode", w.name))
