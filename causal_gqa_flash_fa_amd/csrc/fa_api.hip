@@ -201,25 +201,42 @@ PrefillLayout prefill_layout(int n, int n_head, int n_kv_head, int head_dim) {
     return p;
 }
 
-// Visited key tiles of a prefill call: the stream-K grid never needs more
-// work-groups than that.
-long long prefill_tiles(int n, int pos0, int bq, int sink, int win) {
-    const int bk = fa::kPrefillKeyTile;
-    long long total = 0;
-    for (int q0 = pos0; q0 < pos0 + n; q0 += bq) {
-        const int q1 = q0 + bq - 1 < pos0 + n - 1 ? q0 + bq - 1 : pos0 + n - 1;
-        const int walked = q1 / bk + 1;
-        int count = walked;
-        if (win > 0) {
-            const int win_lo = q0 - win + 1;
-            const int wt = win_lo > 0 ? win_lo / bk : 0;
-            int nsink = ((sink > 0 ? sink : 0) + bk - 1) / bk;
-            if (nsink > walked) nsink = walked;
-            if (wt > nsink) count = nsink + (walked - wt);
-        }
-        total += count;
+// Visited key tiles of a prefill call per kv head (the stream-K grid never
+// needs more work-groups than that) and the schedule units the kernel counts
+// for them, both from the kernel's own tile walk.
+struct PrefillWork {
+    long long tiles, units;
+};
+
+PrefillWork prefill_work(int n, int pos0, int bq, int sink, int win) {
+    PrefillWork w{0, 0};
+    const long long end = (long long)pos0 + n;
+    for (long long b0 = pos0; b0 < end; b0 += bq) {
+        const int q0 = (int)b0;
+        const int q1 = (int)(b0 + bq - 1 < end - 1 ? b0 + bq - 1 : end - 1);
+        const int c = fa::seg_tiles(q0, q1, sink, win, fa::kPrefillKeyTile).count;
+        w.tiles += c;
+        w.units += c > 0 ? (long long)c * fa::kTileUnits + fa::kSegUnits : 0;
     }
-    return total;
+    return w;
+}
+
+// The same for the fp16-shadow launch: per query block, its shadow keys in
+// 32-key tiles (the sink positions, then every position a row's ring window
+// reaches).
+PrefillWork shadow_work(int n, int pos0, int bq, int sh_sink, int sh_win) {
+    PrefillWork w{0, 0};
+    const long long end = (long long)pos0 + n;
+    for (long long b0 = pos0; b0 < end; b0 += bq) {
+        const long long q0 = b0, q1 = b0 + bq - 1 < end - 1 ? b0 + bq - 1 : end - 1;
+        const long long n_sk = sh_sink < q1 + 1 ? sh_sink : q1 + 1;
+        const long long wlo = sh_sink > q0 - sh_win + 1 ? sh_sink : q0 - sh_win + 1;
+        const long long nk = n_sk + (sh_win > 0 && q1 >= wlo ? q1 - wlo + 1 : 0);
+        const long long c = (nk + fa::kPrefillKeyTile - 1) / fa::kPrefillKeyTile;
+        w.tiles += c;
+        w.units += c > 0 ? c * fa::kTileUnits + fa::kSegUnits : 0;
+    }
+    return w;
 }
 }  // namespace
 
@@ -241,17 +258,25 @@ int fa_prefill(const fa_cache *cache, int slot, const float *q, int pos0, int n,
     if ((long long)pos0 + n > cache->max_seq) return FA_ERANGE;
     if (n == 0) return FA_OK;
     if (!q || !out || !ws) return FA_ENULL;
+    const int group = n_head / cache->n_kv_head;
+    const int bq = fa::prefill_q_positions(group);
+    const int sink = attn_sink < 0 ? 0 : attn_sink;
+    const bool shadowed = cache->shadow_sink > 0 || cache->shadow_win > 0;
+    // the stream-K schedule counts its units in 32 bits: refuse what does not fit
+    const PrefillWork wk = prefill_work(n, pos0, bq, sink, attn_win);
+    if (wk.units > fa::kMaxScheduleUnits / cache->n_kv_head) return FA_EUNSUPPORTED;
+    const PrefillWork swk = shadowed ? shadow_work(n, pos0, bq, cache->shadow_sink,
+                                                   cache->shadow_win)
+                                     : PrefillWork{0, 0};
+    if (swk.units > fa::kMaxScheduleUnits / cache->n_kv_head) return FA_EUNSUPPORTED;
     const PrefillLayout lay = prefill_layout(n, n_head, cache->n_kv_head, cache->head_dim);
     if (ws_bytes < lay.total) return FA_EWORKSPACE;
     if ((rc = fa_init())) return rc;
     int dev = 0;
     if (hip_rc(hipGetDevice(&dev))) return FA_EHIP;
-    const int group = n_head / cache->n_kv_head;
-    const int bq = fa::prefill_q_positions(group);
-    const int sink = attn_sink < 0 ? 0 : attn_sink;
     long long n_wg = g_device_cus[dev] < fa::kPrefillMaxWorkGroups ? g_device_cus[dev]
                                                                    : fa::kPrefillMaxWorkGroups;
-    const long long tiles = (long long)cache->n_kv_head * prefill_tiles(n, pos0, bq, sink, attn_win);
+    const long long tiles = (long long)cache->n_kv_head * wk.tiles;
     if (tiles < n_wg) n_wg = tiles;
     if (n_wg < 1) n_wg = 1;
     uint8_t *wsb = (uint8_t *)ws;
@@ -279,22 +304,14 @@ int fa_prefill(const fa_cache *cache, int slot, const float *q, int pos0, int n,
     a.sh = shadow_args(cache, slot);
     a.sh_m = (const float *)(wsb + lay.sh_m_off);
     a.sh_l = (const float *)(wsb + lay.sh_l_off);
-    if (a.sh.sink > 0 || a.sh.win > 0) {
+    if (shadowed) {
         // each row's shadow-key partial (m, l to the workspace, acc to out),
         // from the same kernel in its shadow mode: per query block, the
         // union of its rows' shadow keys in 32-key tiles
         fa::PrefillArgs sa = a;
         sa.stats = nullptr;
         sa.lse = nullptr;
-        long long sh_tiles = 0;
-        for (int q0 = pos0; q0 < pos0 + n; q0 += bq) {
-            const int q1 = q0 + bq - 1 < pos0 + n - 1 ? q0 + bq - 1 : pos0 + n - 1;
-            const int n_sk = a.sh.sink < q1 + 1 ? a.sh.sink : q1 + 1;
-            const int wlo = a.sh.sink > q0 - a.sh.win + 1 ? a.sh.sink : q0 - a.sh.win + 1;
-            const int nk = n_sk + (a.sh.win > 0 && q1 >= wlo ? q1 - wlo + 1 : 0);
-            sh_tiles += (nk + fa::kPrefillKeyTile - 1) / fa::kPrefillKeyTile;
-        }
-        sh_tiles *= cache->n_kv_head;
+        const long long sh_tiles = swk.tiles * cache->n_kv_head;
         long long sh_wg = g_device_cus[dev] < fa::kPrefillMaxWorkGroups ? g_device_cus[dev]
                                                                         : fa::kPrefillMaxWorkGroups;
         if (sh_tiles < sh_wg) sh_wg = sh_tiles;
@@ -363,6 +380,12 @@ DecodeLayout decode_layout_of(int format, int n_kv_head, int head_dim, int sh_gr
     return d;
 }
 
+// The decode kernels count work items (at most kDecodeSplitCap per slot and
+// kv head) in 32 bits.
+bool decode_items_fit(int n_slots, int n_kv_head) {
+    return (long long)n_slots * n_kv_head <= fa::kMaxScheduleUnits / fa::kDecodeSplitCap;
+}
+
 DecodeLayout decode_layout(const fa_cache *c, int n_slots, int n_head, int max_ctx) {
     return decode_layout_of(c->format, c->n_kv_head, c->head_dim, shadow_groups(c), n_slots, n_head,
                             max_ctx);
@@ -388,6 +411,7 @@ int fa_decode(const fa_cache *cache, const float *q, const int *d_pos, int n_slo
     if (max_ctx_hint < 1 || max_ctx_hint > cache->max_seq) return FA_EINVAL;
     if (n_slots == 0) return FA_OK;
     if (!q || !d_pos || !out || !ws) return FA_ENULL;
+    if (!decode_items_fit(n_slots, cache->n_kv_head)) return FA_EUNSUPPORTED;
     const DecodeLayout lay = decode_layout(cache, n_slots, n_head, max_ctx_hint);
     if (ws_bytes < lay.total) return FA_EWORKSPACE;
     if ((rc = fa_init())) return rc;
@@ -526,6 +550,18 @@ int fa_paged_attention(const fa_paged_cache *cache, const float *q, int num_toke
     if (num_tokens == 0 || num_reqs == 0) return FA_OK;
     if (!q || !out || !query_start_loc || !seq_lens || !block_table || !ws) return FA_ENULL;
     if (((uintptr_t)q | (uintptr_t)out) % 16 != 0) return FA_EINVAL;
+    {
+        // The batch is described on the device, so bound the schedule the
+        // kernel will count in 32 bits: at most num_tokens / BQ + num_reqs
+        // query blocks per kv head, each walking at most cap / 32 + 1 tiles.
+        const int bq = fa::prefill_q_positions(n_head / cache->n_kv_head);
+        const long long segs =
+            (long long)cache->n_kv_head * ((num_tokens + (long long)bq - 1) / bq + num_reqs);
+        const long long seg_units =
+            ((long long)max_blocks_per_seq * cache->block_size / fa::kPrefillKeyTile + 1) *
+                fa::kTileUnits + fa::kSegUnits;
+        if (segs > fa::kMaxScheduleUnits / seg_units) return FA_EUNSUPPORTED;
+    }
     const PagedLayout lay = paged_layout(cache->head_dim);
     if (ws_bytes < lay.total) return FA_EWORKSPACE;
     if ((rc = fa_init())) return rc;
@@ -597,6 +633,7 @@ int fa_paged_decode(const fa_paged_cache *cache, const float *q, int num_reqs, i
     if (num_reqs == 0) return FA_OK;
     if (!q || !out || !seq_lens || !block_table || !ws) return FA_ENULL;
     if (((uintptr_t)q | (uintptr_t)out) % 16 != 0) return FA_EINVAL;
+    if (!decode_items_fit(num_reqs, cache->n_kv_head)) return FA_EUNSUPPORTED;
     const int group = n_head / cache->n_kv_head;
     const DecodeLayout lay =
         decode_layout_of(FA_KV_F32, cache->n_kv_head, cache->head_dim, 0, num_reqs, n_head,

@@ -101,8 +101,16 @@ __global__ __launch_bounds__(kAppendThreads) void append_f32_kernel(AppendArgs a
     *(f32x4 *)(dst + row * a.head_dim + 4 * c4) = x;
 }
 
-__device__ __forceinline__ int clamp_code(int c) {
-    return c < 0 ? 0 : (c > 15 ? 15 : c);
+// Code of one element: clamp(rint(x * id) + 8, 0, 15) ([FA] fc_kvq4_quant_block),
+// with the clamp taken in float before the integer conversion so that every
+// product has a defined code: a NaN product (a NaN element, or 0 * inf when
+// 1/d overflows for a block whose amax is below 2^-125) gives code 8, and
+// infinities clamp to codes 0 and 15. On finite in-range data this is the
+// integer clamp exactly.
+__device__ __forceinline__ int q4_code(float x, float id) {
+    const float r = rintf(x * id);
+    const float t = r != r ? 0.0f : fminf(fmaxf(r, -8.0f), 7.0f);
+    return (int)t + 8;
 }
 
 __global__ __launch_bounds__(kAppendThreads) void append_q4_kernel(AppendArgs a) {
@@ -148,10 +156,10 @@ __global__ __launch_bounds__(kAppendThreads) void append_q4_kernel(AppendArgs a)
     out[0] = d == 0.0f ? (uint16_t)0x8000u : __builtin_bit_cast(uint16_t, (_Float16)d);
 #pragma unroll
     for (int j = 0; j < kQ4Block / 2; j += 2) {
-        const int c0 = clamp_code((int)rintf(x[j] * id) + 8);
-        const int c1 = clamp_code((int)rintf(x[j + 1] * id) + 8);
-        const int c16 = clamp_code((int)rintf(x[j + 16] * id) + 8);
-        const int c17 = clamp_code((int)rintf(x[j + 17] * id) + 8);
+        const int c0 = q4_code(x[j], id);
+        const int c1 = q4_code(x[j + 1], id);
+        const int c16 = q4_code(x[j + 16], id);
+        const int c17 = q4_code(x[j + 17], id);
         const uint32_t b0 = (uint32_t)(c0 | (c16 << 4));
         const uint32_t b1 = (uint32_t)(c1 | (c17 << 4));
         out[1 + j / 2] = (uint16_t)(b0 | (b1 << 8));   // bytes 2+j, 3+j (little-endian)

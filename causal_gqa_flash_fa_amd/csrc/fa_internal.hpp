@@ -162,6 +162,47 @@ struct DecodeArgs {
     float *lse;                   // NULL or [n_head][n_slots]: ln sum_j exp(scale q.k_j)
 };
 
+// Visited key tiles of the query block [q0, q1] ([FA] fc_attn_tile_in_window
+// over the union of the block's key sets): the causal walk has q1/bk + 1
+// tiles; with a window, tiles below the sink or reaching the union window
+// [q0 - win + 1, q1] are visited and the rest are skipped. The host sizes
+// the stream-K grid and checks the schedule's range with this function and
+// the kernel walks its tiles with it, so the two cannot disagree.
+struct SegTiles {
+    int walked, nsink, wt, count;       // visited tile i -> i < nsink ? i : wt + i - nsink
+    __host__ __device__ int tile(int i) const { return i < nsink ? i : wt + i - nsink; }
+};
+
+__host__ __device__ inline SegTiles seg_tiles(int q0, int q1, int sink, int win, int bk) {
+    SegTiles t;
+    t.walked = q1 / bk + 1;
+    t.nsink = t.walked;
+    t.wt = t.walked;
+    t.count = t.walked;
+    if (win > 0) {
+        const int win_lo = q0 - win + 1;
+        const int wt = win_lo > 0 ? win_lo / bk : 0;
+        int nsink = ((sink > 0 ? sink : 0) + bk - 1) / bk;
+        if (nsink > t.walked) nsink = t.walked;
+        if (wt > nsink) {
+            t.nsink = nsink;
+            t.wt = wt;
+            t.count = nsink + (t.walked - wt);
+        }
+    }
+    return t;
+}
+
+// Stream-K prefill schedule units: a visited tile is kTileUnits units and
+// starting a segment costs kSegUnits more (measured: a segment switch,
+// output stores plus the next Q load and first-tile latency, costs about one
+// ~9 us tile; 4, 5 and 6 units time the same within noise). The kernel
+// counts units in 32-bit integers, so the host refuses a launch whose total
+// exceeds kMaxScheduleUnits.
+constexpr int kTileUnits = 4;
+constexpr int kSegUnits = 5;
+constexpr long long kMaxScheduleUnits = 0x7fffffffLL;
+
 inline int prefill_q_positions(int group) {
     return kPrefillWaves * kPrefillRowsPerWave / group;
 }

@@ -108,43 +108,7 @@ __device__ __forceinline__ void scale_acc(f32x16 &acc, float c) {
 // Wait for all of this wave's vector-memory operations (incl. LDS DMA).
 __device__ __forceinline__ void wait_vmem() { wait_vmem_le<0>(); }
 
-// Visited key tiles of the query block [q0, q1] ([FA] fc_attn_tile_in_window
-// over the union of the block's key sets): the causal walk has q1/BK + 1
-// tiles; with a window, tiles below the sink or reaching the union window
-// [q0 - win + 1, q1] are visited and the rest are skipped.
-struct SegTiles {
-    int walked, nsink, wt, count;       // visited tile i -> i < nsink ? i : wt + i - nsink
-    __device__ int tile(int i) const { return i < nsink ? i : wt + i - nsink; }
-};
-
-__device__ __forceinline__ SegTiles seg_tiles(int q0, int q1, int sink, int win, int bk) {
-    SegTiles t;
-    t.walked = q1 / bk + 1;
-    t.nsink = t.walked;
-    t.wt = t.walked;
-    t.count = t.walked;
-    if (win > 0) {
-        const int win_lo = q0 - win + 1;
-        const int wt = win_lo > 0 ? win_lo / bk : 0;
-        const int nsink = min((max(sink, 0) + bk - 1) / bk, t.walked);
-        if (wt > nsink) {
-            t.nsink = nsink;
-            t.wt = wt;
-            t.count = nsink + (t.walked - wt);
-        }
-    }
-    return t;
-}
-
 constexpr int kXcds = 8;   // XCDs of an MI355X; block b runs on XCD b % 8
-// Schedule units: a tile is kTileUnits units and starting a segment costs
-// kSegUnits more (measured: a segment switch, output stores plus the next Q
-// load and first-tile latency, costs about one ~9 us tile; 4, 5 and 6 units
-// time the same within noise). A tile belongs to the run that holds its
-// first unit.
-constexpr int kTileUnits = 4;
-constexpr int kSegUnits = 5;
-
 // Segment s of the schedule is query block seg_qblock(s) of kv head
 // s / n_qblocks. Within a head the causal segments alternate long and short
 // (last block, first block, second to last, second, ...), so that a

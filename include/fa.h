@@ -113,7 +113,12 @@ int fa_init(void);
  * fc_attn_kv_append_q4 + fc_kvq4_quant_block (Q4_0: per 32-element block,
  * amax fold, d = amax/-8, id = 1/d or 0, code = clamp(rint(x*id)+8, 0, 15),
  * binary16 scale), all in IEEE fp32 so the bytes are exactly determined.
- *   k_new, v_new: device [n][n_kv_head][head_dim] fp32 (finite values).
+ * The clamp is taken on the rounded product as a float, so non-finite
+ * products have defined codes: a NaN product (a NaN element, or 0 * inf when
+ * a block's amax is below 2^-125 and 1/d overflows) gives code 8, +-inf give
+ * codes 15 / 0; the amax fold skips quiet NaN elements (fmaxf). A scale
+ * beyond binary16 range is stored as -inf.
+ *   k_new, v_new: device [n][n_kv_head][head_dim] fp32.
  *   slot in [0, n_slots); pos0 >= 0; n >= 0; pos0 + n <= max_seq (the
  *   cache never wraps: FA_ERANGE otherwise). n == 0 enqueues nothing. */
 int fa_kv_append(const fa_cache *cache, int slot, int pos0, int n,
@@ -163,7 +168,12 @@ int fa_kv_append_slots(const fa_cache *cache, const int *d_pos, int n_slots,
  * row's pass over the Q4_0 body starts from that partial.
  * Rows of q and out must not overlap. Two launches on `stream` (four with a
  * shadow); nothing in them depends on host reads of device data, so a
- * captured HIP graph replays the call. */
+ * captured HIP graph replays the call.
+ * The work-groups split the visited key tiles by a schedule of 4 units per
+ * tile and 5 per query block of fa_prefill_tile_shape() positions, summed
+ * over kv heads and counted in 32 bits: a call whose total exceeds 2^31 - 1
+ * (a full-causal prefill of about 2^19 positions at 8 kv heads) returns
+ * FA_EUNSUPPORTED, checked before the workspace size. */
 int fa_prefill(const fa_cache *cache, int slot, const float *q, int pos0, int n,
                int n_head, int attn_sink, int attn_win, float scale, float *out,
                void *ws, size_t ws_bytes, unsigned long long *tile_stats, void *stream);
@@ -226,7 +236,9 @@ size_t fa_decode_workspace_bytes(const fa_cache *cache, int n_slots, int n_head,
  *           fa_decode_workspace_bytes(cache, n_slots, n_head, max_ctx_hint).
  *   tile_stats: as in fa_prefill, key tiles of the plan's tile size walked
  *           split by split.
- * n_slots == 0 enqueues nothing. Other rules as fa_prefill. */
+ * n_slots == 0 enqueues nothing. Other rules as fa_prefill. The work items
+ * (at most the plan's cap per slot and kv head) are counted in 32 bits:
+ * n_slots * n_kv_head beyond (2^31 - 1) / cap returns FA_EUNSUPPORTED. */
 int fa_decode(const fa_cache *cache, const float *q, const int *d_pos, int n_slots,
               int max_ctx_hint, int n_head, int attn_sink, int attn_win, float scale,
               float *out, void *ws, size_t ws_bytes, unsigned long long *tile_stats,
@@ -299,7 +311,12 @@ size_t fa_paged_workspace_bytes(int head_dim);
  * never read there); out-of-rule values are clamped on the device so that no
  * access leaves the buffers, and the rows they touch are unspecified.
  * Tokens outside every request's range are not written. Head dims, group
- * sizes and the scale rule as fa_prefill. Two launches on `stream`. */
+ * sizes and the scale rule as fa_prefill. Two launches on `stream`.
+ * The kernel counts its schedule in 32 bits (as fa_prefill); since the batch
+ * is not read on the host, the host bounds it by n_kv_head * (num_tokens / BQ
+ * + num_reqs) query blocks of at most max_blocks_per_seq * block_size / 32 + 1
+ * tiles (BQ from fa_prefill_tile_shape) and returns FA_EUNSUPPORTED when that
+ * bound exceeds 2^31 - 1 schedule units (4 per tile, 5 per block). */
 int fa_paged_attention(const fa_paged_cache *cache, const float *q, int num_tokens,
                        int n_head, const int *query_start_loc, const int *seq_lens,
                        int num_reqs, const int *block_table, int max_blocks_per_seq,
@@ -337,7 +354,8 @@ size_t fa_paged_decode_workspace_bytes(int num_reqs, int n_head, int n_kv_head, 
  *       Longer requests are still computed exactly.
  *   ws, ws_bytes: at least fa_paged_decode_workspace_bytes(...).
  * No device metadata is read on the host. num_reqs == 0 enqueues nothing.
- * Two launches on `stream`. */
+ * Two launches on `stream`. The 32-bit item limit of fa_decode applies to
+ * num_reqs * n_kv_head. */
 int fa_paged_decode(const fa_paged_cache *cache, const float *q, int num_reqs, int n_head,
                     const int *seq_lens, const int *block_table, int max_blocks_per_seq,
                     int max_seq_len_hint, int window_left, int window_right, float scale,

@@ -73,16 +73,30 @@ float oracle_f16_to_f32(uint16_t h)
 
 enum { Q4_BLK = 32, Q4_BLK_BYTES = 18 };
 
-static int clamp_code(int c)
+/* Code of one element: rint(x * id) clamped to [-8, 7], plus 8. The clamp
+ * is done on the float before converting, so that products outside the int
+ * range have a defined code (C leaves the conversion undefined there): a NaN
+ * product (NaN element, or 0 * inf when 1/d overflows) is taken as 0, i.e.
+ * code 8, and +-inf clamp to codes 15 / 0. For finite in-range products this
+ * is clamp(int(rint(x * id)) + 8, 0, 15). */
+static int q4_code(float x, float id)
 {
-    return c < 0 ? 0 : (c > 15 ? 15 : c);
+    float r = rintf(x * id);
+    if (isnan(r))
+        return 8;
+    if (r < -8.0f)
+        r = -8.0f;
+    if (r > 7.0f)
+        r = 7.0f;
+    return (int)r + 8;
 }
 
 /* One 32-element block. Steps, all in fp32:
  *  1. amax: fmaxf fold of |x_j| starting from 0
  *  2. d = amax / -8  (the stored scale is negative)
  *  3. id = 1/d, or 0 when d is zero
- *  4. code_j = clamp(int(rint(x_j * id)) + 8, 0, 15)  (convert, then +8, then clamp)
+ *  4. code_j = clamp(int(rint(x_j * id)) + 8, 0, 15), the clamp taken on the
+ *     float (q4_code) so non-finite products are defined
  *  5. bytes 0-1: binary16(d) little-endian; byte 2+j: code_j | code_{j+16} << 4 */
 static void q4_block(const float *xb, uint8_t *blk)
 {
@@ -96,8 +110,8 @@ static void q4_block(const float *xb, uint8_t *blk)
     blk[0] = (uint8_t)(dh & 0xffu);
     blk[1] = (uint8_t)(dh >> 8);
     for (int j = 0; j < Q4_BLK / 2; j++) {
-        const int lo = clamp_code((int)rintf(xb[j] * id) + 8);
-        const int hi = clamp_code((int)rintf(xb[j + Q4_BLK / 2] * id) + 8);
+        const int lo = q4_code(xb[j], id);
+        const int hi = q4_code(xb[j + Q4_BLK / 2], id);
         blk[2 + j] = (uint8_t)(lo | (hi << 4));
     }
 }

@@ -276,3 +276,53 @@ def test_valid_call_without_a_gpu_fails_loudly():
     assert rc in (fa.FA_EHIP, fa.FA_EDEVICE)
     with pytest.raises(fa.FaError):
         fa.fa_init()
+
+
+def causal_units(n, n_kv, bq, bk):
+    """Stream-K units of a full-causal prefill from position 0: 4 per visited
+    key tile (block [q0, q1] walks q1 // bk + 1 tiles) and 5 per query block,
+    for every kv head (closed form of the causal tile walk)."""
+    import numpy as np
+    q1 = np.minimum(np.arange(0, n, bq, dtype=np.int64) + bq - 1, n - 1)
+    return n_kv * int((4 * (q1 // bk + 1) + 5).sum())
+
+
+def test_prefill_schedule_beyond_32_bits_is_refused():
+    # The prefill kernel counts its stream-K schedule units in 32-bit
+    # integers; a call whose total does not fit is refused before launch.
+    n_kv, hd = 8, 64
+    bq, bk = fa.fa_prefill_tile_shape(n_kv, n_kv, hd)
+    limit = (1 << 31) - 1
+    lo, hi = 1 << 18, 1 << 20
+    assert causal_units(lo, n_kv, bq, bk) <= limit < causal_units(hi, n_kv, bq, bk)
+    while hi - lo > 1:
+        mid = (lo + hi) // 2
+        lo, hi = (mid, hi) if causal_units(mid, n_kv, bq, bk) <= limit else (lo, mid)
+    # the closed form against the oracle's tile walk at the boundary
+    for n in (lo, hi):
+        vis, _ = oracle.prefill_tile_counts(n, 0, 1, 0, 0, bq, bk)
+        assert causal_units(n, n_kv, bq, bk) == n_kv * (4 * vis + 5 * (-(-n // bq)))
+    c = cache(n_slots=1, n_kv=n_kv, hd=hd, max_seq=hi)
+    # accepted (then refused only for the missing workspace) up to the limit
+    assert rc_prefill(c, n=lo, n_head=n_kv, ws_bytes=0) == fa.FA_EWORKSPACE
+    assert rc_prefill(c, n=hi, n_head=n_kv, ws_bytes=0) == fa.FA_EUNSUPPORTED
+    # a window keeps the schedule small at the same length
+    assert rc_prefill(c, n=hi, n_head=n_kv, win=1024, ws_bytes=0) == fa.FA_EWORKSPACE
+
+
+def test_paged_schedule_bound_is_refused():
+    # the batch lives on the device, so the host bounds the schedule from
+    # num_tokens, num_reqs and the block-table width
+    c = paged(nb=1 << 16, bs=16, n_kv=8, hd=64)
+    assert rc_paged(c, T=1 << 20, H=8, R=1, mb=1 << 16, ws_bytes=0) == fa.FA_EUNSUPPORTED
+    assert rc_paged(c, T=8192, H=8, R=50, mb=1 << 13, ws_bytes=0) == fa.FA_EWORKSPACE
+
+
+def test_decode_item_count_beyond_32_bits_is_refused():
+    # decode work items (at most the plan's split cap per slot and kv head)
+    # are counted in 32-bit integers
+    _, cap, _ = fa.fa_decode_plan_params()
+    big = ((1 << 31) - 1) // cap
+    c = cache(n_slots=big + 1, n_kv=1)
+    assert rc_decode(c, n_slots=big + 1, ws_bytes=0) == fa.FA_EUNSUPPORTED
+    assert rc_decode(c, n_slots=big, ws_bytes=0) == fa.FA_EWORKSPACE
