@@ -3,18 +3,21 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 
-Prints ONE JSON line. The headline step is the prefill-f32kv-2k workload
-(2048 query rows, 16 q heads / 2 kv heads, head_dim 256, fp32 KV, full
-causal): fa_kv_append of the 2048 K/V rows followed by fa_prefill, inputs
-resident in HBM. `value` is key-set-counted prefill FLOPs (4*head_dim per
-attended (query, head, key)) per second of step time. The same line carries
-the other workloads as `legs` (Q4_0 8k prefill, 32k sliding-window prefill,
-64-slot Q4_0 decode, both Q4_0 ones again with the fp16 sink/window shadow,
-the 64-slot decode over an fp32 cache, a varlen batch over a paged fp32 cache,
-the 64-slot decode as 64 one-token requests over a paged fp32 cache, and the LSE merge of two attention
-states), a `roofline` object for the dominant kernel (timed with HIP events
-on the launch stream) and the CPU oracle timed on the host cores as
-`cpu_baseline`.
+Prints ONE JSON line. The headline step is fa_prefill on the prefill-q4kv-8k
+workload (8192 query rows, 16 q heads / 2 kv heads, head_dim 256, Q4_0 KV
+written by fa_kv_append, full causal), inputs and cache resident in HBM:
+`value` is key-set-counted prefill FLOPs (4*head_dim per attended (query,
+head, key)) per second of step time. The append that fills the cache is timed
+on its own (`config.append_ms`) and kept out of the metric. The line also
+carries a `roofline` object for the prefill kernel and a `roofline_decode`
+object for the 64-slot Q4_0 decode (the metric's second half: KV-read GB/s
+against HBM and against the fp32 compute ceiling), both timed with HIP events
+on the launch stream; the other workloads as `legs` (the tiny and 2k
+prefills, the 32k sliding-window prefill, both Q4_0 workloads with the fp16
+sink/window shadow, the 64-slot decode over an fp32 cache, a varlen batch
+over a paged fp32 cache, the 64-slot decode as 64 one-token requests over a
+paged fp32 cache, and the LSE merge of two attention states); and the CPU
+oracle timed on the host cores as `cpu_baseline`.
 """
 from __future__ import annotations
 
@@ -104,10 +107,12 @@ def spread(kms, key: str) -> dict:
 
 
 def prefill_leg(fa, torch, w, steps: int, warmup: int, graph: bool = False) -> dict:
-    """Append + prefill of one workload. Kernel time: HIP events around each
-    eager fa_prefill. Step time: the same two calls launched eagerly, or, with
-    `graph`, captured once in a HIP graph and replayed (same kernels, same
-    work, no per-launch host overhead)."""
+    """fa_prefill of one workload over a cache filled by fa_kv_append. The
+    append is timed on its own (HIP events, `append_ms`) and is not part of
+    the step. Kernel time: HIP events around each eager fa_prefill. Step
+    time: fa_prefill launched eagerly, or, with `graph`, captured once in a
+    HIP graph and replayed (same kernels, same work, no per-launch host
+    overhead)."""
     dev = torch.device("cuda:0")
     q = torch.from_numpy(workloads.prefill_q(w)).to(dev)
     k_np, v_np = workloads.prefill_kv(w)
@@ -120,10 +125,21 @@ def prefill_leg(fa, torch, w, steps: int, warmup: int, graph: bool = False) -> d
     rows = w.pos0 + w.n
     ws_bytes = fa.fa_prefill_workspace_bytes(w.n, w.n_head, w.n_kv_head, w.head_dim)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+
+    # the append, timed apart from the step
+    aev = _events(torch, max(3, steps // 4))
+    for i in range(-1, len(aev)):
+        if i >= 0:
+            aev[i][0].record()
+        fa.fa_kv_append(cache, 0, 0, rows, kd, vd)
+        if i >= 0:
+            aev[i][1].record()
+    torch.cuda.synchronize()
+    append_ms = float(np.mean([a.elapsed_time(b) for a, b in aev]))
+
     ev = _events(torch, steps)
 
     def step(i=None):
-        fa.fa_kv_append(cache, 0, 0, rows, kd, vd)
         if i is not None:
             ev[i][0].record()
         fa.fa_prefill(cache, 0, q, w.pos0, w.n, w.n_head, w.attn_sink, w.attn_win, w.scale, out,
@@ -162,6 +178,7 @@ def prefill_leg(fa, torch, w, steps: int, warmup: int, graph: bool = False) -> d
         "n": w.n, "n_head": w.n_head, "n_kv_head": w.n_kv_head, "head_dim": w.head_dim,
         "attn_sink": w.attn_sink, "attn_win": w.attn_win,
         "shadow_sink": w.shadow_sink, "shadow_win": w.shadow_win,
+        "step": "fa_prefill", "append_ms": append_ms,
         "launch": "hip_graph" if graph else "eager", "ms_per_step_eager": eager_ms,
         "flops": flops, "ms_per_step": step_ms, "tflops_step": flops / step_ms / 1e9,
         "prefill_kernel_ms": kern_ms, "prefill_kernel_ms_min": float(np.min(kms)),
@@ -387,7 +404,9 @@ def decode_leg(fa, torch, w, steps: int, warmup: int) -> dict:
 
 def cpu_baseline(w) -> dict:
     """The oracle (plain C, double precision, single-threaded per call) over
-    every row of the workload, rows spread over the host's cores."""
+    every row of the workload, rows spread over the host threads: all of the
+    host's cores up to 16, the CPU share of one GPU on the benchmark machines
+    (their os.cpu_count() reports the whole node, which other GPUs' jobs use)."""
     import oracle
     q = workloads.prefill_q(w)
     k, v = workloads.prefill_kv(w)
@@ -396,24 +415,26 @@ def cpu_baseline(w) -> dict:
     if w.kv_format:
         kt = oracle.q4_dequantize(oracle.q4_quantize(kt), w.head_dim)
         vt = oracle.q4_dequantize(oracle.q4_quantize(vt), w.head_dim)
-    threads = min(16, os.cpu_count() or 1)
+    host_cpus = os.cpu_count() or 1
+    threads = min(16, host_cpus)
     t0 = time.perf_counter()
     oracle.prefill(q, kt, vt, w.pos0, w.attn_sink, w.attn_win, w.scale, threads=threads)
     dt = time.perf_counter() - t0
     value = prefill_flops(w) / dt / 1e12
-    # one thread on a fixed subset: every 16th (position, head) row
-    sel = np.arange(0, w.n * w.n_head, 16, dtype=np.int64)
+    # one thread on a fixed subset: every 64th (position, head) row
+    sel = np.arange(0, w.n * w.n_head, 64, dtype=np.int64)
     pos = w.pos0 + sel // w.n_head
     sel_flops = 4.0 * w.head_dim * sum(keyset_pairs(1, int(p), w.attn_sink, w.attn_win) for p in pos)
     t0 = time.perf_counter()
     oracle.prefill(q, kt, vt, w.pos0, w.attn_sink, w.attn_win, w.scale, sel=sel, threads=1)
     dt1 = time.perf_counter() - t0
-    return {"value": value, "unit": "TFLOP/s", "cores": threads,
+    return {"value": value, "unit": "TFLOP/s", "cores": threads, "host_cpu_count": host_cpus,
             "kind": "oracle", "seconds": dt,
-            "sample": f"all {w.n * w.n_head} rows of {w.name} (fp64 global-max softmax)",
+            "sample": f"all {w.n * w.n_head} rows of {w.name} (fp64 global-max softmax over "
+                      f"the oracle's own dequantised K/V)",
             "per_core_gflops": value * 1e3 / threads,
             "single_thread": {"gflops": sel_flops / dt1 / 1e9, "seconds": dt1,
-                              "sample": f"every 16th row ({sel.size} rows) of {w.name}"},
+                              "sample": f"every 64th row ({sel.size} rows) of {w.name}"},
             "cpu_model": cpu_model()}
 
 
@@ -445,7 +466,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--legs", default="prefill-q4kv-8k,window-prefill-32k,decode-64slots-q4kv,"
+    ap.add_argument("--legs", default="tiny-prefill-128,prefill-f32kv-2k,window-prefill-32k,"
+                                      "decode-64slots-q4kv,"
                                       "prefill-q4kv-8k-shadow,decode-64slots-q4kv-shadow,"
                                       "decode-64slots-f32kv,"
                                       "paged-varlen-8k,paged-decode-64req-f32kv,merge-attn-states",
@@ -484,10 +506,11 @@ def main() -> int:
         print(json.dumps(leg), flush=True)
         return 0
 
-    head = workloads.BY_NAME["prefill-f32kv-2k"]
+    head = workloads.BY_NAME["prefill-q4kv-8k"]
     print(f"[bench] {head.name}: warmup {args.warmup}, steps {args.steps}", file=sys.stderr,
           flush=True)
     main_leg = prefill_leg(fa, torch, head, args.steps, args.warmup, graph=not args.eager)
+    torch.cuda.empty_cache()
     legs = []
     for name in [s for s in args.legs.split(",") if s]:
         print(f"[bench] leg {name}", file=sys.stderr, flush=True)
@@ -506,6 +529,27 @@ def main() -> int:
     rec = measured_traffic("prefill", head.name)
     traffic_bytes = round(rec["traffic_bytes"]) if rec else None
     traffic_src = f"profiles/hbm_traffic__{head.name}.md" if rec else None
+    # the metric's decode half: the 64-slot Q4_0 decode leg (run here if the
+    # leg list left it out)
+    dec = next((g for g in legs if g.get("workload") == "decode-64slots-q4kv"), None)
+    if dec is None:
+        print("[bench] decode-64slots-q4kv (decode roofline)", file=sys.stderr, flush=True)
+        dec = run_leg("decode-64slots-q4kv")
+    drec = measured_traffic("decode", dec["workload"])
+    roofline_decode = {
+        "bound": "hbm", "workload": dec["workload"],
+        "kernel": "fa_decode: decode_partial_kernel<256,8,q4_0> + decode_combine_kernel<256,8>",
+        "achieved": round(dec["gbs"], 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+        "frac": round(dec["gbs"] / PEAK_HBM_GBS, 4),
+        "traffic": round(drec["traffic_bytes"]) if drec else None,
+        "traffic_source": f"profiles/hbm_traffic__{dec['workload']}.md" if drec else None,
+        "kernel_ms": round(dec["decode_ms"], 5), "bytes_per_launch": dec["bytes"],
+        # a Q4_0 cache at G = 8 needs 28.4 FLOP per KV byte, past the fp32 ridge:
+        # the fp32 MFMA peak caps this call below 8 TB/s
+        "fp32_compute_ceiling_gbs": round(dec["fp32_compute_ceiling_gbs"], 1),
+        "frac_of_fp32_ceiling": round(dec["frac_of_min_ceiling"], 4),
+        "frac_fp32_mfma_peak": round(dec["frac_fp32_mfma_peak"], 4),
+    }
     line = {
         "metric": METRIC,
         "value": round(main_leg["tflops_step"], 3),
@@ -521,18 +565,20 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": head.name, "n": head.n, "pos0": head.pos0,
                    "n_head": head.n_head, "n_kv_head": head.n_kv_head,
-                   "head_dim": head.head_dim, "kv": "f32", "attn_sink": head.attn_sink,
-                   "attn_win": head.attn_win, "step": "fa_kv_append + fa_prefill",
+                   "head_dim": head.head_dim, "kv": "q4_0", "attn_sink": head.attn_sink,
+                   "attn_win": head.attn_win, "step": "fa_prefill",
+                   "append_ms": round(main_leg["append_ms"], 5),
                    "launch": main_leg["launch"],
                    "ms_per_step_eager": round(main_leg["ms_per_step_eager"], 4)},
         "roofline": {"bound": "mfma",
-                     "kernel": "fa_prefill: prefill_kernel<256,8,f32> + prefill_combine_kernel<256,8>",
+                     "kernel": "fa_prefill: prefill_kernel<256,8,q4_0> + prefill_combine_kernel<256,8>",
                      "achieved": round(kern_tflops, 3), "peak": PEAK_FP32_MFMA_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(kern_tflops / PEAK_FP32_MFMA_TFLOPS, 4),
                      "traffic": traffic_bytes,
                      "traffic_source": traffic_src,
                      "kernel_ms": round(main_leg["prefill_kernel_ms"], 5),
                      "flops_per_launch": main_leg["flops"]},
+        "roofline_decode": roofline_decode,
         "cpu_baseline": cpu,
         "legs": legs,
         **extra,

@@ -15,6 +15,11 @@ TOL_Q4 = 2e-4      # same, Q4_0 KV cache (oracle on the same dequantised K/V)
 ORACLE_THREADS = min(16, os.cpu_count() or 1)
 
 
+# Parity figures of this session (max |gpu - oracle| per compared output);
+# tests/conftest.py prints them in the terminal summary, passing tests included.
+PARITY_LINES: list[str] = []
+
+
 def log(msg: str) -> None:
     print(f"[gpu-test] {msg}", flush=True)
 
@@ -54,7 +59,9 @@ def compare_rows(gpu: np.ndarray, ref: np.ndarray, tol: float, what: str) -> flo
     bad = np.nonzero(decided & (am_g != am_r))[0]
     assert bad.size == 0, f"{what}: argmax differs on rows {bad[:8]}"
     near = int((~decided).sum())
-    log(f"{what}: max_abs={err:.3e} rows={gpu.shape[0]} near_ties={near}")
+    line = f"{what}: max_abs={err:.3e} (bar {tol:.0e}) rows={gpu.shape[0]} near_ties={near}"
+    PARITY_LINES.append(line)
+    log(line)
     return err
 
 
