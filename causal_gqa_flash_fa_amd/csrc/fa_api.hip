@@ -77,6 +77,14 @@ size_t slot_stride_bytes(const fa_cache *c) {
 // The HIP error behind this thread's most recent FA_EHIP.
 thread_local hipError_t g_last_hip_error = hipSuccess;
 
+// Decode scratch owned by the library, for fa_decode_noalloc: every GPU holds
+// its own copy of this array for the life of the process. Its name is a
+// host-side stand-in in host code, never a device address: fa_init resolves
+// each device's address once (hipGetSymbolAddress, with that device current)
+// into g_scratch, and only that address is passed to kernels.
+static __device__ __align__(256) unsigned char scratch[FA_DECODE_SCRATCH_BYTES];
+void *g_scratch[kMaxDevices];
+
 int hip_rc(hipError_t e) {
     if (e == hipSuccess) return FA_OK;
     g_last_hip_error = e;
@@ -109,8 +117,16 @@ int fa_init(void) {
     if (g_device_ok[dev] == 0) {
         hipDeviceProp_t prop;
         if (hip_rc(hipGetDeviceProperties(&prop, dev))) return FA_EHIP;
-        g_device_ok[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+        const bool gfx950 = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+        if (gfx950) {
+            // this device's copy of the decode scratch (the device is current)
+            void *p = nullptr;
+            if (hip_rc(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)))) return FA_EHIP;
+            if (!p) return FA_EHIP;
+            g_scratch[dev] = p;
+        }
         g_device_cus[dev] = prop.multiProcessorCount;
+        g_device_ok[dev] = gfx950 ? 1 : -1;
     }
     return g_device_ok[dev] == 1 ? FA_OK : FA_EDEVICE;
 }
@@ -399,10 +415,15 @@ size_t fa_decode_workspace_bytes(const fa_cache *cache, int n_slots, int n_head,
     return decode_layout(cache, n_slots, n_head, max_ctx).total;
 }
 
-int fa_decode(const fa_cache *cache, const float *q, const int *d_pos, int n_slots,
-              int max_ctx_hint, int n_head, int attn_sink, int attn_win, float scale,
-              float *out, void *ws, size_t ws_bytes, unsigned long long *tile_stats,
-              void *stream) {
+}  // extern "C"
+
+namespace {
+// fa_decode with the caller's workspace, or (use_scratch) with this GPU's
+// library-owned scratch.
+int decode_entry(const fa_cache *cache, const float *q, const int *d_pos, int n_slots,
+                 int max_ctx_hint, int n_head, int attn_sink, int attn_win, float scale,
+                 float *out, void *ws, size_t ws_bytes, bool use_scratch,
+                 unsigned long long *tile_stats, void *stream) {
     int rc = check_cache(cache);
     if (rc) return rc;
     if ((rc = check_heads(cache, n_head))) return rc;
@@ -410,11 +431,17 @@ int fa_decode(const fa_cache *cache, const float *q, const int *d_pos, int n_slo
     if (n_slots < 0 || n_slots > cache->n_slots) return FA_EINVAL;
     if (max_ctx_hint < 1 || max_ctx_hint > cache->max_seq) return FA_EINVAL;
     if (n_slots == 0) return FA_OK;
-    if (!q || !d_pos || !out || !ws) return FA_ENULL;
+    if (!q || !d_pos || !out || (!use_scratch && !ws)) return FA_ENULL;
     if (!decode_items_fit(n_slots, cache->n_kv_head)) return FA_EUNSUPPORTED;
     const DecodeLayout lay = decode_layout(cache, n_slots, n_head, max_ctx_hint);
-    if (ws_bytes < lay.total) return FA_EWORKSPACE;
+    if (use_scratch ? lay.total > (size_t)FA_DECODE_SCRATCH_BYTES : ws_bytes < lay.total)
+        return FA_EWORKSPACE;
     if ((rc = fa_init())) return rc;
+    if (use_scratch) {
+        int dev = 0;
+        if (hip_rc(hipGetDevice(&dev))) return FA_EHIP;
+        ws = g_scratch[dev];
+    }
     uint8_t *wsb = (uint8_t *)ws;
     fa::DecodeArgs a{};
     a.q = q;
@@ -465,6 +492,24 @@ int fa_decode(const fa_cache *cache, const float *q, const int *d_pos, int n_slo
     }
     return hip_rc(fa::launch_decode(cache->format, cache->head_dim, group, a, lay.waves,
                                     (hipStream_t)stream));
+}
+}  // namespace
+
+extern "C" {
+
+int fa_decode(const fa_cache *cache, const float *q, const int *d_pos, int n_slots,
+              int max_ctx_hint, int n_head, int attn_sink, int attn_win, float scale,
+              float *out, void *ws, size_t ws_bytes, unsigned long long *tile_stats,
+              void *stream) {
+    return decode_entry(cache, q, d_pos, n_slots, max_ctx_hint, n_head, attn_sink, attn_win,
+                        scale, out, ws, ws_bytes, false, tile_stats, stream);
+}
+
+int fa_decode_noalloc(const fa_cache *cache, const float *q, const int *d_pos, int n_slots,
+                      int max_ctx_hint, int n_head, int attn_sink, int attn_win, float scale,
+                      float *out, unsigned long long *tile_stats, void *stream) {
+    return decode_entry(cache, q, d_pos, n_slots, max_ctx_hint, n_head, attn_sink, attn_win,
+                        scale, out, nullptr, 0, true, tile_stats, stream);
 }
 
 // ---------------------------------------------------------------- paged
@@ -707,7 +752,7 @@ const char *fa_strerror(int code) {
     case FA_EINVAL: return "invalid argument value";
     case FA_ENULL: return "required pointer is NULL";
     case FA_EUNSUPPORTED: return "unsupported head_dim, group size or KV format";
-    case FA_EWORKSPACE: return "decode workspace too small";
+    case FA_EWORKSPACE: return "workspace too small (caller's, or the fixed decode scratch)";
     case FA_EHIP: return "HIP runtime error";
     case FA_ERANGE: return "positions beyond the cache (pos0 + n > max_seq)";
     case FA_EDEVICE: return "current device is not gfx950";

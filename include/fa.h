@@ -42,7 +42,8 @@ extern "C" {
 #define FA_EINVAL       -1  /* a size, index or scalar is out of its valid range */
 #define FA_ENULL        -2  /* a required pointer is NULL */
 #define FA_EUNSUPPORTED -3  /* valid but not built: head_dim, group size or format */
-#define FA_EWORKSPACE   -4  /* decode workspace smaller than fa_decode_workspace_bytes() */
+#define FA_EWORKSPACE   -4  /* workspace smaller than the call needs (or than the fixed
+                               decode scratch of fa_decode_noalloc can hold) */
 #define FA_EHIP         -5  /* the HIP runtime refused a launch or query */
 #define FA_ERANGE       -6  /* positions past the cache (pos0 + n > max_seq) */
 #define FA_EDEVICE      -7  /* current device is not a gfx950 GPU */
@@ -243,6 +244,24 @@ int fa_decode(const fa_cache *cache, const float *q, const int *d_pos, int n_slo
               int max_ctx_hint, int n_head, int attn_sink, int attn_win, float scale,
               float *out, void *ws, size_t ws_bytes, unsigned long long *tile_stats,
               void *stream);
+
+/* For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. The same
+ * call as fa_decode (same kernels, same results bit for bit) without the
+ * workspace argument: the partials live in a scratch array the library
+ * holds on every GPU it runs on, FA_DECODE_SCRATCH_BYTES per GPU, for the
+ * life of the process. Nothing is allocated, freed or cleared per call
+ * (every scratch byte the combine reads is written earlier in the same call).
+ * A call whose fa_decode_workspace_bytes(cache, n_slots, n_head,
+ * max_ctx_hint) exceeds FA_DECODE_SCRATCH_BYTES returns FA_EWORKSPACE. All
+ * calls on one GPU share its scratch: calls that overlap in time on one GPU
+ * (other streams, other host threads) race and corrupt each other's
+ * results; calls on one stream are ordered and safe. Arguments and other
+ * rules as fa_decode. */
+#define FA_DECODE_SCRATCH_BYTES (32u << 20)
+int fa_decode_noalloc(const fa_cache *cache, const float *q, const int *d_pos, int n_slots,
+                      int max_ctx_hint, int n_head, int attn_sink, int attn_win, float scale,
+                      float *out, unsigned long long *tile_stats, void *stream);
 
 /* ------------------------------------------------ paged KV, varlen batch */
 /* A paged fp32 KV cache in the NHD layout of [VT] ReshapeAndCache and

@@ -326,3 +326,24 @@ def test_decode_item_count_beyond_32_bits_is_refused():
     c = cache(n_slots=big + 1, n_kv=1)
     assert rc_decode(c, n_slots=big + 1, ws_bytes=0) == fa.FA_EUNSUPPORTED
     assert rc_decode(c, n_slots=big, ws_bytes=0) == fa.FA_EWORKSPACE
+
+
+def test_decode_noalloc_validation():
+    c = cache(n_slots=4, max_seq=100)
+
+    def rc(c=c, q=FAKE, pos=FAKE, n_slots=1, hint=10, n_head=4, scale=0.1, out=FAKE):
+        return fa.lib.fa_decode_noalloc(ctypes.byref(c) if c is not None else None, q, pos,
+                                        n_slots, hint, n_head, 0, 0, scale, out, None, None)
+    assert rc(c=None) == fa.FA_ENULL
+    assert rc(n_slots=5) == fa.FA_EINVAL
+    assert rc(hint=0) == fa.FA_EINVAL
+    assert rc(scale=0.0) == fa.FA_EINVAL
+    assert rc(n_head=3) == fa.FA_EINVAL
+    assert rc(n_slots=0) == fa.FA_OK
+    assert rc(q=0) == fa.FA_ENULL
+    assert rc(pos=0) == fa.FA_ENULL
+    assert rc(out=0) == fa.FA_ENULL
+    # a call that needs more than the library's fixed scratch is refused
+    big = cache(fmt=fa.FA_KV_Q4_0, n_slots=4096, n_kv=2, hd=256, max_seq=4)
+    assert fa.fa_decode_workspace_bytes(big, 4096, 16, 4) > fa.DECODE_SCRATCH_BYTES
+    assert rc(c=big, n_slots=4096, hint=4, n_head=16) == fa.FA_EWORKSPACE
