@@ -44,8 +44,8 @@ CSRC = os.path.join(ROOT, "causal_gqa_flash_fa_amd", "csrc")
 # committed HBM counter figures stale.
 KERNEL_SOURCES = {
     "prefill": ["fa_prefill.hip", "fa_device.hpp", "fa_internal.hpp", "fa_api.hip"],
-    "decode": ["fa_decode.hip", "fa_device.hpp", "fa_internal.hpp", "fa_api.hip",
-               "fa_shadow.hpp"],
+    "decode": ["fa_decode.hip", "fa_decode_hilo.hip", "fa_decode_sched.hpp", "fa_device.hpp",
+               "fa_internal.hpp", "fa_api.hip", "fa_shadow.hpp"],
     "merge": ["fa_paged.hip", "fa_device.hpp", "fa_internal.hpp", "fa_api.hip"],
 }
 
@@ -343,8 +343,12 @@ def merge_leg(fa, torch, steps: int, warmup: int, T: int = 8192, H: int = 16,
             "traffic_bytes": round(rec["traffic_bytes"]) if rec else None}
 
 
-def decode_leg(fa, torch, w, steps: int, warmup: int) -> dict:
+def decode_leg(fa, torch, w, steps: int, warmup: int, lane: str = "fp32") -> dict:
+    """fa_decode (lane "fp32") or fa_decode_q4_hilo (lane "hilo": the Q4_0
+    decode on fp16 MFMA with hi/lo-split operands) over the slots' cache,
+    timed with HIP events, the last-level cache flushed between reps."""
     dev = torch.device("cuda:0")
+    call = fa.fa_decode_q4_hilo if lane == "hilo" else fa.fa_decode
     ctx = workloads.decode_ctx(w)
     cache, kt, vt = fa.make_cache(w.kv_format, w.n_slots, w.n_kv_head, w.head_dim, w.max_seq, dev)
     shadow = fa.add_shadow(cache, w.shadow_sink, w.shadow_win, dev) \
@@ -365,7 +369,7 @@ def decode_leg(fa, torch, w, steps: int, warmup: int) -> dict:
     def step(i=None):
         if i is not None:
             ev[i][0].record()
-        fa.fa_decode(cache, q, pos, w.n_slots, hint, w.n_head, 0, 0, w.scale, out, ws, ws_bytes)
+        call(cache, q, pos, w.n_slots, hint, w.n_head, 0, 0, w.scale, out, ws, ws_bytes)
         if i is not None:
             ev[i][1].record()
 
@@ -385,7 +389,9 @@ def decode_leg(fa, torch, w, steps: int, warmup: int) -> dict:
     gbs = (kv_bytes + qo_bytes) / ms / 1e6
     compute_ceiling_gbs = PEAK_FP32_MFMA_TFLOPS * 1e12 / (flops / (kv_bytes + qo_bytes)) / 1e9
     return {
-        "workload": w.name, "kind": "decode", "kv": "q4_0" if w.kv_format else "f32",
+        "workload": w.name + ("-hilo" if lane == "hilo" else ""), "kind": "decode",
+        "lane": "fp16 MFMA, hi/lo-split operands" if lane == "hilo" else "fp32 MFMA",
+        "kv": "q4_0" if w.kv_format else "f32",
         "n_slots": w.n_slots, "ctx_sum": int(ctx.sum()), "ctx_min": int(ctx.min()),
         "ctx_max": int(ctx.max()), "launch_splits": fa.fa_decode_plan(hint)[0],
         "shadow_sink": w.shadow_sink, "shadow_win": w.shadow_win,
@@ -397,7 +403,9 @@ def decode_leg(fa, torch, w, steps: int, warmup: int) -> dict:
         "frac_fp32_mfma_peak": flops / ms / 1e9 / PEAK_FP32_MFMA_TFLOPS,
         "fp32_compute_ceiling_gbs": compute_ceiling_gbs,
         "frac_of_min_ceiling": gbs / min(PEAK_HBM_GBS, compute_ceiling_gbs),
-        "traffic_bytes": (round(rec["traffic_bytes"]) if (rec := measured_traffic("decode", w.name))
+        "traffic_bytes": (round(rec["traffic_bytes"])
+                          if (rec := measured_traffic("decode", w.name + ("-hilo" if lane == "hilo"
+                                                                          else "")))
                           else None),
     }
 
@@ -467,7 +475,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--legs", default="tiny-prefill-128,prefill-f32kv-2k,window-prefill-32k,"
-                                      "decode-64slots-q4kv,"
+                                      "decode-64slots-q4kv,decode-64slots-q4kv-hilo,"
                                       "prefill-q4kv-8k-shadow,decode-64slots-q4kv-shadow,"
                                       "decode-64slots-f32kv,"
                                       "paged-varlen-8k,paged-decode-64req-f32kv,merge-attn-states",
@@ -494,6 +502,9 @@ def main() -> int:
     def run_leg(name):
         if name == "merge-attn-states":
             return merge_leg(fa, torch, args.steps, args.warmup)
+        if name.endswith("-hilo"):
+            return decode_leg(fa, torch, workloads.BY_NAME[name[:-len("-hilo")]], args.steps,
+                              args.warmup, lane="hilo")
         w = workloads.BY_NAME[name]
         fn = {"prefill": prefill_leg, "decode": decode_leg, "paged": paged_leg,
               "paged_decode": paged_decode_leg}[w.kind]

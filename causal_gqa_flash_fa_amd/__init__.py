@@ -31,7 +31,8 @@ EXPORTS = [
     "fa_cache_row_bytes", "fa_cache_bytes", "fa_init", "fa_kv_append", "fa_kv_append_slots",
     "fa_prefill",
     "fa_prefill_tile_shape", "fa_prefill_workspace_bytes", "fa_decode_plan", "fa_decode_plan_params",
-    "fa_decode_workspace_bytes", "fa_decode", "fa_decode_noalloc", "fa_strerror",
+    "fa_decode_workspace_bytes", "fa_decode", "fa_decode_q4_hilo", "fa_decode_noalloc",
+    "fa_strerror",
     "fa_last_hip_error",
     "fa_paged_append", "fa_paged_workspace_bytes", "fa_paged_attention", "fa_merge_attn_states",
     "fa_paged_decode", "fa_paged_decode_workspace_bytes",
@@ -109,6 +110,8 @@ def _load() -> ctypes.CDLL:
     L.fa_decode_workspace_bytes.restype = Z
     L.fa_decode.argtypes = [C, P, P, I, I, I, I, I, F, P, P, Z, P, P]
     L.fa_decode.restype = I
+    L.fa_decode_q4_hilo.argtypes = [C, P, P, I, I, I, I, I, F, P, P, Z, P, P]
+    L.fa_decode_q4_hilo.restype = I
     L.fa_decode_noalloc.argtypes = [C, P, P, I, I, I, I, I, F, P, P, P]
     L.fa_decode_noalloc.restype = I
     PC = ctypes.POINTER(fa_paged_cache)
@@ -229,6 +232,15 @@ def fa_decode(cache: fa_cache, q, d_pos, n_slots: int, max_ctx_hint: int, n_head
     _check(lib.fa_decode(ctypes.byref(cache), _ptr(q), _ptr(d_pos), n_slots, max_ctx_hint,
                          n_head, attn_sink, attn_win, scale, _ptr(out), _ptr(ws), ws_bytes,
                          _ptr(tile_stats), _stream(stream)), "fa_decode")
+
+
+def fa_decode_q4_hilo(cache: fa_cache, q, d_pos, n_slots: int, max_ctx_hint: int, n_head: int,
+                      attn_sink: int, attn_win: int, scale: float, out, ws, ws_bytes: int,
+                      tile_stats=None, stream=None) -> None:
+    _check(lib.fa_decode_q4_hilo(ctypes.byref(cache), _ptr(q), _ptr(d_pos), n_slots,
+                                 max_ctx_hint, n_head, attn_sink, attn_win, scale, _ptr(out),
+                                 _ptr(ws), ws_bytes, _ptr(tile_stats), _stream(stream)),
+           "fa_decode_q4_hilo")
 
 
 # Bytes of the library's per-GPU decode scratch (fa_decode_noalloc).

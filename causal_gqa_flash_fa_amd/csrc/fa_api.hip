@@ -420,12 +420,20 @@ size_t fa_decode_workspace_bytes(const fa_cache *cache, int n_slots, int n_head,
 namespace {
 // fa_decode with the caller's workspace, or (use_scratch) with this GPU's
 // library-owned scratch.
+// The decode's tile contractions: fp32 MFMA (fa_decode), or fp16 MFMA with
+// hi/lo-split operands over a Q4_0 cache (fa_decode_q4_hilo).
+enum class DecodeLane { kFp32, kHilo };
+
 int decode_entry(const fa_cache *cache, const float *q, const int *d_pos, int n_slots,
                  int max_ctx_hint, int n_head, int attn_sink, int attn_win, float scale,
                  float *out, void *ws, size_t ws_bytes, bool use_scratch,
-                 unsigned long long *tile_stats, void *stream) {
+                 unsigned long long *tile_stats, void *stream,
+                 DecodeLane lane = DecodeLane::kFp32) {
     int rc = check_cache(cache);
     if (rc) return rc;
+    if (lane == DecodeLane::kHilo &&
+        (cache->format != FA_KV_Q4_0 || cache->shadow_sink > 0 || cache->shadow_win > 0))
+        return FA_EUNSUPPORTED;
     if ((rc = check_heads(cache, n_head))) return rc;
     if ((rc = check_scale(scale))) return rc;
     if (n_slots < 0 || n_slots > cache->n_slots) return FA_EINVAL;
@@ -490,6 +498,11 @@ int decode_entry(const fa_cache *cache, const float *q, const int *d_pos, int n_
         sp.acc_out = (float *)a.sh_acc;
         a.sh_waves = n_slots * cache->n_kv_head * lay.sh_groups;   // run inside the partial launch
     }
+    if (lane == DecodeLane::kHilo)
+        return hip_rc(fa::launch_decode_hilo(cache->head_dim, group, a,
+                                             lay.waves < fa::kDecodeMaxWavesHilo
+                                                 ? lay.waves : fa::kDecodeMaxWavesHilo,
+                                             (hipStream_t)stream));
     return hip_rc(fa::launch_decode(cache->format, cache->head_dim, group, a, lay.waves,
                                     (hipStream_t)stream));
 }
@@ -503,6 +516,14 @@ int fa_decode(const fa_cache *cache, const float *q, const int *d_pos, int n_slo
               void *stream) {
     return decode_entry(cache, q, d_pos, n_slots, max_ctx_hint, n_head, attn_sink, attn_win,
                         scale, out, ws, ws_bytes, false, tile_stats, stream);
+}
+
+int fa_decode_q4_hilo(const fa_cache *cache, const float *q, const int *d_pos, int n_slots,
+                      int max_ctx_hint, int n_head, int attn_sink, int attn_win, float scale,
+                      float *out, void *ws, size_t ws_bytes, unsigned long long *tile_stats,
+                      void *stream) {
+    return decode_entry(cache, q, d_pos, n_slots, max_ctx_hint, n_head, attn_sink, attn_win,
+                        scale, out, ws, ws_bytes, false, tile_stats, stream, DecodeLane::kHilo);
 }
 
 int fa_decode_noalloc(const fa_cache *cache, const float *q, const int *d_pos, int n_slots,

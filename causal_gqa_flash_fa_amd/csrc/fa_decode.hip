@@ -53,6 +53,7 @@
 #include "fa_device.hpp"
 #include "fa_internal.hpp"
 #include "fa_shadow.hpp"
+#include "fa_decode_sched.hpp"
 
 namespace fa {
 namespace {
@@ -98,31 +99,6 @@ __device__ __forceinline__ float byte_f(uint32_t w, int t) {
     return (float)((w >> (8 * t)) & 0xffu);   // v_cvt_f32_ubyte{t}
 }
 
-__device__ __forceinline__ int wave_sum_i(int x) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
-    return x;
-}
-__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(x, o);
-        if (lane >= o) x += y;
-    }
-    return x;
-}
-
-// Items (splits) of a slot whose query sits at `pos`; 0 for a position
-// outside the cache.
-__device__ __forceinline__ int slot_items(int pos, const DecodeArgs &a, int *split_len) {
-    if (pos < 0 || pos >= a.max_seq) {
-        *split_len = kDecodeKeyTile;
-        return 0;
-    }
-    int n;
-    return decode_plan(pos + 1, a.kps, a.cap, kDecodeKeyTile, &n, split_len);
-}
-
 template <int HD, int G, int FMT, bool PG>
 // Q4_0 tiles run two waves per SIMD (bound by issue, the waves hide each
 // other's latencies); fp32 tiles one (bound by HBM: the whole register file
@@ -151,33 +127,12 @@ void decode_partial_kernel(DecodeArgs a) {
     }
     const int w = blockIdx.x - (FMT == 1 ? a.sh_waves : 0);
     const int NW = gridDim.x - (FMT == 1 ? a.sh_waves : 0);
-    const int nsegs = a.n_slots * a.n_kv;
-    // query position of a slot (paged: the request's last position, its
-    // length clamped to its block-table row)
-    auto pos_of = [&](int slot) -> int {
-        if constexpr (PG) return min(max(a.seq_lens[slot], 0), a.max_seq) - 1;
-        else return a.pos[slot];
-    };
-
-    // ---- pass 1: total number of items
-    int total = 0;
-    for (int base = 0; base < nsegs; base += 64) {
-        const int s = base + lane;
-        int sl;
-        const int it = s < nsegs ? slot_items(pos_of(s / a.n_kv), a, &sl) : 0;
-        total += __builtin_amdgcn_readfirstlane(wave_sum_i(it));
-    }
-    const long long lo = (long long)w * total / NW;
-    const long long hi = (long long)(w + 1) * total / NW;
-    // wave owning item f: the last wave whose run starts at or before f
-    auto owner = [&](long long f) -> int { return (int)(((f + 1) * NW - 1) / total); };
-
     unsigned vis = 0, skp = 0;
 
     // ---- per-segment fold of items [it_lo, it_hi) into one partial
     auto run_segment = [&](int seg, int it_lo, int it_hi, int pidx) {
         const int slot = seg / a.n_kv, kvh = seg % a.n_kv;
-        const int pos = __builtin_amdgcn_readfirstlane(pos_of(slot));
+        const int pos = __builtin_amdgcn_readfirstlane(decode_query_pos<PG>(a, slot));
         const bool shadowed = a.sh.sink > 0 || a.sh.win > 0;
         const int *wpos = a.sh.win_pos + (size_t)slot * kShadowWinMax;
         int split_len;
@@ -708,36 +663,7 @@ void decode_partial_kernel(DecodeArgs a) {
         }
     };
 
-    // ---- pass 2: segment prefix sums, the partial table, and this wave's run
-    int f_carry = 0, p_carry = 0;
-    for (int base = 0; base < nsegs; base += 64) {
-        const int s = base + lane;
-        int sl;
-        const int it = s < nsegs ? slot_items(pos_of(s / a.n_kv), a, &sl) : 0;
-        const int incl = wave_incl_scan(it, lane);
-        const int F = f_carry + incl - it;
-        const int nw = it > 0 ? owner(F + it - 1) - owner(F) + 1 : 0;
-        const int inclw = wave_incl_scan(nw, lane);
-        const int P = p_carry + inclw - nw;
-        if (w == 0 && s < nsegs) {
-            a.seg_table[2 * s] = P;
-            a.seg_table[2 * s + 1] = nw;
-        }
-        unsigned long long hit = __ballot(it > 0 && F < hi && F + it > lo);
-        while (hit) {
-            const int b = __builtin_ctzll(hit);
-            hit &= hit - 1;
-            // lane b's values, as wave-uniform (scalar) values
-            const int Fs = __builtin_amdgcn_readfirstlane(__shfl(F, b));
-            const int its = __builtin_amdgcn_readfirstlane(__shfl(it, b));
-            const int Ps = __builtin_amdgcn_readfirstlane(__shfl(P, b));
-            const int it_lo = (int)max(lo, (long long)Fs) - Fs;
-            const int it_hi = (int)min(hi, (long long)Fs + its) - Fs;
-            run_segment(base + b, it_lo, it_hi, Ps + (w - owner(Fs)));
-        }
-        f_carry += __builtin_amdgcn_readfirstlane(__shfl(incl, 63));
-        p_carry += __builtin_amdgcn_readfirstlane(__shfl(inclw, 63));
-    }
+    decode_stream_k<PG>(a, w, NW, lane, run_segment);
 
     if (a.stats && lane == 0) {
         atomicAdd(&a.stats[0], (unsigned long long)vis);
@@ -854,6 +780,20 @@ hipError_t launch_decode(int format, int head_dim, int group, const DecodeArgs &
 hipError_t launch_paged_decode(int head_dim, int group, const DecodeArgs &a, int waves,
                                hipStream_t s) {
     return by_dim<0, true>(head_dim, group, a, waves, s);
+}
+
+hipError_t launch_decode_combine(int head_dim, int group, const DecodeArgs &a, hipStream_t s) {
+    const dim3 grid(a.n_slots * a.n_head);
+#define FA_COMBINE(HD, G)                                                                      \
+    if (head_dim == HD && group == G) {                                                        \
+        hipLaunchKernelGGL((decode_combine_kernel<HD, G>), grid, dim3(HD), 0, s, a);           \
+        return hipGetLastError();                                                              \
+    }
+    FA_COMBINE(64, 1) FA_COMBINE(64, 2) FA_COMBINE(64, 4) FA_COMBINE(64, 8)
+    FA_COMBINE(128, 1) FA_COMBINE(128, 2) FA_COMBINE(128, 4) FA_COMBINE(128, 8)
+    FA_COMBINE(256, 1) FA_COMBINE(256, 2) FA_COMBINE(256, 4) FA_COMBINE(256, 8)
+#undef FA_COMBINE
+    return hipErrorInvalidValue;
 }
 
 }  // namespace fa

@@ -1,0 +1,106 @@
+// Stream-K schedule of the split-KV decode, shared by the decode kernels.
+//
+// [FA] "Decode-mode flash attention" and fc_attn_dec_plan: every slot's keys
+// [0, pos] are cut into splits by the plan, computed on the device from that
+// slot's own position. The splits of all (slot, kv head) segments, in order,
+// form one list of work items, and a fixed grid of single-wave work-groups
+// takes equal contiguous runs of it. A wave folds every split of one segment
+// that falls in its run into one running state (consecutive splits are
+// consecutive keys) and writes one partial per segment it touches. The list
+// and the partial offsets are recomputed by every wave from the device
+// positions with wave scans; wave 0 also writes the per-segment partial
+// table {first partial, partial count} that the combine reads.
+#pragma once
+
+#include "fa_device.hpp"
+#include "fa_internal.hpp"
+
+namespace fa {
+
+__device__ __forceinline__ int wave_sum_i(int x) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+    return x;
+}
+
+__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+    }
+    return x;
+}
+
+// Items (splits) of a slot whose query sits at `pos`; 0 for a position
+// outside the cache.
+__device__ __forceinline__ int slot_items(int pos, const DecodeArgs &a, int *split_len) {
+    if (pos < 0 || pos >= a.max_seq) {
+        *split_len = kDecodeKeyTile;
+        return 0;
+    }
+    int n;
+    return decode_plan(pos + 1, a.kps, a.cap, kDecodeKeyTile, &n, split_len);
+}
+
+// Query position of a slot (paged: the request's last position, its length
+// clamped to its block-table row).
+template <bool PG>
+__device__ __forceinline__ int decode_query_pos(const DecodeArgs &a, int slot) {
+    if constexpr (PG) return min(max(a.seq_lens[slot], 0), a.max_seq) - 1;
+    else return a.pos[slot];
+}
+
+// Runs wave w's share (of NW waves) of the item list: for every segment its
+// run touches, calls run_segment(seg, it_lo, it_hi, partial) with the run's
+// items [it_lo, it_hi) of that segment and the index of the partial it writes.
+template <bool PG, class SegFn>
+__device__ __forceinline__ void decode_stream_k(const DecodeArgs &a, int w, int NW, int lane,
+                                                SegFn &&run_segment) {
+    const int nsegs = a.n_slots * a.n_kv;
+    // ---- pass 1: total number of items
+    int total = 0;
+    for (int base = 0; base < nsegs; base += 64) {
+        const int s = base + lane;
+        int sl;
+        const int it = s < nsegs ? slot_items(decode_query_pos<PG>(a, s / a.n_kv), a, &sl) : 0;
+        total += __builtin_amdgcn_readfirstlane(wave_sum_i(it));
+    }
+    const long long lo = (long long)w * total / NW;
+    const long long hi = (long long)(w + 1) * total / NW;
+    // wave owning item f: the last wave whose run starts at or before f
+    auto owner = [&](long long f) -> int { return (int)(((f + 1) * NW - 1) / total); };
+
+    // ---- pass 2: segment prefix sums, the partial table, and this wave's run
+    int f_carry = 0, p_carry = 0;
+    for (int base = 0; base < nsegs; base += 64) {
+        const int s = base + lane;
+        int sl;
+        const int it = s < nsegs ? slot_items(decode_query_pos<PG>(a, s / a.n_kv), a, &sl) : 0;
+        const int incl = wave_incl_scan(it, lane);
+        const int F = f_carry + incl - it;
+        const int nw = it > 0 ? owner(F + it - 1) - owner(F) + 1 : 0;
+        const int inclw = wave_incl_scan(nw, lane);
+        const int P = p_carry + inclw - nw;
+        if (w == 0 && s < nsegs) {
+            a.seg_table[2 * s] = P;
+            a.seg_table[2 * s + 1] = nw;
+        }
+        unsigned long long hit = __ballot(it > 0 && F < hi && F + it > lo);
+        while (hit) {
+            const int b = __builtin_ctzll(hit);
+            hit &= hit - 1;
+            // lane b's values, as wave-uniform (scalar) values
+            const int Fs = __builtin_amdgcn_readfirstlane(__shfl(F, b));
+            const int its = __builtin_amdgcn_readfirstlane(__shfl(it, b));
+            const int Ps = __builtin_amdgcn_readfirstlane(__shfl(P, b));
+            const int it_lo = (int)max(lo, (long long)Fs) - Fs;
+            const int it_hi = (int)min(hi, (long long)Fs + its) - Fs;
+            run_segment(base + b, it_lo, it_hi, Ps + (w - owner(Fs)));
+        }
+        f_carry += __builtin_amdgcn_readfirstlane(__shfl(incl, 63));
+        p_carry += __builtin_amdgcn_readfirstlane(__shfl(inclw, 63));
+    }
+}
+
+}  // namespace fa

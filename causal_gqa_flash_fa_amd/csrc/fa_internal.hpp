@@ -82,6 +82,10 @@ constexpr int kDecodeSplitCap = 512;
 // half the run boundaries and partials.
 constexpr int kDecodeMaxWaves = 2048;
 constexpr int kDecodeMaxWavesF32 = 1024;
+// The fp16 hi/lo Q4_0 decode: two waves per SIMD as well (its MFMA results
+// then stay in VGPRs; at one wave per SIMD the compiler moved them through
+// AGPRs every tile).
+constexpr int kDecodeMaxWavesHilo = 2048;
 
 // Requests of one paged prefill launch (their table sits in LDS).
 constexpr int kPagedMaxReqs = 1024;
@@ -238,6 +242,12 @@ hipError_t launch_decode(int format, int head_dim, int group, const DecodeArgs &
                          hipStream_t s);
 hipError_t launch_paged_decode(int head_dim, int group, const DecodeArgs &a, int waves,
                                hipStream_t s);
+// The combine pass of fa_decode alone (decode partials already written).
+hipError_t launch_decode_combine(int head_dim, int group, const DecodeArgs &a, hipStream_t s);
+// Q4_0 decode on fp16 MFMA with hi/lo-split operands (fa_decode_q4_hilo):
+// partial pass over a Q4_0 cache without fp16 shadow, then the combine.
+hipError_t launch_decode_hilo(int head_dim, int group, const DecodeArgs &a, int waves,
+                              hipStream_t s);
 
 // Host copy of the device plan ([FA] fc_attn_dec_plan).
 __host__ __device__ inline int decode_plan(int seq_len, int kps, int cap, int tile, int *n_splits,

@@ -245,6 +245,25 @@ int fa_decode(const fa_cache *cache, const float *q, const int *d_pos, int n_slo
               float *out, void *ws, size_t ws_bytes, unsigned long long *tile_stats,
               void *stream);
 
+/* fa_decode over a Q4_0 cache with the two tile contractions on fp16 matrix
+ * cores (v_mfma_f32_16x16x32_f16, fp32 accumulate) instead of fp32 ones: an
+ * opt-in lane that departs from fp32 operands, in the way of [FA]'s
+ * "NARROW-STAGING prefill variants" note (fp16-narrowed K staging) and of
+ * the two-pass hi/lo activation lane of the logicaffeine
+ * codegen_cuda/qwen38_batched.rs page, so that a decode over 4-bit keys and
+ * values is no longer bound by the fp32 matrix rate. Q4_0 codes are exact
+ * binary16 values; q, and p times each key's block scale, are carried as an
+ * fp16 high part plus an fp16 low part (their rounding error), so every
+ * product is exact and sums are fp32: results agree with fa_decode to about
+ * fp32 rounding (the oracle bar of the Q4_0 cache applies), not bit for bit.
+ * Same arguments, workspace (fa_decode_workspace_bytes), schedule, partials
+ * and combine as fa_decode. The cache must be FA_KV_Q4_0 without an fp16
+ * shadow (FA_EUNSUPPORTED otherwise); other rules as fa_decode. */
+int fa_decode_q4_hilo(const fa_cache *cache, const float *q, const int *d_pos, int n_slots,
+                      int max_ctx_hint, int n_head, int attn_sink, int attn_win, float scale,
+                      float *out, void *ws, size_t ws_bytes, unsigned long long *tile_stats,
+                      void *stream);
+
 /* For callers that cannot allocate device memory: code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc. The same
  * call as fa_decode (same kernels, same results bit for bit) without the

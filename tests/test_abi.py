@@ -347,3 +347,20 @@ def test_decode_noalloc_validation():
     big = cache(fmt=fa.FA_KV_Q4_0, n_slots=4096, n_kv=2, hd=256, max_seq=4)
     assert fa.fa_decode_workspace_bytes(big, 4096, 16, 4) > fa.DECODE_SCRATCH_BYTES
     assert rc(c=big, n_slots=4096, hint=4, n_head=16) == fa.FA_EWORKSPACE
+
+
+def test_decode_q4_hilo_validation():
+    def rc(c, n_slots=1, hint=10, n_head=4, ws_bytes=1 << 30):
+        return fa.lib.fa_decode_q4_hilo(ctypes.byref(c), FAKE, FAKE, n_slots, hint, n_head, 0, 0,
+                                        0.1, FAKE, FAKE, ws_bytes, None, None)
+    # Q4_0 caches only, and none with an fp16 shadow
+    assert rc(cache(fmt=fa.FA_KV_F32, n_slots=4)) == fa.FA_EUNSUPPORTED
+    shadowed = cache(fmt=fa.FA_KV_Q4_0, n_slots=4)
+    shadowed.shadow_sink, shadowed.k_sink, shadowed.v_sink = 4, FAKE, FAKE
+    assert rc(shadowed) == fa.FA_EUNSUPPORTED
+    c = cache(fmt=fa.FA_KV_Q4_0, n_slots=4)
+    assert rc(c, n_slots=5) == fa.FA_EINVAL
+    assert rc(c, n_head=3) == fa.FA_EINVAL
+    assert rc(c, n_slots=0) == fa.FA_OK
+    need = fa.fa_decode_workspace_bytes(c, 4, 4, 100)
+    assert rc(c, n_slots=4, hint=100, ws_bytes=need - 1) == fa.FA_EWORKSPACE
