@@ -77,7 +77,9 @@ struct HShape {
     static constexpr int TK = 32;                     // keys per tile
     static constexpr int TILE = TK * RB;              // raw tile bytes
     static constexpr int NI = (TILE + 1023) / 1024;   // DMA instructions per tile
-    static constexpr int PS = TK + 4;                 // P table row stride (floats)
+    // P table row stride (floats): padded where the P and D tables still fit
+    // in one K tile
+    static constexpr int PS = 8 * (TK + 4) * 4 + NB * TK * 2 <= TILE ? TK + 4 : TK;
 };
 
 // K/V tile buffers per wave: the tile NBUF - 1 ahead is requested when a
@@ -102,8 +104,7 @@ void decode_hilo_kernel(DecodeArgs a) {
     constexpr int NBUF = kHiloBuffers;
     // ring of NBUF (K tile, V tile) buffers
     __shared__ __attribute__((aligned(16))) uint8_t KV[NBUF * 2 * TILE];
-    __shared__ __attribute__((aligned(16))) float Pt[8 * PS];        // p [head][key]
-    __shared__ __attribute__((aligned(16))) uint16_t Dt[NB * TK];    // V block scales [block][key]
+    static_assert(8 * PS * 4 + NB * TK * 2 <= TILE, "P and D tables fit in a K tile");
 
     const int lane = threadIdx.x;
     const int n16 = lane & 15;          // MFMA column / row index within a 16-lane group
@@ -299,6 +300,13 @@ void decode_hilo_kernel(DecodeArgs a) {
                 if ((t0 & (kDecodeKeyTile - 1)) == 0) vis++;
                 const uint8_t *Kt = KV + 2 * TILE * buf0;
                 const uint8_t *Vt = Kt + TILE;
+                // p [head][key] and the V block scales [block][key] go to this
+                // buffer's K tile once QK has read it (the buffer is refilled
+                // only after every LDS read of this tile has completed). In
+                // arrays of their own, the compiler's LDS-DMA tracking made the
+                // first read of them wait for the next tile's DMA.
+                float *Pt = (float *)(KV + 2 * TILE * buf0);
+                uint16_t *Dt = (uint16_t *)(KV + 2 * TILE * buf0 + 8 * PS * 4);
 
                 // ---- QK: two sets of 16 keys, one MFMA per (set, block) plus
                 // one for the -8 of the codes
@@ -401,7 +409,7 @@ void decode_hilo_kernel(DecodeArgs a) {
                     l[r] += p[r];
                 }
 
-                wave_lds_sync();     // the previous tile's P and D reads are done
+                wave_lds_sync();     // QK's reads of the K tile come first
 #pragma unroll
                 for (int r = 0; r < 4; r++) Pt[(hd4 + r) * PS + kl] = p[r];
                 // V block scales, [block][key]; lane: key lane & 31, blocks of its half
@@ -409,7 +417,8 @@ void decode_hilo_kernel(DecodeArgs a) {
                     const int vk = lane & 31;
                     int emax = 0;
 #pragma unroll
-                    for (int b = lane >> 5; b < NB; b += 2) {
+                    for (int i = 0; i < NB / 2; i++) {        // same trip count in every lane
+                        const int b = 2 * i + (lane >> 5);
                         const uint16_t dbits = *(const uint16_t *)(Vt + vk * RB + 18 * b);
                         Dt[b * TK + vk] = dbits;
                         emax = max(emax, (int)((dbits >> 10) & 31));
