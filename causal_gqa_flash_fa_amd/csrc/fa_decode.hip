@@ -130,9 +130,9 @@ void decode_partial_kernel(DecodeArgs a) {
     unsigned vis = 0, skp = 0;
 
     // ---- per-segment fold of items [it_lo, it_hi) into one partial
-    auto run_segment = [&](int seg, int it_lo, int it_hi, int pidx) {
+    auto run_segment = [&](int seg, int pos_seg, int it_lo, int it_hi, int pidx) {
         const int slot = seg / a.n_kv, kvh = seg % a.n_kv;
-        const int pos = __builtin_amdgcn_readfirstlane(decode_query_pos<PG>(a, slot));
+        const int pos = pos_seg;
         const bool shadowed = a.sh.sink > 0 || a.sh.win > 0;
         const int *wpos = a.sh.win_pos + (size_t)slot * kShadowWinMax;
         int split_len;

@@ -76,7 +76,14 @@ struct HShape {
     static constexpr int RB = NB * kQ4BlockBytes;     // row bytes
     static constexpr int TK = 32;                     // keys per tile
     static constexpr int TILE = TK * RB;              // raw tile bytes
-    static constexpr int NI = (TILE + 1023) / 1024;   // DMA instructions per tile
+    // LDS slot of a tile: TILE rounded up to 256 bytes
+    static constexpr int TSTR = (TILE + 255) / 256 * 256;
+    // DMA instructions per tile, every lane active: 1 KB ones (16 bytes a
+    // lane), then 256-byte dword ones for the rest of the slot (an LDS DMA
+    // of fewer than 4 bytes still takes 4 bytes of LDS per lane); bytes past
+    // the tile arrive as zeros in the slot's padding
+    static constexpr int REM = TILE % 1024;
+    static constexpr int NI = TILE / 1024 + (REM + 255) / 256;
     // P table row stride (floats): padded where the P and D tables still fit
     // in one K tile
     static constexpr int PS = 8 * (TK + 4) * 4 + NB * TK * 2 <= TILE ? TK + 4 : TK;
@@ -98,12 +105,13 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64, 64), amdgpu_waves_per_
 void decode_hilo_kernel(DecodeArgs a) {
     using Sh = HShape<HD>;
     constexpr int NB = Sh::NB, RB = Sh::RB, TK = Sh::TK, TILE = Sh::TILE, NI = Sh::NI;
+    constexpr int TSTR = Sh::TSTR;
     constexpr int PS = Sh::PS;
     static_assert(G >= 1 && G <= 8, "group of at most 8 heads");
 
     constexpr int NBUF = kHiloBuffers;
     // ring of NBUF (K tile, V tile) buffers
-    __shared__ __attribute__((aligned(16))) uint8_t KV[NBUF * 2 * TILE];
+    __shared__ __attribute__((aligned(16))) uint8_t KV[NBUF * 2 * TSTR];
     static_assert(8 * PS * 4 + NB * TK * 2 <= TILE, "P and D tables fit in a K tile");
 
     const int lane = threadIdx.x;
@@ -113,9 +121,9 @@ void decode_hilo_kernel(DecodeArgs a) {
     const int w = blockIdx.x, NW = gridDim.x;
     unsigned vis = 0, skp = 0;
 
-    auto run_segment = [&](int seg, int it_lo, int it_hi, int pidx) {
+    auto run_segment = [&](int seg, int pos_seg, int it_lo, int it_hi, int pidx) {
         const int slot = seg / a.n_kv, kvh = seg % a.n_kv;
-        const int pos = __builtin_amdgcn_readfirstlane(decode_query_pos<false>(a, slot));
+        const int pos = pos_seg;
         int split_len;
         slot_items(pos, a, &split_len);
         const int L = pos + 1;
@@ -126,6 +134,60 @@ void decode_hilo_kernel(DecodeArgs a) {
         const uint8_t *vb = (const uint8_t *)a.v + head_rows * RB;
         const int win_first = pos - a.win + 1;
 
+        // first visited tile at or after j ([FA] fc_attn_tile_in_window), in
+        // the plan's 64-key tiles
+        auto next_visited = [&](int j) -> int {
+            if (j < k_hi && a.win > 0 && j >= a.sink &&
+                min(j + kDecodeKeyTile - 1, k_hi - 1) < win_first) {
+                const int jn = (win_first / kDecodeKeyTile) * kDecodeKeyTile;
+                const int stop = min(jn, k_hi);
+                skp += (unsigned)((stop - j + kDecodeKeyTile - 1) / kDecodeKeyTile);
+                return jn >= k_hi ? k_hi : jn;
+            }
+            return j;
+        };
+        // raw 32-key K and V tiles at t0 <= k_hi into buffer `buf`; rows past
+        // k_hi arrive as zeros (t0 = k_hi: an all-zero tile). The LDS destination stays in the LDS address space
+        // (a generic pointer would have to be cast back).
+        typedef __attribute__((address_space(3))) uint8_t lds_u8;
+        auto dma_tile = [&](int buf, int t0) {
+            const unsigned bytes = (unsigned)(max(0, min(TK, k_hi - t0)) * RB);
+            const __amdgpu_buffer_rsrc_t rk = raw_rsrc(kb + (size_t)t0 * RB, bytes);
+            const __amdgpu_buffer_rsrc_t rv = raw_rsrc(vb + (size_t)t0 * RB, bytes);
+            lds_u8 *dk = (lds_u8 *)KV + 2 * TSTR * buf;
+            // no lane-dependent DMA: a conditional one makes the compiler's
+            // count of outstanding loads conservative, and its wait for the q
+            // loads would then wait for DMAs as well
+#pragma unroll
+            for (int c = 0; c < TILE / 1024; c++) {
+                const unsigned o = (unsigned)(1024 * c + 16 * lane);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, dk + 1024 * c, 16, o, 0, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, dk + TSTR + 1024 * c, 16, o, 0, 0, 0);
+            }
+            constexpr int B0 = TILE - Sh::REM;
+#pragma unroll
+            for (int c = 0; c < (Sh::REM + 255) / 256; c++) {
+                const unsigned o = (unsigned)(B0 + 256 * c + 4 * lane);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, dk + B0 + 256 * c, 4, o, 0, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, dk + TSTR + B0 + 256 * c, 4, o, 0, 0,
+                                                         0);
+            }
+        };
+        // the 32-key tile after t0: its second half, or the next visited
+        // 64-key tile (tiles of the plan start at multiples of 64)
+        auto next_tile = [&](int t0) -> int {
+            if ((t0 & (kDecodeKeyTile - 1)) == 0 && t0 + TK < k_hi) return t0 + TK;
+            return next_visited((t0 & ~(kDecodeKeyTile - 1)) + kDecodeKeyTile);
+        };
+        // wait until at most `later` tiles' requests are outstanding
+        auto wait_tiles = [](int later) {
+            if (later <= 0) wait_vmem_le<0>();
+            else if (later == 1) wait_vmem_le<2 * NI>();
+            else if (later == 2) wait_vmem_le<4 * NI>();
+            else wait_vmem_le<6 * NI>();
+        };
+        wait_vmem_le<0>();          // nothing of an earlier segment in flight
+
         // ---- q operand of QK: row m = 8 limb + head, this lane's 8 contraction
         // elements of every block, and the accumulator inputs that turn the
         // codes c into c - 8. Byte t of the lane's code word (4 code bytes of
@@ -134,29 +196,44 @@ void decode_hilo_kernel(DecodeArgs a) {
         // is element x and hi(x) element 16 + x of the block. Odd blocks: the
         // code word g is bytes 4g..4g+3; even blocks (code bytes start 2 bytes
         // into a dword): g < 3 takes bytes 4g+2..4g+5, g = 3 bytes 0, 1, 14, 15.
+        // Either way the 8 elements are the pairs at o1 and o2 and at o1 + 16,
+        // o2 + 16, interleaved: four 8-byte loads per block.
         const int qh = n16 & 7, limb = n16 >> 3;
-        const float *qrow = a.q + ((size_t)slot * a.n_head + kvh * G + qh) * HD;
-        auto code_byte = [&](int b, int t) -> int {
-            if (b & 1) return 4 * g4 + t;
-            if (g4 < 3) return 4 * g4 + 2 + t;
-            return t < 2 ? t : 12 + t;                  // bytes 0, 1, 14, 15
-        };
-        // B element i -> element of block b: word byte (0, 2, 1, 3) of i % 4,
-        // its low nibble for i < 4 and its high nibble for i >= 4
-        auto elem = [&](int b, int i) -> int {
-            const int t = (i & 1) * 2 + ((i >> 1) & 1);
-            return (i >= 4 ? 16 : 0) + code_byte(b, t);
-        };
-        // two passes over the q elements (the second from cache): the head's
-        // max first, then the limbs
-        auto qval = [&](int b, int i) -> float {
-            return qh < G ? qrow[b * kQ4Block + elem(b, i)] : 0.0f;
-        };
+        // rows past G read head G - 1 and are zeroed
+        const float *qrow = a.q + ((size_t)slot * a.n_head + kvh * G + min(qh, G - 1)) * HD;
+        float qv[NB][8];
+#pragma unroll
+        for (int b = 0; b < NB; b++) {
+            const int o1 = (b & 1) ? 4 * g4 : (g4 < 3 ? 4 * g4 + 2 : 0);
+            const int o2 = (b & 1) ? 4 * g4 + 2 : (g4 < 3 ? 4 * g4 + 4 : 14);
+            const float *qb = qrow + b * kQ4Block;
+            const float2 l1 = *(const float2 *)(qb + o1), l2 = *(const float2 *)(qb + o2);
+            const float2 h1 = *(const float2 *)(qb + 16 + o1), h2 = *(const float2 *)(qb + 16 + o2);
+            const float e[8] = {l1.x, l2.x, l1.y, l2.y, h1.x, h2.x, h1.y, h2.y};
+#pragma unroll
+            for (int i = 0; i < 8; i++) qv[b][i] = qh < G ? e[i] : 0.0f;
+        }
+        // rq[0] is the current tile, rq[1..] the ones requested after it (a
+        // start >= k_hi: none); buf0 is rq[0]'s buffer. The first NBUF - 1
+        // requests go out unconditionally (an empty one is an all-zero tile),
+        // so the compiler's wait for the q loads above does not cover them:
+        // they fly while the q operand is built.
+        int rq[NBUF];
+        int t_next = next_visited(k_lo);
+        int buf0 = 0;
+#pragma unroll
+        for (int d = 0; d < NBUF - 1; d++) {
+            rq[d] = t_next;
+            dma_tile(d, t_next);
+            if (t_next < k_hi) t_next = next_tile(t_next);
+        }
+        rq[NBUF - 1] = k_hi;
+
         float qmax = 0.0f;
 #pragma unroll
         for (int b = 0; b < NB; b++)
 #pragma unroll
-            for (int i = 0; i < 8; i++) qmax = fmaxf(qmax, fabsf(qval(b, i)));
+            for (int i = 0; i < 8; i++) qmax = fmaxf(qmax, fabsf(qv[b][i]));
         qmax = fmaxf(qmax, __shfl_xor(qmax, 16));
         qmax = fmaxf(qmax, __shfl_xor(qmax, 32));
         int ex = 0;
@@ -177,7 +254,7 @@ void decode_hilo_kernel(DecodeArgs a) {
             float part = 0.0f;
 #pragma unroll
             for (int i = 0; i < 8; i++) {
-                const float x = ldexpf(qval(b, i), E + (i < 4 ? 4 : 0));   // low-nibble slots x16
+                const float x = ldexpf(qv[b][i], E + (i < 4 ? 4 : 0));   // low-nibble slots x16
                 const _Float16 hi = (_Float16)x;
                 const _Float16 lo = (_Float16)(x - (float)hi);
                 hv[i] = limb ? lo : hi;
@@ -223,65 +300,6 @@ void decode_hilo_kernel(DecodeArgs a) {
         int F = -64, fthr = 0;
         float pscale = 0.0f;
 
-        // first visited tile at or after j ([FA] fc_attn_tile_in_window), in
-        // the plan's 64-key tiles
-        auto next_visited = [&](int j) -> int {
-            if (j < k_hi && a.win > 0 && j >= a.sink &&
-                min(j + kDecodeKeyTile - 1, k_hi - 1) < win_first) {
-                const int jn = (win_first / kDecodeKeyTile) * kDecodeKeyTile;
-                const int stop = min(jn, k_hi);
-                skp += (unsigned)((stop - j + kDecodeKeyTile - 1) / kDecodeKeyTile);
-                return jn >= k_hi ? k_hi : jn;
-            }
-            return j;
-        };
-        // raw 32-key K and V tiles at t0 into buffer `buf`; rows past k_hi
-        // arrive as zeros. The LDS destination stays in the LDS address space
-        // (a generic pointer would have to be cast back).
-        typedef __attribute__((address_space(3))) uint8_t lds_u8;
-        auto dma_tile = [&](int buf, int t0) {
-            const unsigned bytes = (unsigned)(min(TK, k_hi - t0) * RB);
-            const __amdgpu_buffer_rsrc_t rk = raw_rsrc(kb + (size_t)t0 * RB, bytes);
-            const __amdgpu_buffer_rsrc_t rv = raw_rsrc(vb + (size_t)t0 * RB, bytes);
-            lds_u8 *dk = (lds_u8 *)KV + 2 * TILE * buf;
-#pragma unroll
-            for (int c = 0; c < NI; c++) {
-                const unsigned o = (unsigned)(1024 * c + 16 * lane);
-                if (c < NI - 1 || TILE % 1024 == 0 || o < (unsigned)TILE) {
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, dk + 1024 * c, 16, o, 0, 0, 0);
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, dk + TILE + 1024 * c, 16, o, 0, 0,
-                                                             0);
-                }
-            }
-        };
-        // the 32-key tile after t0: its second half, or the next visited
-        // 64-key tile (tiles of the plan start at multiples of 64)
-        auto next_tile = [&](int t0) -> int {
-            if ((t0 & (kDecodeKeyTile - 1)) == 0 && t0 + TK < k_hi) return t0 + TK;
-            return next_visited((t0 & ~(kDecodeKeyTile - 1)) + kDecodeKeyTile);
-        };
-        // wait until at most `later` tiles' requests are outstanding
-        auto wait_tiles = [](int later) {
-            if (later <= 0) wait_vmem_le<0>();
-            else if (later == 1) wait_vmem_le<2 * NI>();
-            else if (later == 2) wait_vmem_le<4 * NI>();
-            else wait_vmem_le<6 * NI>();
-        };
-        wait_vmem_le<0>();          // nothing of an earlier segment in flight
-        // rq[0] is the current tile, rq[1..] the ones requested after it (a
-        // start >= k_hi: none); buf0 is rq[0]'s buffer
-        int rq[NBUF];
-        int t_next = next_visited(k_lo);
-        int buf0 = 0;
-#pragma unroll
-        for (int d = 0; d < NBUF - 1; d++) {
-            rq[d] = t_next;
-            if (t_next < k_hi) {
-                dma_tile(d, t_next);
-                t_next = next_tile(t_next);
-            }
-        }
-        rq[NBUF - 1] = k_hi;
         while (rq[0] < k_hi) {
             {
                 const int t0 = rq[0];
@@ -298,15 +316,15 @@ void decode_hilo_kernel(DecodeArgs a) {
                 for (int d = 1; d < NBUF; d++) later += rq[d] < k_hi ? 1 : 0;
                 wait_tiles(later);                  // this tile's K and V are in LDS
                 if ((t0 & (kDecodeKeyTile - 1)) == 0) vis++;
-                const uint8_t *Kt = KV + 2 * TILE * buf0;
-                const uint8_t *Vt = Kt + TILE;
+                const uint8_t *Kt = KV + 2 * TSTR * buf0;
+                const uint8_t *Vt = Kt + TSTR;
                 // p [head][key] and the V block scales [block][key] go to this
                 // buffer's K tile once QK has read it (the buffer is refilled
                 // only after every LDS read of this tile has completed). In
                 // arrays of their own, the compiler's LDS-DMA tracking made the
                 // first read of them wait for the next tile's DMA.
-                float *Pt = (float *)(KV + 2 * TILE * buf0);
-                uint16_t *Dt = (uint16_t *)(KV + 2 * TILE * buf0 + 8 * PS * 4);
+                float *Pt = (float *)(KV + 2 * TSTR * buf0);
+                uint16_t *Dt = (uint16_t *)(KV + 2 * TSTR * buf0 + 8 * PS * 4);
 
                 // ---- QK: two sets of 16 keys, one MFMA per (set, block) plus
                 // one for the -8 of the codes

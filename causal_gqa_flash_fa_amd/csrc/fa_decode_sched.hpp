@@ -51,20 +51,40 @@ __device__ __forceinline__ int decode_query_pos(const DecodeArgs &a, int slot) {
     else return a.pos[slot];
 }
 
+// Segments whose items and query position pass 1 keeps in registers for
+// pass 2 (64 per register): pass 2 then reads nothing from memory, which by
+// then is busy with other waves' tile loads.
+constexpr int kSchedCached = 4;
+
 // Runs wave w's share (of NW waves) of the item list: for every segment its
-// run touches, calls run_segment(seg, it_lo, it_hi, partial) with the run's
-// items [it_lo, it_hi) of that segment and the index of the partial it writes.
+// run touches, calls run_segment(seg, pos, it_lo, it_hi, partial) with the
+// segment's query position, the run's items [it_lo, it_hi) of that segment
+// and the index of the partial it writes.
 template <bool PG, class SegFn>
 __device__ __forceinline__ void decode_stream_k(const DecodeArgs &a, int w, int NW, int lane,
                                                 SegFn &&run_segment) {
     const int nsegs = a.n_slots * a.n_kv;
-    // ---- pass 1: total number of items
-    int total = 0;
-    for (int base = 0; base < nsegs; base += 64) {
-        const int s = base + lane;
+    // items and query position of segment s (this lane's of a 64-segment chunk)
+    auto seg_info = [&](int s, int &pos) -> int {
+        pos = s < nsegs ? decode_query_pos<PG>(a, s / a.n_kv) : -1;
         int sl;
-        const int it = s < nsegs ? slot_items(decode_query_pos<PG>(a, s / a.n_kv), a, &sl) : 0;
-        total += __builtin_amdgcn_readfirstlane(wave_sum_i(it));
+        return s < nsegs ? slot_items(pos, a, &sl) : 0;
+    };
+    // ---- pass 1: total number of items
+    int c_it[kSchedCached], c_pos[kSchedCached];
+    int total = 0;
+#pragma unroll
+    for (int c = 0; c < kSchedCached; c++) {
+        c_it[c] = 0;
+        c_pos[c] = -1;
+        if (64 * c < nsegs) {
+            c_it[c] = seg_info(64 * c + lane, c_pos[c]);
+            total += __builtin_amdgcn_readfirstlane(wave_sum_i(c_it[c]));
+        }
+    }
+    for (int base = 64 * kSchedCached; base < nsegs; base += 64) {
+        int pos;
+        total += __builtin_amdgcn_readfirstlane(wave_sum_i(seg_info(base + lane, pos)));
     }
     const long long lo = (long long)w * total / NW;
     const long long hi = (long long)(w + 1) * total / NW;
@@ -73,10 +93,8 @@ __device__ __forceinline__ void decode_stream_k(const DecodeArgs &a, int w, int 
 
     // ---- pass 2: segment prefix sums, the partial table, and this wave's run
     int f_carry = 0, p_carry = 0;
-    for (int base = 0; base < nsegs; base += 64) {
+    auto chunk = [&](int base, int it, int pos) {
         const int s = base + lane;
-        int sl;
-        const int it = s < nsegs ? slot_items(decode_query_pos<PG>(a, s / a.n_kv), a, &sl) : 0;
         const int incl = wave_incl_scan(it, lane);
         const int F = f_carry + incl - it;
         const int nw = it > 0 ? owner(F + it - 1) - owner(F) + 1 : 0;
@@ -94,12 +112,21 @@ __device__ __forceinline__ void decode_stream_k(const DecodeArgs &a, int w, int 
             const int Fs = __builtin_amdgcn_readfirstlane(__shfl(F, b));
             const int its = __builtin_amdgcn_readfirstlane(__shfl(it, b));
             const int Ps = __builtin_amdgcn_readfirstlane(__shfl(P, b));
+            const int poss = __builtin_amdgcn_readfirstlane(__shfl(pos, b));
             const int it_lo = (int)max(lo, (long long)Fs) - Fs;
             const int it_hi = (int)min(hi, (long long)Fs + its) - Fs;
-            run_segment(base + b, it_lo, it_hi, Ps + (w - owner(Fs)));
+            run_segment(base + b, poss, it_lo, it_hi, Ps + (w - owner(Fs)));
         }
         f_carry += __builtin_amdgcn_readfirstlane(__shfl(incl, 63));
         p_carry += __builtin_amdgcn_readfirstlane(__shfl(inclw, 63));
+    };
+#pragma unroll
+    for (int c = 0; c < kSchedCached; c++)
+        if (64 * c < nsegs) chunk(64 * c, c_it[c], c_pos[c]);
+    for (int base = 64 * kSchedCached; base < nsegs; base += 64) {
+        int pos;
+        const int it = seg_info(base + lane, pos);
+        chunk(base, it, pos);
     }
 }
 
