@@ -4,12 +4,16 @@
 // [FA] fc_attn_kv_append_slots ("Multi-user decode attention (slots)"
 // section): row t of [n_slots][n_kv][hd] lands in slot t at the position held
 // in device memory, so the enqueued work does not depend on the position.
-// [FA] fc_kvq4_quant_block: per 32-element block, amax fold from 0,
-// d = amax / -8 (negative scale), id = 1/d or 0, code = clamp(rint(x*id)+8,
-// 0, 15) (convert, then +8, then clamp), binary16 d in bytes 0-1 (LE), byte
-// 2+j = code_j | code_{j+16} << 4. Every step is an IEEE fp32 operation
-// (correctly rounded divide, v_rndne for rint, v_cvt_f16_f32 round-to-even),
-// so the bytes equal any other exact implementation of the same steps.
+// The Q4_0 block format is an interchange format, so its definition fixes
+// both the bytes and the order of the steps that produce them ([FA] "4-bit KV
+// cache (Q4_0 blocks)" section, fc_kvq4_quant_block): per 32-element block,
+// amax is the max of |x| (from 0); the scale d = amax / -8 (negative); with
+// id = 1/d (0 for d = 0) each element's code is rint(x id) + 8 held to
+// [0, 15]; bytes 0-1 are binary16(d) little-endian and byte 2 + j packs
+// code_j | code_{j+16} << 4. A value decodes as (code - 8) d. Every step is an
+// IEEE fp32 operation (correctly rounded divide, v_rndne for rint,
+// v_cvt_f16_f32 round-to-even), so the bytes equal those of any other exact
+// implementation of the definition.
 //
 // One thread owns one 32-element block here (no cross-lane fold), so both
 // launches are plain streaming kernels: each thread reads 128 B of input and

@@ -91,7 +91,9 @@ static int q4_code(float x, float id)
     return (int)r + 8;
 }
 
-/* One 32-element block. Steps, all in fp32:
+/* One 32-element block of the Q4_0 format, whose definition fixes the
+ * bytes and the order of the steps ([FA] "4-bit KV cache (Q4_0 blocks)"
+ * section, fc_kvq4_quant_block). Steps, all in fp32:
  *  1. amax: fmaxf fold of |x_j| starting from 0
  *  2. d = amax / -8  (the stored scale is negative)
  *  3. id = 1/d, or 0 when d is zero

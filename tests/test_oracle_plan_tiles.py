@@ -7,7 +7,10 @@ fc_attn_tile_in_window comment and the file header (tiles meeting neither
 the sink nor the recent window are skipped before any staging; tiles past
 the causal bound are never walked).
 
-The plan is pinned by hand-worked examples; the tile counts by brute force
+The plan is pinned by hand-worked examples and by a search-based
+characterisation of what it computes (fewest kps-key pieces up to cap,
+shortest tile-multiple split length that covers L with them, non-empty
+splits); the tile counts by brute force
 over every (query, key) pair on small shapes, and by the window workload's
 closed-form pair count.
 """
@@ -40,6 +43,31 @@ def test_plan_invariants():
             assert 1 <= n <= cap and sl % tile == 0 and sl > 0
             assert 1 <= live <= n
             assert (live - 1) * sl < L <= live * sl      # live splits cover [0, L) exactly
+
+
+def plan_by_search(L, kps, cap, tile):
+    """The plan derived from what it is for, by search and enumeration rather
+    than by its ceil-division formulas: n is the fewest kps-key pieces that
+    hold L keys, at most cap; the split length is the shortest multiple of the
+    tile with which n splits hold L keys; the live splits are those of the n
+    that hold at least one key."""
+    n = 1
+    while n * kps < L and n < cap:
+        n += 1
+    sl = tile
+    while n * sl < L:
+        sl += tile
+    live = sum(1 for i in range(n) if i * sl < L)
+    return live, n, sl
+
+
+def test_plan_matches_its_characterisation():
+    Ls = list(range(1, 700)) + [1000, 4095, 4096, 4097, 10000, 32767, 32768, 32769, 40000]
+    for L in Ls:
+        for kps, cap, tile in [(64, 512, 64), (16, 64, 16), (256, 8, 64), (1, 1000, 32),
+                               (64, 3, 64), (100, 7, 16)]:
+            assert oracle.decode_plan(L, kps, cap, tile) == plan_by_search(L, kps, cap, tile), \
+                (L, kps, cap, tile)
 
 
 def test_plan_rejects_bad_arguments():
