@@ -13,11 +13,14 @@ carries a `roofline` object for the prefill kernel and a `roofline_decode`
 object for the 64-slot Q4_0 decode (the metric's second half: KV-read GB/s
 against HBM and against the fp32 compute ceiling), both timed with HIP events
 on the launch stream; the other workloads as `legs` (the tiny and 2k
-prefills, the 32k sliding-window prefill, both Q4_0 workloads with the fp16
-sink/window shadow, the 64-slot decode over an fp32 cache, a varlen batch
+prefills, the 32k sliding-window prefill, the 64-slot decode on the opt-in fp16 hi/lo
+lane, both Q4_0 workloads with the fp16 sink/window shadow, the 64-slot
+decode over an fp32 cache, a varlen batch
 over a paged fp32 cache, the 64-slot decode as 64 one-token requests over a
 paged fp32 cache, and the LSE merge of two attention states); and the CPU
-oracle timed on the host cores as `cpu_baseline`.
+oracle timed on the host cores as `cpu_baseline`. Decode legs evict the
+cache between timed calls by reading a 512 MB buffer (--evict write zero-fills
+it instead, whose dirty lines are then written back inside the timed call).
 """
 from __future__ import annotations
 
