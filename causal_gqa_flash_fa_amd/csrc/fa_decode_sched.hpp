@@ -51,15 +51,22 @@ __device__ __forceinline__ int decode_query_pos(const DecodeArgs &a, int slot) {
     else return a.pos[slot];
 }
 
-// Segments whose items and query position pass 1 keeps in registers for
-// pass 2 (64 per register): pass 2 then reads nothing from memory, which by
-// then is busy with other waves' tile loads.
+// Segments whose items, query position and item-list offset the first pass
+// keeps in registers (64 per register): the second pass then reads nothing
+// from memory, which by then is busy with other waves' tile loads.
 constexpr int kSchedCached = 4;
 
 // Runs wave w's share (of NW waves) of the item list: for every segment its
 // run touches, calls run_segment(seg, pos, it_lo, it_hi, partial) with the
 // segment's query position, the run's items [it_lo, it_hi) of that segment
 // and the index of the partial it writes.
+//
+// Partial numbering: along the item list, the (wave, segment) pairs that
+// touch advance monotonically in both, so the pair (w, s) gets number s + w.
+// The numbers are distinct and below nsegs + NW, and the partials of segment
+// s are the consecutive numbers s + owner(first item) .. s + owner(last item),
+// which is what the partial table records (so no wave but wave 0, which
+// writes the table, needs the owner division).
 template <bool PG, class SegFn>
 __device__ __forceinline__ void decode_stream_k(const DecodeArgs &a, int w, int NW, int lane,
                                                 SegFn &&run_segment) {
@@ -70,18 +77,23 @@ __device__ __forceinline__ void decode_stream_k(const DecodeArgs &a, int w, int 
         int sl;
         return s < nsegs ? slot_items(pos, a, &sl) : 0;
     };
-    // ---- pass 1: total number of items
-    int c_it[kSchedCached], c_pos[kSchedCached];
+    // ---- pass 1: items per segment, each segment's offset F in the item
+    // list (an exclusive prefix sum), and the total
+    int c_it[kSchedCached], c_pos[kSchedCached], c_F[kSchedCached];
     int total = 0;
 #pragma unroll
     for (int c = 0; c < kSchedCached; c++) {
         c_it[c] = 0;
         c_pos[c] = -1;
+        c_F[c] = 0;
         if (64 * c < nsegs) {
             c_it[c] = seg_info(64 * c + lane, c_pos[c]);
-            total += __builtin_amdgcn_readfirstlane(wave_sum_i(c_it[c]));
+            const int incl = wave_incl_scan(c_it[c], lane);
+            c_F[c] = total + incl - c_it[c];
+            total += __builtin_amdgcn_readfirstlane(__shfl(incl, 63));
         }
     }
+    const int cached_total = total;
     for (int base = 64 * kSchedCached; base < nsegs; base += 64) {
         int pos;
         total += __builtin_amdgcn_readfirstlane(wave_sum_i(seg_info(base + lane, pos)));
@@ -91,18 +103,13 @@ __device__ __forceinline__ void decode_stream_k(const DecodeArgs &a, int w, int 
     // wave owning item f: the last wave whose run starts at or before f
     auto owner = [&](long long f) -> int { return (int)(((f + 1) * NW - 1) / total); };
 
-    // ---- pass 2: segment prefix sums, the partial table, and this wave's run
-    int f_carry = 0, p_carry = 0;
-    auto chunk = [&](int base, int it, int pos) {
+    // ---- pass 2: the partial table (wave 0) and this wave's run
+    auto chunk = [&](int base, int it, int pos, int F) {
         const int s = base + lane;
-        const int incl = wave_incl_scan(it, lane);
-        const int F = f_carry + incl - it;
-        const int nw = it > 0 ? owner(F + it - 1) - owner(F) + 1 : 0;
-        const int inclw = wave_incl_scan(nw, lane);
-        const int P = p_carry + inclw - nw;
         if (w == 0 && s < nsegs) {
-            a.seg_table[2 * s] = P;
-            a.seg_table[2 * s + 1] = nw;
+            const int w0 = it > 0 ? owner(F) : 0;
+            a.seg_table[2 * s] = s + w0;
+            a.seg_table[2 * s + 1] = it > 0 ? owner(F + it - 1) - w0 + 1 : 0;
         }
         unsigned long long hit = __ballot(it > 0 && F < hi && F + it > lo);
         while (hit) {
@@ -111,22 +118,22 @@ __device__ __forceinline__ void decode_stream_k(const DecodeArgs &a, int w, int 
             // lane b's values, as wave-uniform (scalar) values
             const int Fs = __builtin_amdgcn_readfirstlane(__shfl(F, b));
             const int its = __builtin_amdgcn_readfirstlane(__shfl(it, b));
-            const int Ps = __builtin_amdgcn_readfirstlane(__shfl(P, b));
             const int poss = __builtin_amdgcn_readfirstlane(__shfl(pos, b));
             const int it_lo = (int)max(lo, (long long)Fs) - Fs;
             const int it_hi = (int)min(hi, (long long)Fs + its) - Fs;
-            run_segment(base + b, poss, it_lo, it_hi, Ps + (w - owner(Fs)));
+            run_segment(base + b, poss, it_lo, it_hi, base + b + w);
         }
-        f_carry += __builtin_amdgcn_readfirstlane(__shfl(incl, 63));
-        p_carry += __builtin_amdgcn_readfirstlane(__shfl(inclw, 63));
     };
 #pragma unroll
     for (int c = 0; c < kSchedCached; c++)
-        if (64 * c < nsegs) chunk(64 * c, c_it[c], c_pos[c]);
+        if (64 * c < nsegs) chunk(64 * c, c_it[c], c_pos[c], c_F[c]);
+    int f_carry = cached_total;
     for (int base = 64 * kSchedCached; base < nsegs; base += 64) {
         int pos;
         const int it = seg_info(base + lane, pos);
-        chunk(base, it, pos);
+        const int incl = wave_incl_scan(it, lane);
+        chunk(base, it, pos, f_carry + incl - it);
+        f_carry += __builtin_amdgcn_readfirstlane(__shfl(incl, 63));
     }
 }
 
