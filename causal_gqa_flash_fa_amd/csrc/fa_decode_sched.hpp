@@ -98,10 +98,30 @@ __device__ __forceinline__ void decode_stream_k(const DecodeArgs &a, int w, int 
         int pos;
         total += __builtin_amdgcn_readfirstlane(wave_sum_i(seg_info(base + lane, pos)));
     }
-    const long long lo = (long long)w * total / NW;
-    const long long hi = (long long)(w + 1) * total / NW;
-    // wave owning item f: the last wave whose run starts at or before f
-    auto owner = [&](long long f) -> int { return (int)(((f + 1) * NW - 1) / total); };
+    // Run boundaries. With two waves per SIMD (NW = 2 kDecodeSimds), the
+    // waves of the first kDecodeSimds work-groups are dispatched first, one
+    // per SIMD, and each shares its SIMD with one of the later ones. The
+    // issue arbiter favours the older wave, so with equal runs the later
+    // waves finished ~10% later and then ran alone with nothing to hide
+    // their latencies. Runs are therefore weighted kDecodeWeightFirst :
+    // kDecodeWeightSecond in that case (equal otherwise): wave w's run is
+    // [total cum(w) / Wt, total cum(w + 1) / Wt).
+    const bool paired = NW == 2 * kDecodeSimds;
+    const int wa = paired ? kDecodeWeightFirst : 1, wb = paired ? kDecodeWeightSecond : 1;
+    const int H = paired ? kDecodeSimds : NW;
+    const long long Wt = (long long)wa * H + (long long)wb * (NW - H);
+    auto cum = [&](int v) -> long long {
+        return v <= H ? (long long)wa * v : (long long)wa * H + (long long)wb * (v - H);
+    };
+    const long long lo = total * cum(w) / Wt;
+    const long long hi = total * cum(w + 1) / Wt;
+    // wave owning item f: the last wave whose run starts at or before f, i.e.
+    // the largest v with cum(v) <= ((f + 1) Wt - 1) / total
+    auto owner = [&](long long f) -> int {
+        const long long c = ((f + 1) * Wt - 1) / total;
+        const long long v = c < (long long)wa * H ? c / wa : H + (c - (long long)wa * H) / wb;
+        return (int)min(v, (long long)NW - 1);
+    };
 
     // ---- pass 2: the partial table (wave 0) and this wave's run
     auto chunk = [&](int base, int it, int pos, int F) {

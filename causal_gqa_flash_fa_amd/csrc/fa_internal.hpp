@@ -86,6 +86,11 @@ constexpr int kDecodeMaxWavesF32 = 1024;
 // then stay in VGPRs; at one wave per SIMD the compiler moved them through
 // AGPRs every tile).
 constexpr int kDecodeMaxWavesHilo = 2048;
+// SIMDs of a 256-CU MI355X, and the run weights of the first- and
+// second-dispatched wave of a SIMD when a decode grid holds two per SIMD.
+constexpr int kDecodeSimds = 1024;
+constexpr int kDecodeWeightFirst = 9;
+constexpr int kDecodeWeightSecond = 7;
 
 // Requests of one paged prefill launch (their table sits in LDS).
 constexpr int kPagedMaxReqs = 1024;
