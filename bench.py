@@ -100,6 +100,30 @@ def _events(torch, n):
             for _ in range(n)]
 
 
+# Legs warm up for at least this much wall time (the headline keeps exactly
+# its W steps): the shader clock ramps up under sustained load, and the 2k
+# prefill (a 0.3 ms kernel) ran ~12% slower after 3 warm-up steps than after
+# 300, while the 4 ms headline kernel times the same after 3 or 40.
+LEG_WARM_MS = 150.0
+
+
+def warm(torch, step, warmup: int, min_ms: float = 0.0) -> int:
+    """Runs `warmup` untimed steps, then more until `min_ms` of wall time has
+    passed with the GPU kept busy; returns the number of steps run."""
+    n = 0
+    t0 = time.perf_counter()
+    while n < warmup:
+        step()
+        n += 1
+    torch.cuda.synchronize()
+    while (time.perf_counter() - t0) * 1e3 < min_ms:
+        for _ in range(8):
+            step()
+        n += 8
+        torch.cuda.synchronize()
+    return n
+
+
 class CacheEvict:
     """Evicts a leg's data from L2 and the 256 MB MALL between timed calls by
     READING a 512 MB buffer. A write-based flush (zero-filling the buffer)
@@ -129,7 +153,8 @@ def spread(kms, key: str) -> dict:
             key + "_rel_std": float(np.std(a) / np.mean(a))}
 
 
-def prefill_leg(fa, torch, w, steps: int, warmup: int, graph: bool = False) -> dict:
+def prefill_leg(fa, torch, w, steps: int, warmup: int, graph: bool = False,
+                warm_ms: float = LEG_WARM_MS) -> dict:
     """fa_prefill of one workload over a cache filled by fa_kv_append. The
     append is timed on its own (HIP events, `append_ms`) and is not part of
     the step. Kernel time: HIP events around each eager fa_prefill. Step
@@ -170,9 +195,7 @@ def prefill_leg(fa, torch, w, steps: int, warmup: int, graph: bool = False) -> d
         if i is not None:
             ev[i][1].record()
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_steps = warm(torch, step, warmup, warm_ms)
     t0 = time.perf_counter()
     for i in range(steps):
         step(i)
@@ -201,7 +224,7 @@ def prefill_leg(fa, torch, w, steps: int, warmup: int, graph: bool = False) -> d
         "n": w.n, "n_head": w.n_head, "n_kv_head": w.n_kv_head, "head_dim": w.head_dim,
         "attn_sink": w.attn_sink, "attn_win": w.attn_win,
         "shadow_sink": w.shadow_sink, "shadow_win": w.shadow_win,
-        "step": "fa_prefill", "append_ms": append_ms,
+        "step": "fa_prefill", "append_ms": append_ms, "warmup_steps": warm_steps,
         "launch": "hip_graph" if graph else "eager", "ms_per_step_eager": eager_ms,
         "flops": flops, "ms_per_step": step_ms, "tflops_step": flops / step_ms / 1e9,
         "prefill_kernel_ms": kern_ms, "prefill_kernel_ms_min": float(np.min(kms)),
@@ -259,9 +282,7 @@ def paged_leg(fa, torch, w, steps: int, warmup: int) -> dict:
         if i is not None:
             ev[i][1].record()
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_steps = warm(torch, step, warmup, LEG_WARM_MS)
     t0 = time.perf_counter()
     for i in range(steps):
         step(i)
@@ -273,6 +294,7 @@ def paged_leg(fa, torch, w, steps: int, warmup: int) -> dict:
     kern_ms = float(np.mean(kms))
     return {
         "workload": w.name, "kind": "paged", "kv": "f32", "tokens": T, "requests": len(reqs),
+        "warmup_steps": warm_steps,
         "decode_requests": sum(1 for _, n in reqs if n == 1), "block_size": bs,
         "n_head": w.n_head, "n_kv_head": w.n_kv_head, "head_dim": w.head_dim,
         "flops": flops, "ms_per_step": step_ms, "tflops_step": flops / step_ms / 1e9,
@@ -317,9 +339,8 @@ def paged_decode_leg(fa, torch, w, steps: int, warmup: int) -> dict:
         if i is not None:
             ev[i][1].record()
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
+    # warm-up calls evict too, so that they match the timed ones
+    warm_steps = warm(torch, lambda: (flush(), step()), warmup, LEG_WARM_MS)
     for i in range(steps):
         flush()
         step(i)
@@ -330,6 +351,7 @@ def paged_decode_leg(fa, torch, w, steps: int, warmup: int) -> dict:
     nbytes = kv_bytes + 2 * w.n_slots * w.n_head * w.head_dim * 4
     gbs = nbytes / ms / 1e6
     return {"workload": w.name, "kind": "paged_decode", "kv": "f32", "requests": w.n_slots,
+            "warmup_steps": warm_steps, "evict": CacheEvict.mode,
             "block_size": bs, "num_blocks": num_blocks, "ctx_sum": int(ctx.sum()),
             "bytes": nbytes, "decode_ms": ms, "decode_ms_min": float(np.min(kms)),
             **spread(kms, "decode_ms"), "gbs": gbs, "frac_hbm_peak": gbs / PEAK_HBM_GBS}
@@ -349,18 +371,24 @@ def merge_leg(fa, torch, steps: int, warmup: int, T: int = 8192, H: int = 16,
     out = torch.empty_like(po)
     out_lse = torch.empty_like(pl)
     ev = _events(torch, steps)
-    for i in range(-warmup, steps):
-        if i >= 0:
+
+    def step(i=None):
+        if i is not None:
             ev[i][0].record()
         fa.fa_merge_attn_states(out, out_lse, po, pl, so, sl, T, H, D)
-        if i >= 0:
+        if i is not None:
             ev[i][1].record()
+
+    warm_steps = warm(torch, step, warmup, LEG_WARM_MS)
+    for i in range(steps):
+        step(i)
     torch.cuda.synchronize()
     kms = [a.elapsed_time(b) for a, b in ev]
     nbytes = 3 * T * H * D * 4 + 3 * T * H * 4
     ms = float(np.mean(kms))
     rec = measured_traffic("merge", "merge-attn-states")
     return {"workload": f"merge-attn-states-{T}x{H}x{D}", "kind": "merge", "bytes": nbytes,
+            "warmup_steps": warm_steps,
             "kernel_ms": ms, "kernel_ms_min": float(np.min(kms)), **spread(kms, "kernel_ms"),
             "gbs": nbytes / ms / 1e6, "frac_hbm_peak": nbytes / ms / 1e6 / PEAK_HBM_GBS,
             "traffic_bytes": round(rec["traffic_bytes"]) if rec else None}
@@ -396,9 +424,8 @@ def decode_leg(fa, torch, w, steps: int, warmup: int, lane: str = "fp32") -> dic
         if i is not None:
             ev[i][1].record()
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
+    # warm-up calls evict too, so that they match the timed ones
+    warm_steps = warm(torch, lambda: (flush(), step()), warmup, LEG_WARM_MS)
     for i in range(steps):
         flush()                # evict the KV cache from L2 / MALL between reps (not timed)
         step(i)
@@ -415,7 +442,8 @@ def decode_leg(fa, torch, w, steps: int, warmup: int, lane: str = "fp32") -> dic
         "workload": w.name + ("-hilo" if lane == "hilo" else ""), "kind": "decode",
         "lane": "fp16 MFMA, hi/lo-split operands" if lane == "hilo" else "fp32 MFMA",
         "kv": "q4_0" if w.kv_format else "f32",
-        "evict": CacheEvict.mode, "n_slots": w.n_slots, "ctx_sum": int(ctx.sum()),
+        "evict": CacheEvict.mode, "warmup_steps": warm_steps, "n_slots": w.n_slots,
+        "ctx_sum": int(ctx.sum()),
         "ctx_min": int(ctx.min()),
         "ctx_max": int(ctx.max()), "launch_splits": fa.fa_decode_plan(hint)[0],
         "shadow_sink": w.shadow_sink, "shadow_win": w.shadow_win,
@@ -549,7 +577,8 @@ def main() -> int:
     head = workloads.BY_NAME["prefill-q4kv-8k"]
     print(f"[bench] {head.name}: warmup {args.warmup}, steps {args.steps}", file=sys.stderr,
           flush=True)
-    main_leg = prefill_leg(fa, torch, head, args.steps, args.warmup, graph=not args.eager)
+    main_leg = prefill_leg(fa, torch, head, args.steps, args.warmup, graph=not args.eager,
+                           warm_ms=0.0)
     torch.cuda.empty_cache()
     legs = []
     for name in [s for s in args.legs.split(",") if s]:
