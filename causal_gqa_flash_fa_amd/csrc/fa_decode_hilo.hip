@@ -578,6 +578,9 @@ void decode_hilo_kernel(DecodeArgs a) {
     };
 
     decode_stream_k<false>(a, w, NW, lane, run_segment);
+    // a segment with no tiles still issued its first (all-zero) tile DMA:
+    // nothing may be in flight into this work-group's LDS when it ends
+    wait_vmem_le<0>();
 
     if (a.stats && lane == 0) {
         atomicAdd(&a.stats[0], (unsigned long long)vis);

@@ -51,9 +51,10 @@ __device__ __forceinline__ int decode_query_pos(const DecodeArgs &a, int slot) {
     else return a.pos[slot];
 }
 
-// Segments whose items, query position and item-list offset the first pass
-// keeps in registers (64 per register): the second pass then reads nothing
-// from memory, which by then is busy with other waves' tile loads.
+// Segments whose items, query position and item-list offset the scan keeps
+// in registers (64 per register), for the partial table and for finding the
+// wave's first segment without reading memory again (by then busy with other
+// waves' tile loads).
 constexpr int kSchedCached = 4;
 
 // Runs wave w's share (of NW waves) of the item list: for every segment its
@@ -123,37 +124,81 @@ __device__ __forceinline__ void decode_stream_k(const DecodeArgs &a, int w, int 
         return (int)min(v, (long long)NW - 1);
     };
 
-    // ---- pass 2: the partial table (wave 0) and this wave's run
-    auto chunk = [&](int base, int it, int pos, int F) {
-        const int s = base + lane;
-        if (w == 0 && s < nsegs) {
-            const int w0 = it > 0 ? owner(F) : 0;
-            a.seg_table[2 * s] = s + w0;
-            a.seg_table[2 * s + 1] = it > 0 ? owner(F + it - 1) - w0 + 1 : 0;
+    // ---- the partial table (wave 0): segment s's partials are the numbers
+    // s + owner(F_s) .. s + owner(F_s + it_s - 1)
+    if (w == 0) {
+        auto table = [&](int base, int it, int F) {
+            const int s = base + lane;
+            if (s < nsegs) {
+                const int w0 = it > 0 ? owner(F) : 0;
+                a.seg_table[2 * s] = s + w0;
+                a.seg_table[2 * s + 1] = it > 0 ? owner(F + it - 1) - w0 + 1 : 0;
+            }
+        };
+#pragma unroll
+        for (int c = 0; c < kSchedCached; c++)
+            if (64 * c < nsegs) table(64 * c, c_it[c], c_F[c]);
+        int f_carry = cached_total;
+        for (int base = 64 * kSchedCached; base < nsegs; base += 64) {
+            int pos;
+            const int it = seg_info(base + lane, pos);
+            const int incl = wave_incl_scan(it, lane);
+            table(base, it, f_carry + incl - it);
+            f_carry += __builtin_amdgcn_readfirstlane(__shfl(incl, 63));
         }
-        unsigned long long hit = __ballot(it > 0 && F < hi && F + it > lo);
-        while (hit) {
-            const int b = __builtin_ctzll(hit);
-            hit &= hit - 1;
-            // lane b's values, as wave-uniform (scalar) values
-            const int Fs = __builtin_amdgcn_readfirstlane(__shfl(F, b));
-            const int its = __builtin_amdgcn_readfirstlane(__shfl(it, b));
-            const int poss = __builtin_amdgcn_readfirstlane(__shfl(pos, b));
-            const int it_lo = (int)max(lo, (long long)Fs) - Fs;
-            const int it_hi = (int)min(hi, (long long)Fs + its) - Fs;
-            run_segment(base + b, poss, it_lo, it_hi, base + b + w);
+    }
+    // ---- this wave's first segment: the first one with items past lo (its
+    // offset is then <= lo). An empty run (lo = hi, when there are fewer
+    // items than waves) lies strictly inside at most one segment, whose
+    // partial range then still counts this wave: it writes an empty partial
+    // there. From here on the wave's state is scalar.
+    const bool empty = lo >= hi;
+    int s = -1, Fs = 0, its = 0, poss = -1;
+    auto find = [&](int base, int it, int pos, int F) {
+        const unsigned long long m = __ballot(it > 0 && F + it > lo && (!empty || F < lo));
+        if (m) {
+            const int b = __builtin_ctzll(m);
+            s = base + b;
+            Fs = __builtin_amdgcn_readfirstlane(__shfl(F, b));
+            its = __builtin_amdgcn_readfirstlane(__shfl(it, b));
+            poss = __builtin_amdgcn_readfirstlane(__shfl(pos, b));
         }
     };
 #pragma unroll
     for (int c = 0; c < kSchedCached; c++)
-        if (64 * c < nsegs) chunk(64 * c, c_it[c], c_pos[c], c_F[c]);
-    int f_carry = cached_total;
-    for (int base = 64 * kSchedCached; base < nsegs; base += 64) {
-        int pos;
-        const int it = seg_info(base + lane, pos);
-        const int incl = wave_incl_scan(it, lane);
-        chunk(base, it, pos, f_carry + incl - it);
-        f_carry += __builtin_amdgcn_readfirstlane(__shfl(incl, 63));
+        if (s < 0 && 64 * c < nsegs) find(64 * c, c_it[c], c_pos[c], c_F[c]);
+    if (s < 0) {
+        int f_carry = cached_total;
+        for (int base = 64 * kSchedCached; s < 0 && base < nsegs; base += 64) {
+            int pos;
+            const int it = seg_info(base + lane, pos);
+            const int incl = wave_incl_scan(it, lane);
+            find(base, it, pos, f_carry + incl - it);
+            f_carry += __builtin_amdgcn_readfirstlane(__shfl(incl, 63));
+        }
+    }
+    if (s < 0) return;                         // an empty run on a segment boundary
+    if (empty) {
+        run_segment(s, poss, (int)lo - Fs, (int)lo - Fs, s + w);
+        return;
+    }
+
+    // ---- the run: consecutive segments from s while its items last
+    for (;;) {
+        const int it_lo = (int)max(lo, (long long)Fs) - Fs;
+        const int it_hi = (int)min(hi, (long long)Fs + its) - Fs;
+        run_segment(s, poss, it_lo, it_hi, s + w);
+        Fs += its;
+        if (Fs >= hi) break;
+        // the next segment with items starts at item Fs
+        its = 0;
+        while (++s < nsegs) {
+            poss = __builtin_amdgcn_readfirstlane(decode_query_pos<PG>(a, s / a.n_kv));
+            int sl;
+            its = slot_items(poss, a, &sl);
+            if (its > 0) break;
+        }
+        if (its == 0) break;                   // (not reached: Fs < hi <= total)
     }
 }
 
