@@ -19,25 +19,26 @@
 //     subnormal inputs exactly (checked on the GPU).
 //   * QK. S^T[key][row] for 16 keys, rows = (limb, head): limb 0 holds
 //     hi(q'), limb 1 lo(q') = q' - hi(q'), where q' = q 2^E per head (a power
-//     of two keeps |16 q'| < 2^15). One MFMA covers one 32-element Q4 block:
-//     its accumulator input is -8 * sum(q' weights) * 2^-24 per row, which
-//     turns the codes c into c - 8, and the block scale d (one per key and
-//     block) is applied to the fp32 result by one fused multiply-add per
-//     output. The two limb rows of a head are summed once per tile.
+//     of two keeps |16 q'| < 2^15). One MFMA covers one 32-element Q4 block,
+//     and the block scale d (one per key and block) is applied to its fp32
+//     result by one fused multiply-add per output. The -8 of the codes is one
+//     more MFMA per 16 keys: each row's per-block sums of q' (hi/lo limbs,
+//     scaled by 2^-6) against the keys' block scales, entering the score
+//     times -2^-15. The two limb rows of a head are summed once per tile.
 //   * PV. O[row][dim] for 16 dims of one block, rows = (limb, head) of
 //     p * d * 2^-F (d the block scale of each key, 2^-F a power of two that
 //     keeps the product within fp16), contraction over 32 keys, codes as the
 //     other operand (a byte-transposed read of the V tile in LDS). The -8 of
 //     the codes is sum_j p_j d_j per (head, block): one more MFMA per tile,
-//     p limbs against the block scales, subtracted at the end.
+//     the limbs of 128 p against the block scales, subtracted at the end.
 //   * Every product is exact in fp32 (11-bit by 11-bit significands) and
 //     sums are fp32, so the result matches the fp32-input lane to about the
 //     same rounding; the low limbs carry the bits fp16 drops.
 //
-// K and V tiles (32 keys) are DMA'd raw into LDS (buffer_load ... lds); the
-// next tile's K flies during this tile's softmax and PV, the next V during
-// the next QK. One query row per slot, so the G heads of a GQA group (padded
-// to 8) and the two limbs fill the MFMA's 16 rows.
+// K and V tiles (32 keys) are DMA'd raw into a two-deep LDS ring
+// (buffer_load ... lds): the next tile is requested as a tile starts and
+// flies during its QK, softmax and PV. One query row per slot, so the G heads
+// of a GQA group (padded to 8) and the two limbs fill the MFMA's 16 rows.
 #include "fa_device.hpp"
 #include "fa_internal.hpp"
 #include "fa_decode_sched.hpp"
@@ -94,7 +95,6 @@ struct HShape {
 constexpr int kHiloBuffers = 2;
 
 constexpr float kTau = 8.0f;            // lazy-rescale slack (log2 units)
-constexpr float kTwoM24 = 5.9604644775390625e-08f;   // 2^-24
 
 // Two waves per SIMD (256 registers each): one wave's LDS reads and waits
 // hide behind the other's VALU work. O (16 rows x head_dim) and the q limbs
@@ -147,8 +147,9 @@ void decode_hilo_kernel(DecodeArgs a) {
             return j;
         };
         // raw 32-key K and V tiles at t0 <= k_hi into buffer `buf`; rows past
-        // k_hi arrive as zeros (t0 = k_hi: an all-zero tile). The LDS destination stays in the LDS address space
-        // (a generic pointer would have to be cast back).
+        // k_hi arrive as zeros (t0 = k_hi: an all-zero tile). The LDS
+        // destination stays in the LDS address space (a generic pointer would
+        // have to be cast back).
         typedef __attribute__((address_space(3))) uint8_t lds_u8;
         auto dma_tile = [&](int buf, int t0) {
             const unsigned bytes = (unsigned)(max(0, min(TK, k_hi - t0)) * RB);
@@ -189,8 +190,8 @@ void decode_hilo_kernel(DecodeArgs a) {
         wait_vmem_le<0>();          // nothing of an earlier segment in flight
 
         // ---- q operand of QK: row m = 8 limb + head, this lane's 8 contraction
-        // elements of every block, and the accumulator inputs that turn the
-        // codes c into c - 8. Byte t of the lane's code word (4 code bytes of
+        // elements of every block, and the per-block sums that the -8
+        // correction MFMA takes. Byte t of the lane's code word (4 code bytes of
         // the block) gives B elements (lo(byte0), lo(byte2), lo(byte1),
         // lo(byte3), hi(byte0), hi(byte2), hi(byte1), hi(byte3)) where lo(x)
         // is element x and hi(x) element 16 + x of the block. Odd blocks: the
