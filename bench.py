@@ -547,7 +547,7 @@ def main() -> int:
     args = ap.parse_args()
     CacheEvict.mode = args.evict
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported",
+        print(f"bench.py: the path runs on one GPU; --gpus {args.gpus} is not supported",
               file=sys.stderr)
         return 2
 
