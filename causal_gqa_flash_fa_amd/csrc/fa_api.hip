@@ -440,6 +440,7 @@ int decode_entry(const fa_cache *cache, const float *q, const int *d_pos, int n_
     if (max_ctx_hint < 1 || max_ctx_hint > cache->max_seq) return FA_EINVAL;
     if (n_slots == 0) return FA_OK;
     if (!q || !d_pos || !out || (!use_scratch && !ws)) return FA_ENULL;
+    if (!use_scratch && (uintptr_t)ws % 16 != 0) return FA_EINVAL;
     if (!decode_items_fit(n_slots, cache->n_kv_head)) return FA_EUNSUPPORTED;
     const DecodeLayout lay = decode_layout(cache, n_slots, n_head, max_ctx_hint);
     if (use_scratch ? lay.total > (size_t)FA_DECODE_SCRATCH_BYTES : ws_bytes < lay.total)
@@ -698,7 +699,7 @@ int fa_paged_decode(const fa_paged_cache *cache, const float *q, int num_reqs, i
     if (window_left >= 0 && window_right < 0) return FA_EINVAL;
     if (num_reqs == 0) return FA_OK;
     if (!q || !out || !seq_lens || !block_table || !ws) return FA_ENULL;
-    if (((uintptr_t)q | (uintptr_t)out) % 16 != 0) return FA_EINVAL;
+    if (((uintptr_t)q | (uintptr_t)out | (uintptr_t)ws) % 16 != 0) return FA_EINVAL;
     if (!decode_items_fit(num_reqs, cache->n_kv_head)) return FA_EUNSUPPORTED;
     const int group = n_head / cache->n_kv_head;
     const DecodeLayout lay =

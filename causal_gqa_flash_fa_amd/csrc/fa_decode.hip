@@ -672,24 +672,30 @@ void decode_partial_kernel(DecodeArgs a) {
 }
 
 // out = sum_r exp2(m_r - M) acc_r / sum_r exp2(m_r - M) l_r over the
-// segment's partials in ascending order, then its fp16-shadow partials. The
-// partials are read in chunks of CH with predicated loads, every load of a
-// chunk in flight at once (a loop over the partials would wait for each
-// load in turn). A chunk is summed against the running max M including the
-// chunk's own partials; when a later chunk (or the shadow partials) raises
-// M, the sums so far are rescaled by exp2(M_old - M_new). With at most CH
-// partials this is exactly the two-pass form: one max, then the weighted
-// sums in ascending order.
+// segment's partials in ascending order, then its fp16-shadow partials.
+// One wave per (slot, head); lane e owns the V = HD/64 consecutive output
+// elements from V*e. The partials are taken in chunks of up to CH: lane u
+// loads m and l of the chunk's partial u, every lane loads its V elements of
+// each of the chunk's accumulators (one 4V-byte load per partial), and all of
+// a chunk's loads are in flight at once. The chunk max and the sum of the
+// weighted l are wave reductions; the weight exp2(m_u - M) of partial u is
+// computed by lane u and read back with readlane. When a later chunk (or a
+// shadow partial) raises M, the sums so far are rescaled by
+// exp2(M_old - M_new); with at most CH partials this is exactly the two-pass
+// form: one max, then the weighted sums.
 template <int HD, int G>
-__global__ __launch_bounds__(HD) void decode_combine_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
+    constexpr int V = HD / 64;
     constexpr int CH = 32;
+    typedef float vec __attribute__((ext_vector_type(V)));
     const int gh = blockIdx.x;              // slot * n_head + head
     const int slot = gh / a.n_head, h = gh % a.n_head;
     const int seg = slot * a.n_kv + h / G, g = h % G;
     const int P = a.seg_table[2 * seg], n = a.seg_table[2 * seg + 1];
-    const int dd = threadIdx.x;
-    float M = -INFINITY, o = 0.0f, L = 0.0f;
-    // move the reference max up to m_new, rescaling the sums so far
+    const int lane = threadIdx.x;
+    float M = -INFINITY, L = 0.0f;
+    vec o = 0.0f;
+    // move the reference max up to m_new (uniform), rescaling the sums so far
     auto rebase = [&](float m_new) {
         if (m_new > M) {
             const float cs = M == -INFINITY ? 0.0f : fast_exp2(M - m_new);
@@ -699,27 +705,29 @@ __global__ __launch_bounds__(HD) void decode_combine_kernel(DecodeArgs a) {
         }
     };
     for (int r0 = 0; r0 < n; r0 += CH) {
-        float mv[CH], lv[CH], xv[CH];
-#pragma unroll
-        for (int u = 0; u < CH; u++) {
-            const size_t pi = (size_t)(P + r0 + u) * G + g;
-            const bool ok = r0 + u < n;
-            mv[u] = ok ? a.ws_m[pi] : -INFINITY;
-            lv[u] = ok ? a.ws_l[pi] : 0.0f;
-            xv[u] = ok ? a.ws_acc[pi * HD + dd] : 0.0f;
+        const int cnt = min(CH, n - r0);
+        const size_t p0 = (size_t)(P + r0) * G + g;   // (partial r0, head g)
+        float mu = -INFINITY, lu = 0.0f;
+        if (lane < cnt) {
+            mu = a.ws_m[p0 + (size_t)lane * G];
+            lu = a.ws_l[p0 + (size_t)lane * G];
         }
-        float cm = mv[0];
+        vec x[CH];
 #pragma unroll
-        for (int u = 1; u < CH; u++) cm = fmaxf(cm, mv[u]);
-        rebase(cm);
+        for (int u = 0; u < CH; u++)
+            x[u] = u < cnt ? *(const vec *)(a.ws_acc + (p0 + (size_t)u * G) * HD + lane * V)
+                           : vec(0.0f);
+        rebase(wave_max(mu));
+        // an empty partial (m = -inf: a split whose keys all come from the
+        // fp16 shadow) weighs 0, also while M is still -inf
+        const float wu = mu == -INFINITY ? 0.0f : fast_exp2(mu - M);
+        L += wave_sum(lu * wu);
 #pragma unroll
         for (int u = 0; u < CH; u++) {
-            if (r0 + u < n) {
-                // an empty partial (m = -inf: a split whose keys all come from
-                // the fp16 shadow) weighs 0, also while M is still -inf
-                const float wgt = mv[u] == -INFINITY ? 0.0f : fast_exp2(mv[u] - M);
-                L += lv[u] * wgt;
-                o += xv[u] * wgt;
+            if (u < cnt) {
+                const float wgt = __builtin_bit_cast(
+                    float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wu), u));
+                o += x[u] * wgt;
             }
         }
     }
@@ -730,11 +738,18 @@ __global__ __launch_bounds__(HD) void decode_combine_kernel(DecodeArgs a) {
         rebase(m);
         const float wgt = fast_exp2(m - M);
         L += a.sh_l[pi] * wgt;
-        o += a.sh_acc[pi * HD + dd] * wgt;
+        o += *(const vec *)(a.sh_acc + pi * HD + lane * V) * wgt;
     }
-    a.out[(size_t)gh * HD + dd] = o / L;   // no partial (bad position): 0/0 = NaN
+    const vec r = o / L;                        // no partial (bad position): 0/0 = NaN
+    float *dst = a.out + (size_t)gh * HD + lane * V;
+    if (((uintptr_t)a.out & (sizeof(vec) - 1)) == 0) {
+        *(vec *)dst = r;
+    } else {                                    // out is only 4-byte aligned
+#pragma unroll
+        for (int i = 0; i < V; i++) dst[i] = r[i];
+    }
     // ln sum exp(scale q.k) = ln 2 * (M + log2 L): partial m are in base-2 units
-    if (a.lse && dd == 0) a.lse[(size_t)h * a.n_slots + slot] = (M + log2f(L)) * kLn2;
+    if (a.lse && lane == 0) a.lse[(size_t)h * a.n_slots + slot] = (M + log2f(L)) * kLn2;
 }
 
 template <int HD, int G, int FMT, bool PG>
@@ -743,7 +758,7 @@ hipError_t launch_one(const DecodeArgs &a, int waves, hipStream_t s) {
                        0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_combine_kernel<HD, G>), dim3(a.n_slots * a.n_head), dim3(HD), 0, s,
+    hipLaunchKernelGGL((decode_combine_kernel<HD, G>), dim3(a.n_slots * a.n_head), dim3(64), 0, s,
                        a);
     return hipGetLastError();
 }
@@ -786,7 +801,7 @@ hipError_t launch_decode_combine(int head_dim, int group, const DecodeArgs &a, h
     const dim3 grid(a.n_slots * a.n_head);
 #define FA_COMBINE(HD, G)                                                                      \
     if (head_dim == HD && group == G) {                                                        \
-        hipLaunchKernelGGL((decode_combine_kernel<HD, G>), grid, dim3(HD), 0, s, a);           \
+        hipLaunchKernelGGL((decode_combine_kernel<HD, G>), grid, dim3(64), 0, s, a);           \
         return hipGetLastError();                                                              \
     }
     FA_COMBINE(64, 1) FA_COMBINE(64, 2) FA_COMBINE(64, 4) FA_COMBINE(64, 8)

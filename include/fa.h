@@ -234,7 +234,8 @@ size_t fa_decode_workspace_bytes(const fa_cache *cache, int n_slots, int n_head,
  *           read). A slot with more keys than the hint is still computed
  *           exactly.
  *   ws, ws_bytes: device scratch of at least
- *           fa_decode_workspace_bytes(cache, n_slots, n_head, max_ctx_hint).
+ *           fa_decode_workspace_bytes(cache, n_slots, n_head, max_ctx_hint),
+ *           16-byte aligned (FA_EINVAL otherwise).
  *   tile_stats: as in fa_prefill, key tiles of the plan's tile size walked
  *           split by split.
  * n_slots == 0 enqueues nothing. Other rules as fa_prefill. The work items
@@ -390,7 +391,8 @@ size_t fa_paged_decode_workspace_bytes(int num_reqs, int n_head, int n_kv_head, 
  *   max_seq_len_hint: host upper bound on seq_lens, 1..max_blocks_per_seq *
  *       block_size ([VT] PagedAttentionArgs max_seq_len); sizes the launch.
  *       Longer requests are still computed exactly.
- *   ws, ws_bytes: at least fa_paged_decode_workspace_bytes(...).
+ *   ws, ws_bytes: at least fa_paged_decode_workspace_bytes(...), 16-byte
+ *       aligned.
  * No device metadata is read on the host. num_reqs == 0 enqueues nothing.
  * Two launches on `stream`. The 32-bit item limit of fa_decode applies to
  * num_reqs * n_kv_head. */

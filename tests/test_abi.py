@@ -153,6 +153,7 @@ def test_decode_validation():
     assert rc_decode(c, n_slots=4, hint=100, ws_bytes=need - 1) == fa.FA_EWORKSPACE
     assert rc_decode(c, n_slots=0) == fa.FA_OK
     assert rc_decode(c, ws=0) == fa.FA_ENULL
+    assert rc_decode(c, ws=FAKE + 4) == fa.FA_EINVAL             # not 16-byte aligned
     assert rc_decode(c, pos=0) == fa.FA_ENULL
 
 
@@ -229,6 +230,7 @@ def test_paged_decode_validation():
     assert rc(R=0) == fa.FA_OK
     for name in ("q", "sl", "bt", "out", "ws"):
         assert rc(**{name: 0}) == fa.FA_ENULL, name
+    assert rc(ws=FAKE + 8) == fa.FA_EINVAL                      # not 16-byte aligned
     need = fa.fa_paged_decode_workspace_bytes(3, 4, 2, 128, 50)
     assert need > 0 and rc(ws_bytes=need - 1) == fa.FA_EWORKSPACE
     assert fa.fa_paged_decode_workspace_bytes(3, 4, 2, 128, 0) == 0
