@@ -663,7 +663,7 @@ void decode_partial_kernel(DecodeArgs a) {
         }
     };
 
-    decode_stream_k<PG>(a, w, NW, lane, run_segment);
+    decode_stream_k<PG, kDecodeWeightFirst, kDecodeWeightSecond>(a, w, NW, lane, run_segment);
 
     if (a.stats && lane == 0) {
         atomicAdd(&a.stats[0], (unsigned long long)vis);

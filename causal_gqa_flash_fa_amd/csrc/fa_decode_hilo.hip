@@ -578,7 +578,8 @@ void decode_hilo_kernel(DecodeArgs a) {
         }
     };
 
-    decode_stream_k<false>(a, w, NW, lane, run_segment);
+    decode_stream_k<false, kDecodeWeightFirstHilo, kDecodeWeightSecondHilo>(a, w, NW, lane,
+                                                                            run_segment);
     // a segment with no tiles still issued its first (all-zero) tile DMA:
     // nothing may be in flight into this work-group's LDS when it ends
     wait_vmem_le<0>();

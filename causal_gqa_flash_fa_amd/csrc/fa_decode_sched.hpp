@@ -68,7 +68,7 @@ constexpr int kSchedCached = 4;
 // s are the consecutive numbers s + owner(first item) .. s + owner(last item),
 // which is what the partial table records (so no wave but wave 0, which
 // writes the table, needs the owner division).
-template <bool PG, class SegFn>
+template <bool PG, int WA, int WB, class SegFn>
 __device__ __forceinline__ void decode_stream_k(const DecodeArgs &a, int w, int NW, int lane,
                                                 SegFn &&run_segment) {
     const int nsegs = a.n_slots * a.n_kv;
@@ -104,11 +104,10 @@ __device__ __forceinline__ void decode_stream_k(const DecodeArgs &a, int w, int 
     // per SIMD, and each shares its SIMD with one of the later ones. The
     // issue arbiter favours the older wave, so with equal runs the later
     // waves finished ~10% later and then ran alone with nothing to hide
-    // their latencies. Runs are therefore weighted kDecodeWeightFirst :
-    // kDecodeWeightSecond in that case (equal otherwise): wave w's run is
-    // [total cum(w) / Wt, total cum(w + 1) / Wt).
+    // their latencies. Runs are therefore weighted WA : WB in that case
+    // (equal otherwise): wave w's run is [total cum(w) / Wt, total cum(w + 1) / Wt).
     const bool paired = NW == 2 * kDecodeSimds;
-    const int wa = paired ? kDecodeWeightFirst : 1, wb = paired ? kDecodeWeightSecond : 1;
+    const int wa = paired ? WA : 1, wb = paired ? WB : 1;
     const int H = paired ? kDecodeSimds : NW;
     const long long Wt = (long long)wa * H + (long long)wb * (NW - H);
     auto cum = [&](int v) -> long long {

@@ -87,10 +87,15 @@ constexpr int kDecodeMaxWavesF32 = 1024;
 // AGPRs every tile).
 constexpr int kDecodeMaxWavesHilo = 2048;
 // SIMDs of a 256-CU MI355X, and the run weights of the first- and
-// second-dispatched wave of a SIMD when a decode grid holds two per SIMD.
+// second-dispatched wave of a SIMD when a decode grid holds two per SIMD:
+// for the fp32-MFMA Q4_0 tiles (bound by instruction issue, where the
+// arbiter's preference for the older wave weighs most) and for the fp16
+// hi/lo tiles. Set by timing the 64-slot decode over a sweep of ratios.
 constexpr int kDecodeSimds = 1024;
-constexpr int kDecodeWeightFirst = 9;
-constexpr int kDecodeWeightSecond = 7;
+constexpr int kDecodeWeightFirst = 5;
+constexpr int kDecodeWeightSecond = 3;
+constexpr int kDecodeWeightFirstHilo = 3;
+constexpr int kDecodeWeightSecondHilo = 2;
 
 // Requests of one paged prefill launch (their table sits in LDS).
 constexpr int kPagedMaxReqs = 1024;

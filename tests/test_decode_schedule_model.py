@@ -3,8 +3,9 @@ checked against the properties the kernels and the combine rely on.
 
 The schedule: the items (splits) of all (slot, kv head) segments form one
 list; wave w of NW takes the run [total cum(w) / Wt, total cum(w+1) / Wt),
-where cum weights the first kDecodeSimds waves kDecodeWeightFirst and the rest
-kDecodeWeightSecond when NW = 2 kDecodeSimds (else all 1); the wave that
+where cum weights the first kDecodeSimds waves A and the rest B when
+NW = 2 kDecodeSimds (else all 1), (A, B) being each lane's pair of run
+weights (kDecodeWeightFirst/Second, kDecodeWeightFirstHilo/SecondHilo); the wave that
 owns item f is recovered by one division (owner); the pair (wave w, segment s)
 writes partial number s + w; the partial table gives segment s the numbers
 s + owner(F_s) .. s + owner(F_s + it_s - 1); a wave walks its segments from
@@ -35,12 +36,14 @@ CSRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
 def constants():
     text = open(os.path.join(CSRC, "fa_internal.hpp")).read()
     get = lambda n: int(re.search(rf"constexpr int {n} = (\d+);", text).group(1))
-    return get("kDecodeSimds"), get("kDecodeWeightFirst"), get("kDecodeWeightSecond")
+    return get("kDecodeSimds"), [(get("kDecodeWeightFirst"), get("kDecodeWeightSecond")),
+                                 (get("kDecodeWeightFirstHilo"), get("kDecodeWeightSecondHilo"))]
 
 
-def schedule(its, NW):
-    """(partial table, writes) of the model for per-segment item counts."""
-    S, A, B = constants()
+def schedule(its, NW, A, B):
+    """(partial table, writes) of the model for per-segment item counts,
+    with run weights A : B for a paired grid."""
+    S, _ = constants()
     nsegs, total = len(its), sum(its)
     paired = NW == 2 * S
     wa, wb, H = (A, B, S) if paired else (1, 1, NW)
@@ -84,7 +87,12 @@ def schedule(its, NW):
 
 
 def check(its, NW):
-    bound, owner, table, writes, total = schedule(its, NW)
+    for A, B in constants()[1]:
+        check_weights(its, NW, A, B)
+
+
+def check_weights(its, NW, A, B):
+    bound, owner, table, writes, total = schedule(its, NW, A, B)
     b = [bound(v) for v in range(NW + 1)]
     assert b[0] == 0 and b[-1] == total and all(x <= y for x, y in zip(b, b[1:]))
     for f in range(0, total, max(1, total // 500)):
@@ -108,7 +116,7 @@ def check(its, NW):
 @pytest.mark.parametrize("seed", range(6))
 def test_schedule_model_random(seed):
     rng = random.Random(seed)
-    S, _, _ = constants()
+    S, _ = constants()
     for _ in range(150):
         nsegs = rng.randint(1, 260)
         NW = rng.choice([1, 7, 96, S, 2 * S, 2 * S, 1500, 4 * S])
@@ -118,7 +126,7 @@ def test_schedule_model_random(seed):
 
 
 def test_schedule_model_workload_shapes():
-    S, _, _ = constants()
+    S, _ = constants()
     # the 64-slot decode's item counts: one 64-key split per item, 2 kv heads
     rng = random.Random(20261202)
     ctx = [rng.randint(4096, 32768) for _ in range(64)]
