@@ -8,7 +8,6 @@ namespace fa {
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -114,11 +113,11 @@ __device__ __forceinline__ void dequant_word(uint32_t w, const BlockScale &sc, c
 }
 
 // MFMA wrappers (fp32 inputs, fp32 accumulate).
-//   32x32x2: A[m][k] from lane (m = lane&31, k = lane>>5), B[k][n] from lane
-//   (k = lane>>5, n = lane&31); D[m][n] in lane (n = lane&31), register r
-//   holding m = 8*(r/4) + 4*(lane>>5) + r%4.
-__device__ __forceinline__ f32x16 mfma32(float a, float b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+//   16x16x4: A[m][k] from lane (m = lane&15, k = lane>>4), B[k][n] from lane
+//   (k = lane>>4, n = lane&15); D[m][n] in lane (n = lane&15), register r
+//   holding m = 4*(lane>>4) + r.
+__device__ __forceinline__ f32x4 mfma16(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 //   4x4x1, 16 blocks: lane 4*blk+i gives A_blk[i], lane 4*blk+j gives
 //   B_blk[j]; D_blk[i][j] lands in lane 4*blk+j, register i.
@@ -142,6 +141,13 @@ __device__ __forceinline__ float half_swap_max(float x) {
     const uint32_t u = __builtin_bit_cast(uint32_t, x);
     const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
     return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+
+// max(x[l], x[l ^ 16]) for every lane l: ds_swizzle in bitmask mode (within
+// each 32-lane half, lane j reads lane j ^ 16), no LDS access.
+__device__ __forceinline__ float row16_swap_max(float x) {
+    const int y = __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), (0x10 << 10) | 0x1f);
+    return fmaxf(x, __builtin_bit_cast(float, y));
 }
 
 __device__ __forceinline__ float wave_sum(float x) {

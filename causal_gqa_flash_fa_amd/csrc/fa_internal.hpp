@@ -60,9 +60,12 @@ struct AppendArgs {
     ShadowArgs sh;                // Q4_0 only: mirror rows into the fp16 shadow
 };
 
-// Geometry of the prefill work-group: 4 waves of 32 (position, head) rows.
-constexpr int kPrefillWaves = 4;
-constexpr int kPrefillRowsPerWave = 32;
+// Geometry of the prefill work-group: 8 waves of 16 (position, head) rows,
+// two waves per SIMD (one work-group per CU), on 16x16x4 fp32 MFMAs; the
+// same 128 rows as 4 waves of 32 on 32x32x2 MFMAs, which timed 3.5% slower
+// on the 8k Q4_0 prefill (one wave per SIMD exposes its waits and barriers).
+constexpr int kPrefillWaves = 8;
+constexpr int kPrefillRowsPerWave = 16;
 constexpr int kPrefillKeyTile = 32;
 // Stream-K prefill grid: at most one work-group per CU of a 256-CU MI355X.
 constexpr int kPrefillMaxWorkGroups = 256;

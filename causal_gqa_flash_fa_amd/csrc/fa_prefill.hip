@@ -7,19 +7,27 @@
 // skipped before any load or barrier ([FA] fc_attn_tile_in_window).
 //
 // MI355X layout of the work:
-//   * A work-group of 4 waves owns BQ = 128/G consecutive query positions of
-//     one kv head; each wave owns 32 (position, head) rows, row R -> position
-//     q0 + R/G, head kvh*G + R%G. One 32-key K tile and V tile (fp32, padded
-//     rows) sit in LDS and are shared by all 128 rows of the group.
-//   * S^T = K Q^T with v_mfma_f32_32x32x2_f32: K rows come from LDS, Q^T is
-//     held in registers (pre-scaled by scale*log2 e). The accumulator puts
-//     one query row per lane (lane&31) and 16 keys per lane, so the softmax
-//     needs one cross-lane step (lane ^ 32) per tile.
-//   * O^T = V^T P^T, also 32x32x2: P^T is exactly the S^T accumulator after
-//     the exponentials (the key order of the contraction is chosen to match
-//     the accumulator layout), V^T comes from LDS with 16-byte reads, and O^T
-//     keeps one query row per lane, so the rescale by exp(m_old - m_new) is a
-//     per-lane multiply, done only when some row's max moved.
+//   * A work-group of 8 waves (two per SIMD, one work-group per CU) owns
+//     BQ = 128/G consecutive query positions of one kv head; each wave owns
+//     16 (position, head) rows, row R -> position q0 + R/G, head
+//     kvh*G + R%G. One 32-key K tile and V tile (fp32, padded rows) sit in
+//     LDS and are shared by all 128 rows of the group. The second wave of a
+//     SIMD issues its MFMAs while the first waits (LDS reads, the QK chain's
+//     drain, the barrier).
+//   * S^T = K Q^T with v_mfma_f32_16x16x4_f32, over the tile's two 16-key
+//     sets: K rows come from LDS, Q^T is held in registers (pre-scaled by
+//     scale*log2 e). The contraction order of each group of 4 MFMAs is
+//     chosen so that a lane's K operands are one 16-byte read. The
+//     accumulator puts one query row per 16 lanes (lane&15) and 8 keys per
+//     lane, so the softmax needs two cross-lane steps (lane ^ 16, ^ 32).
+//   * O^T = V^T P^T, also 16x16x4: P^T is exactly the S^T accumulator after
+//     the exponentials (the key order of each contraction step is chosen to
+//     match the accumulator layout). Output block b of O^T holds dims
+//     64 (b/4) + 4 m + b%4, so that a lane's V operands of one key are 16
+//     contiguous floats (four 16-byte reads, contiguous across the 16 lanes
+//     of a group). O^T keeps one query row per lane, so the rescale by
+//     exp(m_old - m_new) is a per-lane multiply, done only when some row's
+//     max moved.
 //   * Q4_0 tiles are loaded as raw 18-byte blocks and decoded exactly
 //     ((c-8)*d) while being written to the fp32 LDS tile.
 //   * Stream-K schedule: the visited key tiles of every (kv head, query
@@ -70,18 +78,19 @@ template <int HD, int G, int FMT>
 struct PrefillShape {
     static constexpr int W = kPrefillWaves;
     static constexpr int R = kPrefillRowsPerWave;
+    static_assert(R == 16, "16-row waves (16x16x4 MFMA tiles)");
+    static constexpr int NTHR = 64 * W;         // threads per work-group
     static constexpr int BK = kPrefillKeyTile;
     static constexpr int BQ = W * R / G;        // query positions per work-group
     static constexpr int PW = R / G;            // query positions per wave
     static constexpr int KS = HD + 4;           // LDS row stride (floats): conflict-free 16-B reads
-    static constexpr int NT = HD / 32;          // 32-wide output tiles of O^T
-    static constexpr int GS = NT < 4 ? NT : 4;  // output tiles fed by one V read
-    static constexpr int HH = HD / 2;           // contraction elements per lane half
+    static constexpr int NBLK = HD / 16;        // 16-dim output blocks of O^T
+    static constexpr int NBB = HD / 64;         // 16-byte V reads per lane per PV step
+    static constexpr int QPL = HD / 4;          // q operand floats per lane
     static constexpr int NB = HD / kQ4Block;    // Q4 blocks per row
     static constexpr int RB = FMT == 0 ? HD * 4 : NB * kQ4BlockBytes;
-    static constexpr int NC = BK * HD / 4 / 256;                       // fp32 float4 per thread per tensor
     static constexpr int QITEMS = 2 * BK * NB;                         // Q4 (row, block) items, K and V
-    static constexpr int IPT = (QITEMS + 255) / 256;                   // Q4 items per thread
+    static constexpr int IPT = (QITEMS + NTHR - 1) / NTHR;             // Q4 items per thread
     static constexpr int BUF = 2 * BK * KS;     // floats per buffer: K tile then V tile
     static constexpr size_t LDS_BYTES = (size_t)2 * BUF * sizeof(float);
 };
@@ -89,21 +98,7 @@ struct PrefillShape {
 // Reference-max slack of the lazy rescale (log2 units): p <= 2^kTau.
 constexpr float kTau = 8.0f;
 
-// acc *= c in place in the accumulation registers, one element at a time
-// through a single temporary VGPR: keeps the O accumulators in AGPRs (a
-// plain multiply makes the compiler carry a VGPR copy of all of O).
-__device__ __forceinline__ void scale_acc(f32x16 &acc, float c) {
-#pragma unroll
-    for (int r = 0; r < 16; r++) {
-        float x = acc[r], t;
-        asm volatile("v_accvgpr_read_b32 %1, %0\n\t"
-                     "v_mul_f32 %1, %1, %2\n\t"
-                     "v_accvgpr_write_b32 %0, %1"
-                     : "+a"(x), "=&v"(t)
-                     : "v"(c));
-        acc[r] = x;
-    }
-}
+__device__ __forceinline__ void scale_acc(f32x4 &acc, float c) { acc *= c; }
 
 // Wait for all of this wave's vector-memory operations (incl. LDS DMA).
 __device__ __forceinline__ void wait_vmem() { wait_vmem_le<0>(); }
@@ -119,8 +114,8 @@ __device__ __forceinline__ int seg_qblock(int s, int n_qblocks) {
     return (i & 1) ? (i >> 1) : n_qblocks - 1 - (i >> 1);
 }
 
-// Block-wide exclusive scan of one int per thread (256 threads); also
-// returns the total. `scratch` holds 4 ints.
+// Block-wide exclusive scan of one int per thread (a prefill work-group of
+// kPrefillWaves waves); also returns the total. `scratch` holds one int per wave.
 __device__ __forceinline__ int block_excl_scan(int x, int tid, int *scratch, int *total) {
     const int lane = tid & 63, w = tid >> 6;
     int incl = x;
@@ -134,7 +129,7 @@ __device__ __forceinline__ int block_excl_scan(int x, int tid, int *scratch, int
     __syncthreads();
     int before = 0, sum = 0;
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
+    for (int i = 0; i < kPrefillWaves; i++) {
         const int v = scratch[i];
         before += i < w ? v : 0;
         sum += v;
@@ -149,24 +144,28 @@ __device__ __forceinline__ int block_excl_scan(int x, int tid, int *scratch, int
 constexpr int kModePlain = 0, kModePaged = 1, kModeShadow = 2;
 
 template <int HD, int G, int FMT, int MODE>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * kPrefillWaves, 64 * kPrefillWaves),
+                          amdgpu_waves_per_eu(kPrefillWaves / 4, kPrefillWaves / 4)))
 void prefill_kernel(PrefillArgs a) {
     constexpr bool PG = MODE == kModePaged;
     constexpr bool SH = MODE == kModeShadow;
     static_assert(!(PG || SH) || FMT == 0, "paged and shadow modes stage fp32 tiles");
     using Sh = PrefillShape<HD, G, FMT>;
-    constexpr int BK = Sh::BK, KS = Sh::KS, NT = Sh::NT, GS = Sh::GS, HH = Sh::HH;
+    constexpr int BK = Sh::BK, KS = Sh::KS;
     constexpr int NB = Sh::NB, RB = Sh::RB;
     constexpr int ROWS = Sh::W * Sh::R;
+    constexpr int R = Sh::R, NTHR = Sh::NTHR;
     extern __shared__ __attribute__((aligned(16))) float lds[];   // 16-byte LDS accesses need 16-byte alignment
-    __shared__ int scan_scratch[4];
+    __shared__ int scan_scratch[kPrefillWaves];
     __shared__ int run_info[8];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index: uniform
-    const int hlf = lane >> 5;        // which half of the contraction / key sub-block
-    const int r32 = lane & 31;        // this lane's query row within the wave
+    // lane = (query row n16 of the wave, lane group g4): the B column and
+    // B row of a 16x16x4 MFMA
+    const int n16 = lane & 15, g4 = lane >> 4;
+    const bool row_lead = g4 == 0;    // one lane per row
 
     // ---- paged batch: the requests' geometry, in LDS behind the K/V
     // buffers. Segments are numbered request by request, then kv head, then
@@ -181,7 +180,7 @@ void prefill_kernel(PrefillArgs a) {
     if constexpr (PG) {
         const int cap = a.bt_stride * a.block_size;
         int carry = 0;
-        for (int base = 0; base < a.n_req; base += 256) {
+        for (int base = 0; base < a.n_req; base += NTHR) {
             const int r = base + tid;
             int cnt = 0;
             if (r < a.n_req) {
@@ -268,7 +267,7 @@ void prefill_kernel(PrefillArgs a) {
         return *cnt > 0 ? *cnt * kTileUnits + kSegUnits : 0;
     };
     int total = 0;
-    for (int base = 0; base < nsegs; base += 256) {
+    for (int base = 0; base < nsegs; base += NTHR) {
         const int s = base + tid;
         int cnt = 0;
         const int u = seg_units(s, &cnt);
@@ -296,7 +295,7 @@ void prefill_kernel(PrefillArgs a) {
     }
     {
         int f_carry = 0, p_carry = 0, c_carry = 0;
-        for (int base = 0; base < nsegs; base += 256) {
+        for (int base = 0; base < nsegs; base += NTHR) {
             const int s = base + tid;
             int cnt = 0;
             const int u = seg_units(s, &cnt);
@@ -350,7 +349,7 @@ void prefill_kernel(PrefillArgs a) {
     // first key (plain, paged) or list entry (shadow) of visited tile t
     auto tile_at = [&](int t) { return SH ? t * BK : st.tile(t) * BK; };
 
-    const int row_wg = w * Sh::R + r32;
+    const int row_wg = w * Sh::R + n16;
     const int p_row = q0 + row_wg / G;
     const int g = row_wg % G;
     const bool row_live = p_row <= q1;
@@ -360,28 +359,32 @@ void prefill_kernel(PrefillArgs a) {
     const uint8_t *kbase = (const uint8_t *)a.k + (size_t)kvh * a.max_seq * RB;
     const uint8_t *vbase = (const uint8_t *)a.v + (size_t)kvh * a.max_seq * RB;
 
-    // Q^T operand: this lane's row, contraction half hlf, pre-scaled. Loaded
-    // after the first tile's request, so that the two latencies overlap.
-    float qr[HH];
+    // Q^T operand: this lane's row, pre-scaled, dims 16 j + 4 g4 + t as
+    // qr[4 j + t]. Loaded after the first tile's request, so that the two
+    // latencies overlap.
+    float qr[Sh::QPL];
     auto load_q = [&]() {
         if (row_live) {
-            const f32x4 *qp = (const f32x4 *)(a.q + ((size_t)(p_row + sg.tok) * a.n_head +
-                                                     kvh * G + g) * HD + hlf * HH);
+            const float *qrow = a.q + ((size_t)(p_row + sg.tok) * a.n_head + kvh * G + g) * HD;
 #pragma unroll
-            for (int i = 0; i < HH / 4; i++) {
-                const f32x4 v = qp[i];
+            for (int i = 0; i < Sh::QPL / 4; i++) {
+                const f32x4 v = *(const f32x4 *)(qrow + 16 * i + 4 * g4);
 #pragma unroll
                 for (int t = 0; t < 4; t++) qr[4 * i + t] = v[t] * a.qscale;
             }
         } else {
 #pragma unroll
-            for (int i = 0; i < HH; i++) qr[i] = 0.0f;
+            for (int i = 0; i < Sh::QPL; i++) qr[i] = 0.0f;
         }
     };
 
-    f32x16 O[NT];
+    // O^T accumulators: NBLK 16x16 blocks; block b holds dims
+    // 64 (b >> 2) + 4 m + (b & 3) (m its row index), so that a lane's PV
+    // operands of a key are contiguous in the V row
+    constexpr int NO = Sh::NBLK;
+    f32x4 O[NO];
 #pragma unroll
-    for (int n = 0; n < NT; n++) O[n] = f32x16{};
+    for (int n = 0; n < NO; n++) O[n] = f32x4{};
     float m_run = -INFINITY, l_run = 0.0f;
     // fp16 shadow: one piece per segment (the first) starts from the row's
     // shadow-key partial, its acc read through the d permutation of the
@@ -392,17 +395,16 @@ void prefill_kernel(PrefillArgs a) {
         const size_t rf = (size_t)(p_row + sg.tok) * a.n_head + kvh * G + g;
         const float *sp = a.out + rf * HD;
 #pragma unroll
-        for (int r = 0; r < 16; r++) {
-            const int mi = 8 * (r >> 2) + 4 * hlf + (r & 3);
+        for (int r = 0; r < 4; r++) {
 #pragma unroll
-            for (int ng = 0; ng < NT / GS; ng++) {
-                const float *src = sp + ng * 32 * GS + GS * mi;
+            for (int bb = 0; bb < Sh::NBB; bb++) {
+                const f32x4 v = *(const f32x4 *)(sp + 64 * bb + 16 * g4 + 4 * r);
 #pragma unroll
-                for (int u = 0; u < GS; u++) O[ng * GS + u][r] = src[u];
+                for (int e = 0; e < 4; e++) O[4 * bb + e][r] = v[e];
             }
         }
         m_run = a.sh_m[rf];
-        l_run = hlf == 0 ? a.sh_l[rf] : 0.0f;
+        l_run = row_lead ? a.sh_l[rf] : 0.0f;
     }
 
     // ---- staging registers of a Q4_0 tile (fp32 tiles need none)
@@ -413,7 +415,8 @@ void prefill_kernel(PrefillArgs a) {
     // shadow mode: fp16 rows staged as 16-byte chunks (8 values), item idx
     // -> chunk idx % CPR of row (idx / CPR) % BK of K (or V past BK rows)
     constexpr int CPR = HD / 8;
-    constexpr int SIPT = SH ? 2 * BK * CPR / 256 : 1;
+    constexpr int SIPT = SH ? 2 * BK * CPR / NTHR : 1;
+    static_assert(!SH || (2 * BK * CPR) % NTHR == 0, "shadow staging chunks per thread");
     u32x4 sraw[SIPT];
     // Q4_0 item idx -> (row, block) of the K tile (idx < BK*NB) or V tile:
     // 8 consecutive items take 8 consecutive rows of one block, then the
@@ -506,7 +509,7 @@ void prefill_kernel(PrefillArgs a) {
             // entries past the list are zero rows (their keys are masked)
 #pragma unroll
             for (int i = 0; i < SIPT; i++) {
-                const int idx = tid + 256 * i;
+                const int idx = tid + NTHR * i;
                 const int c = idx % CPR, kk = (idx / CPR) % BK;
                 const bool isv = idx >= BK * CPR;
                 const int li = j0 + kk;
@@ -530,7 +533,7 @@ void prefill_kernel(PrefillArgs a) {
         } else {
 #pragma unroll
             for (int i = 0; i < Sh::IPT; i++) {
-                const int idx = tid + 256 * i;
+                const int idx = tid + NTHR * i;
                 int row, blk;
                 q4_item(idx, row, blk);
                 const uint8_t *base = idx < BK * NB ? kbase : vbase;
@@ -555,7 +558,7 @@ void prefill_kernel(PrefillArgs a) {
             float *vd = kd + BK * KS;
 #pragma unroll
             for (int i = 0; i < SIPT; i++) {
-                const int idx = tid + 256 * i;
+                const int idx = tid + NTHR * i;
                 const int c = idx % CPR, kk = (idx / CPR) % BK;
                 float *dst = (idx >= BK * CPR ? vd : kd) + kk * KS + 8 * c;
                 const u32x4 r = sraw[i];
@@ -568,7 +571,7 @@ void prefill_kernel(PrefillArgs a) {
             const NibConsts nk = nib_consts();
 #pragma unroll
             for (int i = 0; i < Sh::IPT; i++) {
-                const int idx = tid + 256 * i;
+                const int idx = tid + NTHR * i;
                 if (idx < Sh::QITEMS) {
                     int row, blk;
                     q4_item(idx, row, blk);
@@ -596,114 +599,132 @@ void prefill_kernel(PrefillArgs a) {
     auto compute_tile = [&](int jc, int buf, bool dma, const RowDma &nd) {
         const float *Ks = lds + buf * Sh::BUF;
         const float *Vs = Ks + BK * KS;
-        // O^T += V^T P^T operands: contraction step kk covers keys
-        // 8*(kk/4) + 4*hlf + kk%4
-        constexpr int NG = NT / GS;
-        using VVec = typename std::conditional<GS == 4, f32x4, f32x2>::type;
-        auto vread = [&](int step) {
-            const int kk = step / NG, ng = step % NG;
-            const int key = 8 * (kk >> 2) + 4 * hlf + (kk & 3);
-            return *(const VVec *)(Vs + key * KS + GS * r32 + ng * 32 * GS);
-        };
-        // S^T = K Q^T: lane holds row r32, keys 8*(r/4) + 4*hlf + r%4
-        // LDS reads run one step ahead of the MFMAs that consume them; the
-        // scheduling fences keep the compiler from sinking them back.
-        f32x16 s = f32x16{};
-        const float *krow = Ks + r32 * KS + hlf * HH;
-        f32x4 kc = *(const f32x4 *)krow;
-        VVec vc0{};
+        constexpr int NBB = Sh::NBB;
+        // S^T = K Q^T over the tile's two 16-key sets: in set ks the A row m
+        // is key 16 ks + m; MFMA t of group j contracts dims 16 j + 4 k + t
+        // (k = the B row, lane group g4), so a lane's K operand of a group is
+        // one 16-byte read and its q operands are qr[4 j + t]. Register r of
+        // set ks then holds key 16 ks + 4 g4 + r of row n16. LDS reads run one
+        // group ahead of the MFMAs that consume them.
+        f32x4 s0 = f32x4{}, s1 = f32x4{};
+        const float *kr0 = Ks + n16 * KS + 4 * g4;
+        const float *kr1 = kr0 + 16 * KS;
+        // PV step st (0..7) contracts keys 16 (st >> 2) + 4 k + (st & 3): its
+        // B operand is register st & 3 of set st >> 2. Its A operand for
+        // output block b is V at dim 64 (b >> 2) + 4 m + (b & 3) of that key
+        // (m = lane & 15), so a lane's operands of a step are NBB 16-byte
+        // reads of its key's row, contiguous across the 16 lanes of a group.
+        auto vread = [&](int st, f32x4 (&vv)[NBB]) {
+            const float *vr = Vs + (16 * (st >> 2) + 4 * g4 + (st & 3)) * KS + 4 * n16;
 #pragma unroll
-        for (int i = 0; i < HH / 4; i++) {
-            f32x4 kn = kc;
-            if (i + 1 < HH / 4) kn = *(const f32x4 *)(krow + 4 * (i + 1));
-            else vc0 = vread(0);       // PV's first operand, read during the last MFMAs
+            for (int bb = 0; bb < NBB; bb++) vv[bb] = *(const f32x4 *)(vr + 64 * bb);
+        };
+        constexpr int NJ = HD / 16;
+        f32x4 kc0 = *(const f32x4 *)kr0, kc1 = *(const f32x4 *)kr1;
+        f32x4 vc[NBB];
+#pragma unroll
+        for (int j = 0; j < NJ; j++) {
+            f32x4 kn0 = kc0, kn1 = kc1;
+            if (j + 1 < NJ) {
+                kn0 = *(const f32x4 *)(kr0 + 16 * (j + 1));
+                kn1 = *(const f32x4 *)(kr1 + 16 * (j + 1));
+            } else {
+                vread(0, vc);     // PV's first operands, read during the last MFMAs
+            }
             if constexpr (SPLIT) {
-                if (dma && i < RPW) issue_row(nd, i);
+                if (dma && j < RPW) issue_row(nd, j);
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int t = 0; t < 4; t++) s = mfma32(kc[t], qr[4 * i + t], s);
+            for (int t = 0; t < 4; t++) {
+                s0 = mfma16(kc0[t], qr[4 * j + t], s0);
+                s1 = mfma16(kc1[t], qr[4 * j + t], s1);
+            }
             __builtin_amdgcn_sched_barrier(0);
-            kc = kn;
+            kc0 = kn0;
+            kc1 = kn1;
         }
-        // every key of the tile is in the key set of every row of the wave
-        // no key of the tile is an fp16-shadow key for any row of the wave
         const bool shadow_free =
             !shadowed || (jc >= a.sh.sink && (a.sh.win <= 0 || jc + BK - 1 <= pw0 - a.sh.win));
         const bool full = !SH && jc + BK - 1 <= pw0 && shadow_free &&
                           (a.win <= 0 || jc + BK - 1 < a.sink || jc >= pw1 - a.win + 1);
         if (SH) {
-            // list entry li (position ps) is live for this row iff it is in
-            // the row's key set and read from the shadow for it: a sink
-            // position, or a ring row inside the row's shadow window that
-            // still holds ps (tag bit from one lane per entry)
             const int lane_li = jc + (lane & 31);
             const int lane_ps = shl.pos(lane_li);
             const bool tag_ok = lane_li < shl.nk && lane_ps >= a.sh.sink &&
                                 a.sh.win_pos[lane_ps % kShadowWinMax] == lane_ps;
             const unsigned tags = (unsigned)__ballot(tag_ok);
 #pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int kl = 8 * (r >> 2) + 4 * hlf + (r & 3);
-                const int li = jc + kl;
-                const int ps = shl.pos(li);
-                const bool from_shadow =
-                    ps < a.sh.sink || (ps > p_row - a.sh.win && ((tags >> kl) & 1u) != 0);
-                const bool ok = row_live && li < shl.nk && from_shadow &&
-                                in_key_set(ps, p_row, a.sink, a.win);
-                s[r] = ok ? s[r] : -INFINITY;
+            for (int ks = 0; ks < 2; ks++) {
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    const int kl = 16 * ks + 4 * g4 + r;
+                    const int li = jc + kl;
+                    const int ps = shl.pos(li);
+                    const bool from_shadow =
+                        ps < a.sh.sink || (ps > p_row - a.sh.win && ((tags >> kl) & 1u) != 0);
+                    const bool ok = row_live && li < shl.nk && from_shadow &&
+                                    in_key_set(ps, p_row, a.sink, a.win);
+                    f32x4 &sv = ks ? s1 : s0;
+                    sv[r] = ok ? sv[r] : -INFINITY;
+                }
             }
         } else if (!full) {
-            // key j is live for this row iff lo_win <= j <= p_row or j < sink_end
             const int hi_key = row_live ? p_row : -1;
             const int lo_win = a.win > 0 ? p_row - a.win + 1 : 0;
             const int sink_end = a.win > 0 ? min(a.sink, hi_key + 1) : 0;
 #pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int key = jc + 8 * (r >> 2) + 4 * hlf + (r & 3);
-                bool ok = (key <= hi_key) & ((key >= lo_win) | (key < sink_end));
-                if (FMT == 1 && !shadow_free)
-                    ok = ok && !shadow_key(a.sh, a.sh.win_pos, key, p_row);
-                s[r] = ok ? s[r] : -INFINITY;
+            for (int ks = 0; ks < 2; ks++) {
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    const int key = jc + 16 * ks + 4 * g4 + r;
+                    bool ok = (key <= hi_key) & ((key >= lo_win) | (key < sink_end));
+                    if (FMT == 1 && !shadow_free)
+                        ok = ok && !shadow_key(a.sh, a.sh.win_pos, key, p_row);
+                    f32x4 &sv = ks ? s1 : s0;
+                    sv[r] = ok ? sv[r] : -INFINITY;
+                }
             }
         }
-        float tmax = s[0];
-#pragma unroll
-        for (int r = 1; r < 16; r++) tmax = fmaxf(tmax, s[r]);
-        tmax = half_swap_max(tmax);
-        // move the reference max only when the tile max passes it by kTau
-        // (from -inf: whenever the tile has a live key)
+        float tmax = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])),
+                           fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
+        tmax = half_swap_max(row16_swap_max(tmax));   // over the row's four lane groups
         const bool rebase = tmax > m_run + kTau;
         if (__ballot(rebase)) {
             const float corr = rebase ? fast_exp2(m_run - tmax) : 1.0f;
-            if (__ballot(rebase && m_run != -INFINITY)) {   // rows starting at -inf hold O = 0
+            if (__ballot(rebase && m_run != -INFINITY)) {
 #pragma unroll
-                for (int n = 0; n < NT; n++) scale_acc(O[n], corr);
+                for (int n = 0; n < NO; n++) scale_acc(O[n], corr);
             }
             l_run *= corr;
             m_run = rebase ? tmax : m_run;
         }
-        const float m_use = m_run == -INFINITY ? 0.0f : m_run;   // all-masked row: keep p = 0
+        const float m_use = m_run == -INFINITY ? 0.0f : m_run;
         float psum = 0.0f;
 #pragma unroll
-        for (int r = 0; r < 16; r++) {
-            s[r] = fast_exp2(s[r] - m_use);
-            psum += s[r];
+        for (int r = 0; r < 4; r++) {
+            s0[r] = fast_exp2(s0[r] - m_use);
+            s1[r] = fast_exp2(s1[r] - m_use);
+            psum += s0[r] + s1[r];
         }
         l_run += psum;
 
-        // O^T += V^T P^T (reads one step ahead, as above)
-        VVec vc = vc0;
+        // O^T += V^T P^T
 #pragma unroll
-        for (int step = 0; step < 16 * NG; step++) {
-            VVec vn = vc;
-            if (step + 1 < 16 * NG) vn = vread(step + 1);
+        for (int st = 0; st < 8; st++) {
+            f32x4 vn[NBB];
+            if (st + 1 < 8) vread(st + 1, vn);
             __builtin_amdgcn_sched_barrier(0);
-            const int kk = step / NG, ng = step % NG;
+            const float p = (st >> 2) ? s1[st & 3] : s0[st & 3];
 #pragma unroll
-            for (int u = 0; u < GS; u++) O[ng * GS + u] = mfma32(vc[u], s[kk], O[ng * GS + u]);
+            for (int bb = 0; bb < NBB; bb++)
+#pragma unroll
+                for (int e = 0; e < 4; e++) O[4 * bb + e] = mfma16(vc[bb][e], p, O[4 * bb + e]);
             __builtin_amdgcn_sched_barrier(0);
-            vc = vn;
+            if (st + 1 < 8) {
+#pragma unroll
+                for (int bb = 0; bb < NBB; bb++) vc[bb] = vn[bb];
+            }
         }
     };
 
@@ -742,13 +763,15 @@ void prefill_kernel(PrefillArgs a) {
     }
 
     // ---- finalise: out = acc / l (whole segment) or this piece's partial
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    // a row's l is spread over its four lane groups
+    float l_tot = l_run + __shfl_xor(l_run, 32);
+    l_tot += __shfl_xor(l_tot, 16);
     float scale_out;
     if (whole && SH) {
         // the row's shadow partial: m, l to the workspace, acc (unnormalised) to out
         const size_t rf = (size_t)(p_row + sg.tok) * a.n_head + kvh * G + g;
         scale_out = 1.0f;
-        if (row_live && hlf == 0) {
+        if (row_live && row_lead) {
             const_cast<float *>(a.sh_m)[rf] = m_run;
             const_cast<float *>(a.sh_l)[rf] = l_tot;
         }
@@ -756,12 +779,12 @@ void prefill_kernel(PrefillArgs a) {
         const size_t t = (size_t)(p_row + sg.tok);
         scale_out = 1.0f / l_tot;
         // ln sum exp(scale q.k) = ln 2 * (m + log2 l): m is in base-2 units
-        if (a.lse && row_live && hlf == 0)
+        if (a.lse && row_live && row_lead)
             a.lse[(size_t)(kvh * G + g) * a.n + t] = (m_run + log2f(l_tot)) * kLn2;
     } else {
         const size_t prow = (size_t)piece * ROWS + row_wg;
         scale_out = 1.0f;
-        if (hlf == 0) {
+        if (row_lead) {
             a.ws_m[prow] = m_run;
             a.ws_l[prow] = l_tot;
         }
@@ -776,18 +799,14 @@ void prefill_kernel(PrefillArgs a) {
     // LDS only; this segment's output stores stay in flight.
     lds_barrier();
     float *stg = lds + (size_t)w * Sh::R * KS;
+    // block b, register r holds dim 64 (b >> 2) + 16 g4 + 4 r + (b & 3)
 #pragma unroll
-    for (int r = 0; r < 16; r++) {
-        const int mi = 8 * (r >> 2) + 4 * hlf + (r & 3);
+    for (int r = 0; r < 4; r++) {
 #pragma unroll
-        for (int ng = 0; ng < NT / GS; ng++) {
-            float *dst = stg + r32 * KS + ng * 32 * GS + GS * mi;
-            if constexpr (GS == 4) {
-                *(f32x4 *)dst = f32x4{O[ng * 4 + 0][r], O[ng * 4 + 1][r], O[ng * 4 + 2][r],
-                                      O[ng * 4 + 3][r]} * scale_out;
-            } else {
-                *(f32x2 *)dst = f32x2{O[ng * 2 + 0][r], O[ng * 2 + 1][r]} * scale_out;
-            }
+        for (int bb = 0; bb < Sh::NBB; bb++) {
+            float *dst = stg + n16 * KS + 64 * bb + 16 * g4 + 4 * r;
+            *(f32x4 *)dst = f32x4{O[4 * bb + 0][r], O[4 * bb + 1][r], O[4 * bb + 2][r],
+                                  O[4 * bb + 3][r]} * scale_out;
         }
     }
     wave_lds_sync();
@@ -915,7 +934,8 @@ hipError_t launch_one(const PrefillArgs &a, hipStream_t s) {
         attr_set = true;
     }
     const size_t lds = lds_bytes<HD, G, FMT, MODE>(a.n_req);
-    hipLaunchKernelGGL((prefill_kernel<HD, G, FMT, MODE>), dim3(a.n_wg), dim3(256), lds, s, a);
+    hipLaunchKernelGGL((prefill_kernel<HD, G, FMT, MODE>), dim3(a.n_wg), dim3(64 * kPrefillWaves),
+                       lds, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     // fewer cut segments than work-groups
