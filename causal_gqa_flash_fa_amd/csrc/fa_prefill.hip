@@ -18,8 +18,9 @@
 //     sets: K rows come from LDS, Q^T is held in registers (pre-scaled by
 //     scale*log2 e). The contraction order of each group of 4 MFMAs is
 //     chosen so that a lane's K operands are one 16-byte read. The
-//     accumulator puts one query row per 16 lanes (lane&15) and 8 keys per
-//     lane, so the softmax needs two cross-lane steps (lane ^ 16, ^ 32).
+//     accumulator gives lane l 8 keys of query row l&15, so a row's scores
+//     sit in its 4 lane groups and the softmax needs two cross-lane steps
+//     (lane ^ 16, ^ 32).
 //   * O^T = V^T P^T, also 16x16x4: P^T is exactly the S^T accumulator after
 //     the exponentials (the key order of each contraction step is chosen to
 //     match the accumulator layout). Output block b of O^T holds dims
